@@ -1,0 +1,448 @@
+// C ABI of the MoE FFN layer: argument checks, workspace layout and the launch
+// sequence of each entry point (declared in include/moe_ffn.h).
+#include "../../include/moe_ffn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+moe_status fail_hip(hipError_t err, const char* where) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: %s", where, hipGetErrorString(err));
+  g_last_error = buf;
+  return MOE_ERR_HIP;
+}
+
+// Optional per-kernel timing: an event recorded after every launch.
+struct Timeline {
+  static constexpr int kMax = 32;
+  hipEvent_t ev[kMax + 1];
+  const char* names[kMax];
+  int n = 0;
+};
+
+// Record the end of the kernel just launched (no-op without a timeline).
+hipError_t mark(Timeline* tl, const char* name, hipStream_t st) {
+  if (!tl || tl->n >= Timeline::kMax) return hipSuccess;
+  tl->names[tl->n] = name;
+  return hipEventRecord(tl->ev[++tl->n], st);
+}
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
+constexpr int kMaxDim = 65536;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->hidden <= 0 || c->hidden % 32 || c->hidden > kMaxDim)
+    return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 32, at most 65536");
+  if (c->inter <= 0 || c->inter % 32 || c->inter > kMaxDim)
+    return fail(MOE_ERR_INVALID_ARG, "inter must be a positive multiple of 32, at most 65536");
+  if (c->n_experts < 1 || c->n_experts > 1024) return fail(MOE_ERR_INVALID_ARG, "n_experts must be in [1, 1024]");
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, min(n_experts, 16)]");
+  if (c->n_shared != 0 && c->n_shared != 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
+  if (c->n_shared == 1 && (c->shared_inter <= 0 || c->shared_inter % 32 || c->shared_inter > kMaxDim))
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter must be a positive multiple of 32, at most 65536");
+  if (c->score_func != 0) return fail(MOE_ERR_UNSUPPORTED, "score_func must be 0 (sqrtsoftplus)");
+  if (!std::isfinite(c->route_scale)) return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite");
+  if (!(c->swiglu_limit > 0.f)) return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be > 0");
+  return MOE_OK;
+}
+
+moe_status check_tokens(int64_t tokens) {
+  if (tokens < 0 || tokens > kMaxTokens) return fail(MOE_ERR_INVALID_ARG, "tokens must be in [0, 2^22]");
+  return MOE_OK;
+}
+
+moe_status need(const void* p, size_t align, const char* name) {
+  static thread_local char buf[160];
+  if (!p) {
+    std::snprintf(buf, sizeof(buf), "%s is NULL", name);
+    return fail(MOE_ERR_INVALID_ARG, buf);
+  }
+  if (!aligned(p, align)) {
+    std::snprintf(buf, sizeof(buf), "%s is not %zu-byte aligned", name, align);
+    return fail(MOE_ERR_ALIGNMENT, buf);
+  }
+  return MOE_OK;
+}
+
+moe_status check_routed_weights(const moe_config* c, const moe_weights* w, bool need_router, bool need_experts) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  moe_status s;
+  if (need_router) {
+    if ((s = need(w->router_w, 16, "router_w")) != MOE_OK) return s;
+    if (w->router_bias && !aligned(w->router_bias, 4)) return fail(MOE_ERR_ALIGNMENT, "router_bias is not 4-byte aligned");
+  }
+  if (need_experts) {
+    if ((s = need(w->gu_q, 16, "gu_q")) != MOE_OK) return s;
+    if ((s = need(w->gu_s, 16, "gu_s")) != MOE_OK) return s;
+    if ((s = need(w->dn_q, 16, "dn_q")) != MOE_OK) return s;
+    if ((s = need(w->dn_s, 16, "dn_s")) != MOE_OK) return s;
+    if (c->n_shared == 1) {
+      if ((s = need(w->sh_gu, 16, "sh_gu")) != MOE_OK) return s;
+      if ((s = need(w->sh_dn, 16, "sh_dn")) != MOE_OK) return s;
+    } else if (w->sh_gu || w->sh_dn) {
+      return fail(MOE_ERR_INVALID_ARG, "sh_gu/sh_dn must be NULL when n_shared == 0");
+    }
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- workspace layout
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct WsLayout {
+  moe::RouterPlan router;
+  int gemm_mt = 1, shared_mt = 1;
+  int64_t max_tiles = 0, shared_tiles = 0;
+  Region logits, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h, y_slot,
+      h_sh, y_sh;
+  size_t total = 0;
+};
+
+WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
+  WsLayout L;
+  const int64_t n = tokens * c->top_k;
+  const int E = c->n_experts;
+  L.router = moe::router_plan(tokens, E, c->hidden);
+  L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E));
+  L.shared_mt = moe::expert_gemm_mt(tokens, 1);
+  L.max_tiles = moe::max_gemm_tiles(n, E, 16 * L.gemm_mt);
+  L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
+  const int64_t nchunks = moe::permute_chunks(n);
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off += (bytes + 255) & ~size_t(255);
+  };
+  take(L.logits, sizeof(float) * (size_t)L.router.ksplit * tokens * E);
+  take(L.rank, sizeof(int32_t) * n);
+  take(L.chunk_counts, sizeof(int32_t) * nchunks * E);
+  take(L.chunk_base, sizeof(int32_t) * nchunks * E);
+  take(L.tiles, sizeof(moe::GemmTile) * L.max_tiles);
+  take(L.tile_count, sizeof(int32_t) * 4);
+  take(L.idx, sizeof(int32_t) * n);
+  take(L.w, sizeof(float) * n);
+  take(L.offsets, sizeof(int32_t) * (E + 1));
+  take(L.sorted, sizeof(int32_t) * n);
+  take(L.slot_pos, sizeof(int32_t) * n);
+  take(L.h, sizeof(uint16_t) * n * c->inter);
+  take(L.y_slot, sizeof(uint16_t) * n * c->hidden);
+  const int64_t is = c->n_shared ? c->shared_inter : 0;
+  take(L.h_sh, sizeof(uint16_t) * tokens * is);
+  take(L.y_sh, sizeof(uint16_t) * (c->n_shared ? tokens * c->hidden : 0));
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, const Region& r) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + r.off);
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, const WsLayout& L) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGNMENT, "ws is not 256-byte aligned");
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "ws_bytes is smaller than moe_workspace_bytes()");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- launch sequences (arguments already checked)
+moe_status run_route(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, int32_t* idx,
+                     float* wts, float* gap, void* ws, const WsLayout& L, hipStream_t st, Timeline* tl) {
+  float* part = at<float>(ws, L.logits);
+  hipError_t err = moe::launch_router_logits(L.router, x, w->router_w, part, (int)T, c->n_experts, c->hidden, st);
+  if (err == hipSuccess) err = mark(tl, "router_logits", st);
+  if (err != hipSuccess) return fail_hip(err, "router logits launch");
+  err = moe::launch_router_topk(part, L.router.ksplit, w->router_bias, (int)T, c->n_experts, c->top_k,
+                                c->route_scale, idx, wts, gap, st);
+  if (err == hipSuccess) err = mark(tl, "router_topk", st);
+  if (err != hipSuccess) return fail_hip(err, "router top-k launch");
+  return MOE_OK;
+}
+
+moe_status run_permute(const moe_config* c, const int32_t* idx, int64_t T, int32_t* offsets, int32_t* sorted,
+                       int32_t* slot_pos, void* ws, const WsLayout& L, bool with_tiles, hipStream_t st,
+                       Timeline* tl) {
+  moe::PermuteScratch s{at<int32_t>(ws, L.rank), at<int32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.chunk_base)};
+  hipError_t err = moe::launch_permute(idx, (int)(T * c->top_k), c->n_experts, s, offsets, sorted, slot_pos,
+                                       16 * L.gemm_mt, with_tiles ? at<moe::GemmTile>(ws, L.tiles) : nullptr,
+                                       at<int32_t>(ws, L.tile_count), st);
+  if (err == hipSuccess) err = mark(tl, "permute", st);
+  if (err != hipSuccess) return fail_hip(err, "permute launch");
+  return MOE_OK;
+}
+
+// Routed gate/up + down over the tile table in ws, then the shared expert.
+moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
+                       const int32_t* sorted, uint16_t* y_slot, uint16_t* y_shared, void* ws, const WsLayout& L,
+                       hipStream_t st, Timeline* tl) {
+  const int H = c->hidden, I = c->inter;
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  moe::GemmParams p{};
+  p.tiles = at<moe::GemmTile>(ws, L.tiles);
+  p.tile_count = at<int32_t>(ws, L.tile_count);
+  // gate/up: A = gathered token rows of x, B = W_gu[e] [2I][H], C = h [n][I]
+  p.gather = sorted;
+  p.gather_div = c->top_k;
+  p.A = x;
+  p.lda = H;
+  p.a_rows = (int)T;
+  p.K = H;
+  p.bq = w->gu_q;
+  p.bs = w->gu_s;
+  p.b_expert_rows = 2 * (int64_t)I;
+  p.b_row_second = I;
+  p.N = I;
+  p.C = h;
+  p.ldc = I;
+  p.limit = c->swiglu_limit;
+  hipError_t err = moe::launch_expert_gemm(p, true, true, L.gemm_mt, L.max_tiles, st);
+  if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+  // down: A = h rows in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
+  p.gather = nullptr;
+  p.A = h;
+  p.lda = I;
+  p.a_rows = (int)(T * c->top_k);
+  p.K = I;
+  p.bq = w->dn_q;
+  p.bs = w->dn_s;
+  p.b_expert_rows = H;
+  p.b_row_second = 0;
+  p.N = H;
+  p.C = y_slot;
+  p.ldc = H;
+  err = moe::launch_expert_gemm(p, false, true, L.gemm_mt, L.max_tiles, st);
+  if (err == hipSuccess) err = mark(tl, "routed_down", st);
+  if (err != hipSuccess) return fail_hip(err, "routed down launch");
+  if (c->n_shared == 1) {
+    const int Is = c->shared_inter;
+    uint16_t* hs = at<uint16_t>(ws, L.h_sh);
+    moe::GemmParams q{};
+    q.M = (int)T;
+    q.A = x;
+    q.lda = H;
+    q.a_rows = (int)T;
+    q.K = H;
+    q.bh = w->sh_gu;
+    q.b_expert_rows = 2 * (int64_t)Is;
+    q.b_row_second = Is;
+    q.N = Is;
+    q.C = hs;
+    q.ldc = Is;
+    q.limit = c->swiglu_limit;
+    err = moe::launch_expert_gemm(q, true, false, L.shared_mt, L.shared_tiles, st);
+    if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
+    q.A = hs;
+    q.lda = Is;
+    q.a_rows = (int)T;
+    q.K = Is;
+    q.bh = w->sh_dn;
+    q.b_expert_rows = H;
+    q.b_row_second = 0;
+    q.N = H;
+    q.C = y_shared;
+    q.ldc = H;
+    err = moe::launch_expert_gemm(q, false, false, L.shared_mt, L.shared_tiles, st);
+    if (err == hipSuccess) err = mark(tl, "shared_down", st);
+  if (err != hipSuccess) return fail_hip(err, "shared down launch");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg, int64_t tokens) {
+  if (check_config(cfg) != MOE_OK || check_tokens(tokens) != MOE_OK) return 0;
+  return plan_workspace(cfg, tokens).total;
+}
+
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                     int32_t* topk_idx, float* topk_w, float* tie_gap, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_routed_weights(cfg, w, true, false)) != MOE_OK) return s;
+  if ((s = need(x, 16, "x")) != MOE_OK || (s = need(topk_idx, 4, "topk_idx")) != MOE_OK ||
+      (s = need(topk_w, 4, "topk_w")) != MOE_OK)
+    return s;
+  if (tie_gap && !aligned(tie_gap, 4)) return fail(MOE_ERR_ALIGNMENT, "tie_gap is not 4-byte aligned");
+  const WsLayout L = plan_workspace(cfg, tokens);
+  if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
+  if (tokens == 0) return MOE_OK;
+  return run_route(cfg, w, x, tokens, topk_idx, topk_w, tie_gap, ws, L, static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t tokens, int32_t* expert_offsets,
+                       int32_t* sorted_slots, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = need(topk_idx, 4, "topk_idx")) != MOE_OK || (s = need(expert_offsets, 4, "expert_offsets")) != MOE_OK ||
+      (s = need(sorted_slots, 4, "sorted_slots")) != MOE_OK || (s = need(slot_pos, 4, "slot_pos")) != MOE_OK)
+    return s;
+  const WsLayout L = plan_workspace(cfg, tokens);
+  if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
+  if (tokens == 0) return MOE_OK;
+  return run_permute(cfg, topk_idx, tokens, expert_offsets, sorted_slots, slot_pos, ws, L, false,
+                     static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                          const int32_t* expert_offsets, const int32_t* sorted_slots, uint16_t* y_slot,
+                          uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_routed_weights(cfg, w, false, true)) != MOE_OK) return s;
+  if ((s = need(x, 16, "x")) != MOE_OK || (s = need(expert_offsets, 4, "expert_offsets")) != MOE_OK ||
+      (s = need(sorted_slots, 4, "sorted_slots")) != MOE_OK || (s = need(y_slot, 16, "y_slot")) != MOE_OK)
+    return s;
+  if (cfg->n_shared == 1) {
+    if ((s = need(y_shared, 16, "y_shared")) != MOE_OK) return s;
+  } else if (y_shared) {
+    return fail(MOE_ERR_INVALID_ARG, "y_shared must be NULL when n_shared == 0");
+  }
+  const WsLayout L = plan_workspace(cfg, tokens);
+  if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
+  if (tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = moe::launch_tile_table(expert_offsets, cfg->n_experts, (int)(tokens * cfg->top_k), 16 * L.gemm_mt,
+                                          at<moe::GemmTile>(ws, L.tiles), at<int32_t>(ws, L.tile_count), st);
+  if (err != hipSuccess) return fail_hip(err, "tile table launch");
+  return run_experts(cfg, w, x, tokens, sorted_slots, y_slot, y_shared, ws, L, st, nullptr);
+}
+
+moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int32_t* slot_pos, const float* topk_w,
+                       const uint16_t* y_shared, int64_t tokens, uint16_t* y, void* stream) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = need(y_slot, 16, "y_slot")) != MOE_OK || (s = need(slot_pos, 4, "slot_pos")) != MOE_OK ||
+      (s = need(topk_w, 4, "topk_w")) != MOE_OK || (s = need(y, 16, "y")) != MOE_OK)
+    return s;
+  if (y_shared && !aligned(y_shared, 16)) return fail(MOE_ERR_ALIGNMENT, "y_shared is not 16-byte aligned");
+  if (tokens == 0) return MOE_OK;
+  hipError_t err = moe::launch_combine(y_slot, slot_pos, topk_w, y_shared, (int)tokens, cfg->top_k, cfg->hidden, y,
+                                       static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail_hip(err, "combine launch");
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                              hipStream_t st, Timeline* tl) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_routed_weights(cfg, w, true, true)) != MOE_OK) return s;
+  if ((s = need(x, 16, "x")) != MOE_OK || (s = need(y, 16, "y")) != MOE_OK) return s;
+  if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_idx_out is not 4-byte aligned");
+  if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_w_out is not 4-byte aligned");
+  const WsLayout L = plan_workspace(cfg, tokens);
+  if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
+  if (tokens == 0) return MOE_OK;
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;
+  uint16_t* y_slot = at<uint16_t>(ws, L.y_slot);
+  uint16_t* y_sh = cfg->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;
+  if ((s = run_experts(cfg, w, x, tokens, sorted, y_slot, y_sh, ws, L, st, tl)) != MOE_OK) return s;
+  hipError_t err = moe::launch_combine(y_slot, slot_pos, wts, y_sh, (int)tokens, cfg->top_k, cfg->hidden, y, st);
+  if (err == hipSuccess) err = mark(tl, "combine", st);
+  if (err != hipSuccess) return fail_hip(err, "combine launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                             uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return layer_forward_impl(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                            static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                                   uint16_t* y, void* ws, size_t ws_bytes, void* stream, float* kernel_ms,
+                                   const char** kernel_names, int32_t max_kernels, int32_t* n_kernels) {
+  if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0)
+    return fail(MOE_ERR_INVALID_ARG, "kernel_ms, kernel_names and n_kernels are required");
+  *n_kernels = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Timeline tl;
+  int created = 0;
+  hipError_t err = hipSuccess;
+  for (; created <= Timeline::kMax && err == hipSuccess; ++created) err = hipEventCreate(&tl.ev[created]);
+  moe_status s = MOE_OK;
+  if (err != hipSuccess) {
+    --created;
+    s = fail_hip(err, "hipEventCreate");
+  } else if ((err = hipEventRecord(tl.ev[0], st)) != hipSuccess) {
+    s = fail_hip(err, "hipEventRecord");
+  } else {
+    s = layer_forward_impl(cfg, w, x, tokens, y, nullptr, nullptr, ws, ws_bytes, st, &tl);
+    if (s == MOE_OK && tl.n > 0 && (err = hipEventSynchronize(tl.ev[tl.n])) != hipSuccess)
+      s = fail_hip(err, "hipEventSynchronize");
+    if (s == MOE_OK) {
+      for (int i = 0; i < tl.n && i < max_kernels; ++i) {
+        float ms = 0.f;
+        if ((err = hipEventElapsedTime(&ms, tl.ev[i], tl.ev[i + 1])) != hipSuccess) {
+          s = fail_hip(err, "hipEventElapsedTime");
+          break;
+        }
+        kernel_ms[i] = ms;
+        kernel_names[i] = tl.names[i];
+      }
+      *n_kernels = tl.n;
+    }
+  }
+  for (int i = 0; i < created; ++i) (void)hipEventDestroy(tl.ev[i]);
+  return s;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+}  // extern "C"

@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     ExpertTensor,
     LayerInputs,
     make_inputs,
+    make_router_inputs,
     mxfp4_encode,
     pack_nibbles,
     f32_to_bf16_bits,

@@ -145,6 +145,19 @@ def zipf_bias(cfg: LayerConfig, seed: int, weight_set: int = 0) -> torch.Tensor:
     return (cfg.zipf_alpha * rank.pow(-cfg.zipf_s)).to(torch.float32)
 
 
+def make_router_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set: int = 0,
+                       x_seed: Optional[int] = None):
+    """(x bits [T, H], W_r [E, H], bias [E] or None): the same tensors make_inputs draws."""
+    dev = torch.device(device)
+    xs = seed if x_seed is None else x_seed
+    x = f32_to_bf16_bits(_randn((cfg.tokens, cfg.hidden), derive_seed(xs, cfg.cfg_id, TENSOR_X, 0, 0), dev,
+                                cfg.x_std))
+    router_w = _randn((cfg.n_experts, cfg.hidden), derive_seed(seed, cfg.cfg_id, TENSOR_ROUTER, 0, weight_set),
+                      dev, 1.0 / math.sqrt(cfg.hidden))
+    bias = zipf_bias(cfg, seed, weight_set).to(dev) if cfg.bias == "zipf" else None
+    return x, router_w, bias
+
+
 def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set: int = 0,
                 x_seed: Optional[int] = None) -> LayerInputs:
     """All inputs of one layer, generated on ``device``.
@@ -155,11 +168,7 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set: int =
     """
     dev = torch.device(device)
     t, h, e, inter = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.inter
-    xs = seed if x_seed is None else x_seed
-    x = f32_to_bf16_bits(_randn((t, h), derive_seed(xs, cfg.cfg_id, TENSOR_X, 0, 0), dev, cfg.x_std))
-    router_w = _randn((e, h), derive_seed(seed, cfg.cfg_id, TENSOR_ROUTER, 0, weight_set), dev,
-                      1.0 / math.sqrt(h))
-    bias = zipf_bias(cfg, seed, weight_set).to(dev) if cfg.bias == "zipf" else None
+    x, router_w, bias = make_router_inputs(cfg, seed, device, weight_set, x_seed)
     gu_q = torch.empty((e, 2 * inter, h // 2), dtype=torch.uint8, device=dev)
     gu_s = torch.empty((e, 2 * inter, h // 32), dtype=torch.uint8, device=dev)
     dn_q = torch.empty((e, h, inter // 2), dtype=torch.uint8, device=dev)

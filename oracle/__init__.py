@@ -31,4 +31,5 @@ from .moe_oracle import (  # noqa: F401
     shared_expert,
     combine,
     layer_forward,
+    routed_expert_weights,
 )

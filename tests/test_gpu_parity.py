@@ -1,0 +1,296 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on an MI355X.
+
+Inputs are the seeded synthetic workloads; expert ids must match except at
+oracle-reported near-ties, outputs must meet the relative-L2 / max-abs bar
+(see tests/parity.py), integer outputs must match bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_07_amd as moe
+import oracle
+from moe_synth import CONFIGS, make_inputs, make_router_inputs
+
+from parity import (TIE_TOL, assert_bar, bf16_to_f64, gpu_expert_ffn, gpu_layer, gpu_permute, gpu_route,
+                    match_routing)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_route(cfg, x, router_w, bias):
+    return oracle.route(x.cpu().numpy().view(np.uint16), router_w.cpu().numpy(),
+                        None if bias is None else bias.cpu().numpy(), cfg.top_k, cfg.route_scale)
+
+
+def _check_layer(inp, tokens=None, gpu=None):
+    """Run the GPU layer (or take its results) and compare rows `tokens` (all if None) with the oracle."""
+    y, idx, w = gpu if gpu is not None else gpu_layer(inp)
+    cfg = inp.cfg
+    args = inp.oracle_args()
+    sel_rows = np.arange(cfg.tokens) if tokens is None else np.asarray(tokens)
+    ref = oracle.layer_forward(**args, tokens=sel_rows)
+    g_idx = idx.cpu().numpy()[sel_rows]
+    g_w = w.cpu().numpy()[sel_rows]
+    alt = match_routing(g_idx, g_w, ref, cfg.route_scale)
+    y_ref = ref["y"]
+    if alt:  # near-tie tokens: the oracle's result for the selection the GPU made
+        sels = [alt.get(i, ref["idx"][i].tolist()) for i in range(len(sel_rows))]
+        y_ref = oracle.layer_forward(**args, tokens=sel_rows, selections=sels)["y"]
+    stats = assert_bar(bf16_to_f64(y)[sel_rows], y_ref, f"{cfg.name} y")
+    return stats, ref, alt
+
+
+# ------------------------------------------------------------------ router
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_route_full_size(name):
+    cfg = CONFIGS[name]
+    x, wr, b = make_router_inputs(cfg, seed=0, device=DEV)
+    idx, w, gap = gpu_route(cfg, x, wr, b)
+    ref = _oracle_route(cfg, x, wr, b)
+    alt = match_routing(idx.cpu().numpy(), w.cpu().numpy(), ref, cfg.route_scale)
+    g = gap.cpu().numpy().astype(np.float64)
+    same = np.array([t not in alt for t in range(cfg.tokens)])
+    fin = np.isfinite(ref["gap"])
+    assert np.all(np.abs(g[same & fin] - ref["gap"][same & fin]) <= 4e-6)
+    assert np.all(np.isinf(g[~fin]))
+    # weights sum to the route scale
+    assert np.allclose(w.sum(dim=1).cpu().numpy(), cfg.route_scale, rtol=0, atol=4e-6)
+    print(f"{name}: near-tie alternatives {len(alt)}, oracle gaps < 1e-6: {(ref['gap'] < TIE_TOL).sum()}")
+
+
+def test_route_exact_ties_resolve_to_lowest_index():
+    cfg = CONFIGS["decode_t64_h5120_e384"]
+    x, wr, _ = make_router_inputs(cfg, seed=1, device=DEV)
+    wr[:] = wr[7]  # every expert has the same router row: all logits tie exactly
+    idx, w, gap = gpu_route(cfg, x, wr, None)
+    assert torch.all(idx.cpu() == torch.arange(cfg.top_k, dtype=torch.int32)[None, :])
+    assert torch.all(gap.cpu() == 0.0)
+    assert torch.allclose(w.cpu(), torch.full_like(w.cpu(), cfg.route_scale / cfg.top_k), rtol=0, atol=1e-6)
+    x.zero_()
+    idx, w, _ = gpu_route(cfg, x, make_router_inputs(cfg, seed=2, device=DEV)[1], None)
+    assert torch.all(idx.cpu() == torch.arange(cfg.top_k, dtype=torch.int32)[None, :])
+
+
+def test_route_duplicate_rows_tie():
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=256)
+    x, wr, _ = make_router_inputs(cfg, seed=3, device=DEV)
+    wr[20] = wr[3]
+    wr[31] = wr[3]
+    idx, _, _ = gpu_route(cfg, x, wr, None)
+    for row in idx.cpu().numpy().tolist():
+        have = [e for e in (3, 20, 31) if e in row]
+        if have:
+            pos = [row.index(e) for e in have]
+            # equal scores: taken lowest index first, adjacent in the selection order
+            assert have == sorted(have) and pos == list(range(pos[0], pos[0] + len(pos)))
+            assert have == [3, 20, 31][:len(have)]
+
+
+# ------------------------------------------------------------------ permute
+
+
+def _random_routing(t, e, k, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    if skew:
+        p = 1.0 / np.arange(1, e + 1) ** 1.2
+        rows = [rng.choice(e, size=k, replace=False, p=p / p.sum()) for _ in range(t)]
+    else:
+        rows = [rng.permutation(e)[:k] for _ in range(t)]
+    return np.array(rows, dtype=np.int32).reshape(t, k)
+
+
+@pytest.mark.parametrize("t,e,k,skew", [(1, 384, 6, False), (3, 32, 6, False), (64, 384, 6, False),
+                                        (170, 384, 6, False), (171, 384, 6, False), (4096, 384, 6, False),
+                                        (16384, 128, 3, True), (1000, 1, 1, False), (2000, 1000, 16, False),
+                                        (700, 2, 2, False)])
+def test_permute_bit_exact(t, e, k, skew):
+    idx = _random_routing(t, e, k, seed=t * 7 + e, skew=skew)
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=t, n_experts=e, top_k=k)
+    off, srt, pos = gpu_permute(cfg, torch.from_numpy(idx).to(DEV))
+    ref = oracle.permute(idx, e)
+    assert np.array_equal(off.cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(srt.cpu().numpy(), ref["sorted_slots"])
+    assert np.array_equal(pos.cpu().numpy(), ref["slot_pos"])
+
+
+# ------------------------------------------------------------------ experts and combine
+
+
+@pytest.mark.parametrize("variant", ["tiny", "ragged_k", "no_shared", "min_dims"])
+def test_expert_ffn(variant):
+    base = CONFIGS["tiny_t8_h512_e32"]
+    cfg = {"tiny": base.with_(tokens=40),
+           "ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224),
+           "no_shared": base.with_(tokens=16, n_shared=0, shared_inter=0),
+           "min_dims": base.with_(tokens=20, hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2)}[variant]
+    inp = make_inputs(cfg, seed=5, device=DEV)
+    idx = _random_routing(cfg.tokens, cfg.n_experts, cfg.top_k, seed=11)
+    perm = oracle.permute(idx, cfg.n_experts)
+    off = torch.from_numpy(perm["expert_offsets"]).to(DEV)
+    srt = torch.from_numpy(perm["sorted_slots"]).to(DEV)
+    y_slot, y_sh = gpu_expert_ffn(inp, off, srt)
+    a = inp.oracle_args()
+    x = oracle.bf16_bits_to_f64(a["x_bits"])
+    ref_slot = np.zeros((cfg.tokens * cfg.top_k, cfg.hidden))
+    for e in range(cfg.n_experts):
+        lo, hi = perm["expert_offsets"][e], perm["expert_offsets"][e + 1]
+        if hi > lo:
+            wgu, wdn = oracle.routed_expert_weights(a["gu_q"], a["gu_s"], a["dn_q"], a["dn_s"], e, cfg.hidden,
+                                                    cfg.inter)
+            rows = perm["sorted_slots"][lo:hi] // cfg.top_k
+            ref_slot[lo:hi] = oracle.expert_mlp(x[rows], wgu, wdn, cfg.swiglu_limit)[1]
+    assert_bar(bf16_to_f64(y_slot), ref_slot, "y_slot")
+    if cfg.n_shared:
+        assert_bar(bf16_to_f64(y_sh), oracle.shared_expert(a["x_bits"], a["sh_gu"], a["sh_dn"],
+                                                          cfg.swiglu_limit)[1], "y_shared")
+
+
+def test_combine():
+    from moe_synth import f32_to_bf16_bits
+    t, k, h = 37, 6, 640
+    g = torch.Generator().manual_seed(9)
+    y_slot = f32_to_bf16_bits(torch.randn(t * k, h, generator=g))
+    y_sh = f32_to_bf16_bits(torch.randn(t, h, generator=g))
+    w = torch.rand(t, k, generator=g, dtype=torch.float32) * 1.5
+    pos = torch.randperm(t * k, generator=g).to(torch.int32)
+    cfg = moe.make_config(h, 32, k, 256)
+    for shared in (y_sh, None):
+        y = torch.empty(t, h, dtype=torch.int16, device=DEV)
+        moe.moe_combine(cfg, y_slot.to(DEV), pos.to(DEV), w.to(DEV), None if shared is None else shared.to(DEV),
+                        t, y)
+        torch.cuda.synchronize()
+        ref = oracle.combine(bf16_to_f64(y_slot), pos.numpy(), w.numpy().astype(np.float64),
+                             None if shared is None else bf16_to_f64(shared), k)
+        got = bf16_to_f64(y)
+        # one bf16 rounding of an fp32 sum: within 2^-8 relative, plus fp32 accumulation error
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+
+
+# ------------------------------------------------------------------ whole layer
+
+
+def test_layer_tiny_full():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"], seed=0, device=DEV)
+    stats, _, _ = _check_layer(inp)
+    print("tiny:", stats)
+
+
+def test_layer_decode_t1_full():
+    inp = make_inputs(CONFIGS["decode_t1_h5120_e384"], seed=0, device=DEV)
+    stats, ref, _ = _check_layer(inp)
+    print("decode_t1:", stats, "experts", ref["idx"].tolist())
+
+
+def _sample(n, count, seed, must=()):
+    rng = np.random.default_rng(seed)
+    s = set(int(v) for v in rng.choice(n, size=min(count, n), replace=False))
+    s |= {0, n - 1} | set(int(v) for v in must)
+    return sorted(s)
+
+
+@pytest.mark.parametrize("name,count", [("decode_t64_h5120_e384", 12), ("prefill_t4096_h5120_e384", 10),
+                                        ("skew_t16384_h5120_e128", 10)])
+def test_layer_full_size_sampled(name, count):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    gpu = gpu_layer(inp)
+    must = ()
+    if inp.router_bias is not None:  # include tokens routed to the hottest expert
+        hot = int(torch.argmax(inp.router_bias).item())
+        hits = np.nonzero((gpu[1].cpu().numpy() == hot).any(axis=1))[0]
+        must = hits[:3]
+        load = np.bincount(gpu[1].cpu().numpy().reshape(-1), minlength=cfg.n_experts)
+        print(f"{name}: hottest expert load {load.max()} = {load.max() / load.mean():.1f}x mean")
+    toks = _sample(cfg.tokens, count, seed=1, must=must)
+    stats, _, alt = _check_layer(inp, tokens=toks, gpu=gpu)
+    print(f"{name}: {len(toks)} sampled tokens {stats}, near-tie alternatives {len(alt)}")
+
+
+@pytest.mark.parametrize("tokens", [1, 2, 3, 17])
+def test_layer_small_token_counts(tokens):
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens), seed=2, device=DEV)
+    _check_layer(inp)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7, 8, 16])
+def test_layer_top_k_range(k):
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=12, top_k=k), seed=3, device=DEV)
+    _check_layer(inp)
+
+
+@pytest.mark.parametrize("e,k", [(1, 1), (2, 2), (128, 3), (1000, 6)])
+def test_layer_expert_counts(e, k):
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=24, n_experts=e, top_k=k, hidden=256, inter=64,
+                                                         shared_inter=96), seed=4, device=DEV)
+    _check_layer(inp)
+
+
+@pytest.mark.parametrize("variant", ["min_dims", "ragged_k", "no_shared", "zipf_bias"])
+def test_layer_shapes(variant):
+    base = CONFIGS["tiny_t8_h512_e32"]
+    cfg = {"min_dims": base.with_(hidden=32, inter=32, shared_inter=32),
+           "ragged_k": base.with_(tokens=33, hidden=160, inter=96, shared_inter=224),
+           "no_shared": base.with_(n_shared=0, shared_inter=0),
+           "zipf_bias": base.with_(tokens=64, bias="zipf")}[variant]
+    _check_layer(make_inputs(cfg, seed=6, device=DEV))
+
+
+def test_layer_clamp_stress():
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=32, x_std=40.0)
+    inp = make_inputs(cfg, seed=7, device=DEV)
+    _, ref, _ = _check_layer(inp)
+    # the clamp must actually fire on a good share of the gate pre-activations
+    a = inp.oracle_args()
+    x = oracle.bf16_bits_to_f64(a["x_bits"])
+    e = int(ref["idx"][0, 0])
+    wgu, _ = oracle.routed_expert_weights(a["gu_q"], a["gu_s"], a["dn_q"], a["dn_s"], e, cfg.hidden, cfg.inter)
+    g = x @ wgu[:cfg.inter].T
+    assert np.mean(g > cfg.swiglu_limit) > 0.1
+
+
+def test_layer_zero_input_gives_exact_zero():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"], seed=8, device=DEV)
+    inp.x.zero_()
+    y, idx, w = gpu_layer(inp)
+    assert torch.all(y == 0)
+    assert torch.all(idx.cpu() == torch.arange(6, dtype=torch.int32)[None, :])
+
+
+def test_layer_zero_routed_weights_gives_shared_output():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"], seed=9, device=DEV)
+    inp.gu_q.zero_()
+    gpu = gpu_layer(inp)
+    y = gpu[0]
+    _check_layer(inp, gpu=gpu)
+    ref_sh = oracle.shared_expert(inp.x.cpu().numpy().view(np.uint16), inp.sh_gu.cpu().numpy().view(np.uint16),
+                                  inp.sh_dn.cpu().numpy().view(np.uint16), 10.0)[1]
+    assert_bar(bf16_to_f64(y), ref_sh, "y vs shared")
+
+
+def test_layer_down_scale_plus_one():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"], seed=10, device=DEV)
+    inp.dn_s += 1
+    _check_layer(inp)
+
+
+def test_layer_deterministic():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=300), seed=11, device=DEV)
+    a = gpu_layer(inp)
+    b = gpu_layer(inp)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_layer_many_tokens_small_dims():
+    """A large token count (multi-chunk permutation, many tiles) on a small layer, sampled."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=1 << 18, hidden=64, inter=32, shared_inter=32)
+    inp = make_inputs(cfg, seed=12, device=DEV)
+    gpu = gpu_layer(inp)
+    idx = gpu[1].cpu().numpy()
+    assert idx.min() >= 0 and idx.max() < cfg.n_experts
+    _check_layer(inp, tokens=_sample(cfg.tokens, 48, seed=2), gpu=gpu)
