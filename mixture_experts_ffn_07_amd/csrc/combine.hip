@@ -31,16 +31,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
-  for (int j = 0; j < top_k; ++j) {
-    const int64_t f = (int64_t)t * top_k + j;
-    const float wj = w[f];
-    const int pos = min(max(slot_pos[f], 0), tokens * top_k - 1);  // stays in y_slot for any slot_pos
-    const uint4 v = *reinterpret_cast<const uint4*>(y_slot + (int64_t)pos * hidden + h);
-    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  // Positions and weights of all k slots first, then all k rows, so each
+  // group of loads issues together (k <= 16).
+  const int n = tokens * top_k;
+  int pos[16];
+  float wj[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wj, bf16_to_f32((uint16_t)(vv[i] & 0xffffu)), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, bf16_to_f32((uint16_t)(vv[i] >> 16)), acc[2 * i + 1]);
+  for (int j = 0; j < 16; ++j) {
+    const int64_t f = min((int64_t)t * top_k + j, (int64_t)n - 1);
+    pos[j] = min(max(slot_pos[f], 0), n - 1);  // stays in y_slot for any slot_pos
+    wj[j] = j < top_k ? w[f] : 0.f;
+  }
+  uint4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < top_k) v[j] = *reinterpret_cast<const uint4*>(y_slot + (int64_t)pos[j] * hidden + h);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < top_k) {
+      const uint32_t vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wj[j], bf16_to_f32((uint16_t)(vv[i] & 0xffffu)), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj[j], bf16_to_f32((uint16_t)(vv[i] >> 16)), acc[2 * i + 1]);
+      }
     }
   }
   uint4 o;

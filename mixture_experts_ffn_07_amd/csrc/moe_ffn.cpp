@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <string>
 
+#include "mx_device.h"
+
 #include "moe_internal.h"
 
 namespace {
@@ -42,6 +44,9 @@ hipError_t mark(Timeline* tl, const char* name, hipStream_t st) {
 }
 
 constexpr int64_t kMaxTokens = int64_t(1) << 22;
+// few-token path: T <= 8 rows staged in at most 64 KB of LDS per block
+constexpr int64_t kDecodeMaxTokens = 8;
+constexpr size_t kDecodeMaxLds = 64 * 1024;
 constexpr int kMaxDim = 65536;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -111,10 +116,14 @@ struct Region {
 
 struct WsLayout {
   moe::RouterPlan router;
+  bool decode = false;  // few tokens: GEMV router, fused routing, weight-streaming projections
+  int bm = 16;          // rows per routed GEMM tile
   int gemm_mt = 1, shared_mt = 1;
   int64_t max_tiles = 0, shared_tiles = 0;
-  Region logits, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h, y_slot,
-      h_sh, y_sh;
+  bool route_small = false;   // decode with T * k <= 64: scores from the router GEMV, one-block routing
+  bool down_combine = false;  // decode: routed down projection with the combine folded in
+  Region logits, scores, xmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
+      y_slot, h_sh, y_sh;
   size_t total = 0;
 };
 
@@ -125,7 +134,27 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   L.router = moe::router_plan(tokens, E, c->hidden);
   L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E));
   L.shared_mt = moe::expert_gemm_mt(tokens, 1);
-  L.max_tiles = moe::max_gemm_tiles(n, E, 16 * L.gemm_mt);
+  const int k_fp4 = c->hidden > c->inter ? c->hidden : c->inter;
+  const int k_bf16 = c->n_shared ? (c->hidden > c->shared_inter ? c->hidden : c->shared_inter) : 0;
+  L.decode = tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&
+             moe::gemv_lds_bytes((int)tokens, k_fp4, true) <= kDecodeMaxLds &&
+             moe::gemv_lds_bytes((int)tokens, k_bf16, false) <= kDecodeMaxLds;
+  if (L.decode) {
+    L.route_small = n <= moe::kRouteSmallMaxSlots;
+    L.down_combine = tokens <= moe::kDownCombineMaxTokens && n <= 64 && c->inter <= moe::kDownCombineMaxInter &&
+                     moe::down_combine_lds_bytes((int)tokens, c->top_k, c->inter) <= kDecodeMaxLds;
+    L.router.ksplit = 1;  // full logits from the GEMV router
+    L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
+  } else {
+    L.bm = 16 * L.gemm_mt;
+  }
+  L.max_tiles = moe::max_gemm_tiles(n, E, L.bm);
+  {
+    // each expert holds at most T rows, so at most ceil(T / bm) tiles
+    const int64_t per_expert = (tokens + L.bm - 1) / L.bm;
+    const int64_t bound = (n < E ? n : E) * per_expert;
+    if (bound < L.max_tiles) L.max_tiles = bound;
+  }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
   const int64_t nchunks = moe::permute_chunks(n);
   size_t off = 0;
@@ -135,6 +164,8 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     off += (bytes + 255) & ~size_t(255);
   };
   take(L.logits, sizeof(float) * (size_t)L.router.ksplit * tokens * E);
+  take(L.scores, L.route_small ? sizeof(float) * 2 * (size_t)tokens * E : 0);
+  take(L.xmx, L.route_small ? (size_t)tokens * moe::mx_row_bytes(c->hidden) : 0);
   take(L.rank, sizeof(int32_t) * n);
   take(L.chunk_counts, sizeof(int32_t) * nchunks * E);
   take(L.chunk_base, sizeof(int32_t) * nchunks * E);
@@ -170,7 +201,10 @@ moe_status check_ws(void* ws, size_t ws_bytes, const WsLayout& L) {
 moe_status run_route(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, int32_t* idx,
                      float* wts, float* gap, void* ws, const WsLayout& L, hipStream_t st, Timeline* tl) {
   float* part = at<float>(ws, L.logits);
-  hipError_t err = moe::launch_router_logits(L.router, x, w->router_w, part, (int)T, c->n_experts, c->hidden, st);
+  hipError_t err = L.decode
+                       ? moe::launch_router_gemv(x, w->router_w, part, (int)T, c->n_experts, c->hidden, nullptr,
+                                                 nullptr, st)
+                       : moe::launch_router_logits(L.router, x, w->router_w, part, (int)T, c->n_experts, c->hidden, st);
   if (err == hipSuccess) err = mark(tl, "router_logits", st);
   if (err != hipSuccess) return fail_hip(err, "router logits launch");
   err = moe::launch_router_topk(part, L.router.ksplit, w->router_bias, (int)T, c->n_experts, c->top_k,
@@ -185,10 +219,245 @@ moe_status run_permute(const moe_config* c, const int32_t* idx, int64_t T, int32
                        Timeline* tl) {
   moe::PermuteScratch s{at<int32_t>(ws, L.rank), at<int32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.chunk_base)};
   hipError_t err = moe::launch_permute(idx, (int)(T * c->top_k), c->n_experts, s, offsets, sorted, slot_pos,
-                                       16 * L.gemm_mt, with_tiles ? at<moe::GemmTile>(ws, L.tiles) : nullptr,
+                                       L.bm, (int)L.max_tiles, with_tiles ? at<moe::GemmTile>(ws, L.tiles) : nullptr,
                                        at<int32_t>(ws, L.tile_count), st);
   if (err == hipSuccess) err = mark(tl, "permute", st);
   if (err != hipSuccess) return fail_hip(err, "permute launch");
+  return MOE_OK;
+}
+
+// Few tokens: weight-streaming projections, one tile per expert (routed) or
+// one for all T rows (shared).
+moe::GemvParams routed_gemv(const moe_config* c, const moe_weights* w, const uint16_t* x, const uint8_t* xmx,
+                            int64_t T, const int32_t* sorted, void* ws, const WsLayout& L, bool gate_up,
+                            uint16_t* y_slot) {
+  const int H = c->hidden, I = c->inter;
+  moe::GemvParams g{};
+  g.rows_cap = (int)T;
+  g.limit = c->swiglu_limit;
+  moe::GemvProblem& r = g.p[0];
+  r.tiles = at<moe::GemmTile>(ws, L.tiles);
+  r.tile_count = at<int32_t>(ws, L.tile_count);
+  r.grid_tiles = (int)L.max_tiles;
+  if (gate_up) {  // A = gathered token rows of x, B = W_gu[e] [2I][H], C = h
+    r.gather = sorted;
+    r.gather_div = c->top_k;
+    r.A = x;
+    r.amx = xmx;
+    r.lda = H;
+    r.a_rows = (int)T;
+    r.K = H;
+    r.bq = w->gu_q;
+    r.bs = w->gu_s;
+    r.b_expert_rows = 2 * (int64_t)I;
+    r.b_row_second = I;
+    r.N = I;
+    r.C = at<uint16_t>(ws, L.h);
+    r.ldc = I;
+  } else {  // A = h rows in position order, B = W_dn[e] [H][I], C = y_slot
+    r.A = at<uint16_t>(ws, L.h);
+    r.lda = I;
+    r.a_rows = (int)(T * c->top_k);
+    r.K = I;
+    r.bq = w->dn_q;
+    r.bs = w->dn_s;
+    r.b_expert_rows = H;
+    r.N = H;
+    r.C = y_slot;
+    r.ldc = H;
+  }
+  r.col_tiles = r.N / 16;
+  return g;
+}
+
+moe::GemvParams shared_gemv(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, void* ws,
+                            const WsLayout& L, bool gate_up, uint16_t* y_shared) {
+  const int H = c->hidden, Is = c->shared_inter;
+  moe::GemvParams g{};
+  g.rows_cap = (int)T;
+  g.limit = c->swiglu_limit;
+  moe::GemvProblem& s = g.p[0];
+  s.M = (int)T;
+  s.grid_tiles = 1;
+  s.a_rows = (int)T;
+  if (gate_up) {
+    s.A = x;
+    s.lda = H;
+    s.K = H;
+    s.bh = w->sh_gu;
+    s.b_expert_rows = 2 * (int64_t)Is;
+    s.b_row_second = Is;
+    s.N = Is;
+    s.C = at<uint16_t>(ws, L.h_sh);
+    s.ldc = Is;
+  } else {
+    s.A = at<uint16_t>(ws, L.h_sh);
+    s.lda = Is;
+    s.K = Is;
+    s.bh = w->sh_dn;
+    s.b_expert_rows = H;
+    s.N = H;
+    s.C = y_shared;
+    s.ldc = H;
+  }
+  s.col_tiles = s.N / 16;
+  return g;
+}
+
+moe_status run_shared_decode(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
+                             uint16_t* y_shared, void* ws, const WsLayout& L, hipStream_t st, Timeline* tl) {
+  hipError_t err = moe::launch_expert_gemv(shared_gemv(c, w, x, T, ws, L, true, y_shared), true, false, st);
+  if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
+  err = moe::launch_expert_gemv(shared_gemv(c, w, x, T, ws, L, false, y_shared), false, false, st);
+  if (err == hipSuccess) err = mark(tl, "shared_down", st);
+  if (err != hipSuccess) return fail_hip(err, "shared down launch");
+  return MOE_OK;
+}
+
+moe_status run_experts_decode(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
+                              const int32_t* sorted, uint16_t* y_slot, uint16_t* y_shared, void* ws,
+                              const WsLayout& L, hipStream_t st, Timeline* tl) {
+  hipError_t err =
+      moe::launch_expert_gemv(routed_gemv(c, w, x, nullptr, T, sorted, ws, L, true, y_slot), true, true, st);
+  if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+  err = moe::launch_expert_gemv(routed_gemv(c, w, x, nullptr, T, sorted, ws, L, false, y_slot), false, true, st);
+  if (err == hipSuccess) err = mark(tl, "routed_down", st);
+  if (err != hipSuccess) return fail_hip(err, "routed down launch");
+  if (c->n_shared == 1) return run_shared_decode(c, w, x, T, y_shared, ws, L, st, tl);
+  return MOE_OK;
+}
+
+// Internal side stream of the calling thread for the current device, with
+// fork/join events: the shared expert of the few-token path runs there,
+// beside the router.  Created on first use outside stream capture (default
+// priority, non-blocking) and kept for the life of the process.  NULL when
+// it cannot be created now; the caller then runs everything on its stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false;
+};
+
+SideStream* side_stream(hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = cache[dev];
+  if (ss.ready) return &ss;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    (void)hipStreamDestroy(ss.s);
+    ss = SideStream{};
+    return nullptr;
+  }
+  ss.ready = true;
+  return &ss;
+}
+
+// Few-token layer: router GEMV (scores) -> one-block routing -> routed
+// gate/up -> routed down with the combine folded in; the shared expert runs
+// on the side stream meanwhile and joins before the down projection.  With
+// a timeline (per-kernel timing) every launch goes to the caller's stream.
+moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
+                                uint16_t* y, int32_t* idx, float* wts, void* ws, const WsLayout& L,
+                                hipStream_t st, Timeline* tl) {
+  const int E = c->n_experts;
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  moe::GemmTile* tiles = at<moe::GemmTile>(ws, L.tiles);
+  int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  uint16_t* y_sh = c->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;
+  uint16_t* y_slot = at<uint16_t>(ws, L.y_slot);
+  hipError_t err;
+  moe_status s;
+
+  SideStream* side = (c->n_shared && !tl) ? side_stream(st) : nullptr;
+  if (side) {
+    if ((err = hipEventRecord(side->fork, st)) != hipSuccess) return fail_hip(err, "fork event");
+    if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return fail_hip(err, "fork wait");
+    if ((s = run_shared_decode(c, w, x, T, y_sh, ws, L, side->s, nullptr)) != MOE_OK) return s;
+    if ((err = hipEventRecord(side->join, side->s)) != hipSuccess) return fail_hip(err, "join event");
+  } else if (c->n_shared) {
+    if ((s = run_shared_decode(c, w, x, T, y_sh, ws, L, st, tl)) != MOE_OK) return s;
+  }
+
+  uint8_t* xmx = nullptr;
+  if (L.route_small) {
+    float* scores = at<float>(ws, L.scores);
+    err = moe::launch_router_gemv(x, w->router_w, nullptr, (int)T, E, c->hidden, scores, w->router_bias, st);
+    if (err == hipSuccess) err = mark(tl, "router_logits", st);
+    if (err != hipSuccess) return fail_hip(err, "router launch");
+    xmx = at<uint8_t>(ws, L.xmx);
+    moe::RouteSmallParams rp{};
+    rp.x = x;
+    rp.xmx = xmx;
+    rp.scores = scores;
+    rp.tokens = (int)T;
+    rp.n_experts = E;
+    rp.hidden = c->hidden;
+    rp.top_k = c->top_k;
+    rp.route_scale = c->route_scale;
+    rp.idx = idx;
+    rp.w = wts;
+    rp.sorted_slots = sorted;
+    rp.slot_pos = slot_pos;
+    rp.tiles = tiles;
+    rp.tile_count = tile_count;
+    rp.max_tiles = (int)L.max_tiles;
+    err = moe::launch_route_small(rp, st);
+    if (err == hipSuccess) err = mark(tl, "route_permute", st);
+    if (err != hipSuccess) return fail_hip(err, "routing launch");
+  } else {
+    float* logits = at<float>(ws, L.logits);
+    err = moe::launch_router_gemv(x, w->router_w, logits, (int)T, E, c->hidden, nullptr, nullptr, st);
+    if (err == hipSuccess) err = mark(tl, "router_logits", st);
+    if (err != hipSuccess) return fail_hip(err, "router launch");
+    err = moe::launch_route_permute_small(logits, 1, w->router_bias, (int)T, E, c->top_k, c->route_scale, idx, wts,
+                                          nullptr, at<int32_t>(ws, L.offsets), sorted, slot_pos, L.bm,
+                                          (int)L.max_tiles, tiles, tile_count, st);
+    if (err == hipSuccess) err = mark(tl, "route_permute", st);
+    if (err != hipSuccess) return fail_hip(err, "routing launch");
+  }
+
+  err = moe::launch_expert_gemv(routed_gemv(c, w, x, xmx, T, sorted, ws, L, true, y_slot), true, true, st);
+  if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+  if (side && (err = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return fail_hip(err, "join wait");
+
+  if (L.down_combine) {
+    moe::DownCombineParams dp{};
+    dp.h = at<uint16_t>(ws, L.h);
+    dp.tiles = tiles;
+    dp.tile_count = tile_count;
+    dp.sorted_slots = sorted;
+    dp.topk_w = wts;
+    dp.dn_q = w->dn_q;
+    dp.dn_s = w->dn_s;
+    dp.y_shared = y_sh;
+    dp.y = y;
+    dp.tokens = (int)T;
+    dp.top_k = c->top_k;
+    dp.n_experts = E;
+    dp.hidden = c->hidden;
+    dp.inter = c->inter;
+    err = moe::launch_down_combine(dp, st);
+    if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
+    if (err != hipSuccess) return fail_hip(err, "down/combine launch");
+    return MOE_OK;
+  }
+  err = moe::launch_expert_gemv(routed_gemv(c, w, x, nullptr, T, sorted, ws, L, false, y_slot), false, true, st);
+  if (err == hipSuccess) err = mark(tl, "routed_down", st);
+  if (err != hipSuccess) return fail_hip(err, "routed down launch");
+  err = moe::launch_combine(y_slot, slot_pos, wts, y_sh, (int)T, c->top_k, c->hidden, y, st);
+  if (err == hipSuccess) err = mark(tl, "combine", st);
+  if (err != hipSuccess) return fail_hip(err, "combine launch");
   return MOE_OK;
 }
 
@@ -198,6 +467,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
                        hipStream_t st, Timeline* tl) {
   const int H = c->hidden, I = c->inter;
   uint16_t* h = at<uint16_t>(ws, L.h);
+  if (L.decode) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
   moe::GemmParams p{};
   p.tiles = at<moe::GemmTile>(ws, L.tiles);
   p.tile_count = at<int32_t>(ws, L.tile_count);
@@ -327,7 +597,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const uin
   if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
   if (tokens == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err = moe::launch_tile_table(expert_offsets, cfg->n_experts, (int)(tokens * cfg->top_k), 16 * L.gemm_mt,
+  hipError_t err = moe::launch_tile_table(expert_offsets, cfg->n_experts, (int)(tokens * cfg->top_k), L.bm, (int)L.max_tiles,
                                           at<moe::GemmTile>(ws, L.tiles), at<int32_t>(ws, L.tile_count), st);
   if (err != hipSuccess) return fail_hip(err, "tile table launch");
   return run_experts(cfg, w, x, tokens, sorted_slots, y_slot, y_shared, ws, L, st, nullptr);
@@ -366,10 +636,11 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   if (tokens == 0) return MOE_OK;
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
-  if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  if (L.decode) return layer_forward_decode(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
+  if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
   if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;
   uint16_t* y_slot = at<uint16_t>(ws, L.y_slot);
   uint16_t* y_sh = cfg->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;

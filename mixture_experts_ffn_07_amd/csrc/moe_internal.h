@@ -17,6 +17,11 @@ RouterPlan router_plan(int64_t tokens, int n_experts, int hidden);
 // partial logits [ksplit][T][E] fp32
 hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const float* router_w, float* part,
                                 int tokens, int n_experts, int hidden, hipStream_t stream);
+// few tokens: full fp32 logits [T][E] by a weight-streaming GEMV (logits optional);
+// with `scores` non-null also s = sqrtsoftplus(l) at scores[t][e] and
+// u = s + bias[e] at scores[T + t][e] (bias optional)
+hipError_t launch_router_gemv(const uint16_t* x, const float* router_w, float* logits, int tokens, int n_experts,
+                              int hidden, float* scores, const float* bias, hipStream_t stream);
 // sum of the partials, sqrtsoftplus, biased top-k, weights
 hipError_t launch_router_topk(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
                               int top_k, float route_scale, int32_t* idx, float* w, float* gap,
@@ -42,11 +47,12 @@ struct PermuteScratch {
 // Stable counting sort of the flat slots by expert; optionally also writes
 // the tile table for a grouped GEMM with `bm` rows per tile (tiles != NULL).
 hipError_t launch_permute(const int32_t* idx, int n, int n_experts, const PermuteScratch& s,
-                          int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, int bm, GemmTile* tiles,
-                          int32_t* tile_count, hipStream_t stream);
+                          int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, int bm, int max_tiles,
+                          GemmTile* tiles, int32_t* tile_count, hipStream_t stream);
 // Tile table from expert offsets alone.
-hipError_t launch_tile_table(const int32_t* offsets, int n_experts, int n_total, int bm, GemmTile* tiles,
-                             int32_t* tile_count, hipStream_t stream);
+// At most max_tiles tiles are written (the size of the tile array).
+hipError_t launch_tile_table(const int32_t* offsets, int n_experts, int n_total, int bm, int max_tiles,
+                             GemmTile* tiles, int32_t* tile_count, hipStream_t stream);
 
 // ---------------------------------------------------------------- expert GEMMs
 struct GemmParams {
@@ -76,6 +82,85 @@ struct GemmParams {
 int expert_gemm_mt(int64_t n_rows, int n_groups);
 hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, bool fp4, int mt, int64_t grid_tiles,
                               hipStream_t stream);
+
+// Few-token (decode) projections: up to two problems in one launch.
+struct GemvProblem {
+  const GemmTile* tiles;       // grouped problem (routed experts); NULL: dense rows [0, M)
+  const int32_t* tile_count;
+  int M;
+  int grid_tiles;              // grid.x blocks reserved for this problem (0: absent)
+  const int32_t* gather;       // A row of position p: gather[p] / gather_div, else p
+  int gather_div;
+  const uint16_t* A;
+  int64_t lda;
+  int a_rows;
+  const uint8_t* amx;          // MXFP4 problems: A rows already in two-term MXFP8 form
+                               // (stride mx_row_bytes(K)), else NULL and A is converted
+  int K;
+  const uint8_t* bq;           // MXFP4 codes (NULL: bf16 weights in bh)
+  const uint8_t* bs;
+  const uint16_t* bh;
+  int64_t b_expert_rows;
+  int b_row_second;
+  int N;
+  int col_tiles;               // N / 16
+  uint16_t* C;
+  int64_t ldc;
+};
+struct GemvParams {
+  GemvProblem p[2];
+  int rows_cap;  // rows per tile (<= 16), also rows staged in LDS
+  float limit;
+};
+size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4);
+// Both problems of one launch have the same weight format (fp4: MXFP4 in bq/bs, else bf16 in bh).
+hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream);
+
+// One-block routing of T tokens with T * top_k <= 64 from the scores of
+// launch_router_gemv: top-k and weights, the stable permutation and the
+// tile table (one tile per selected expert); also the two-term MXFP8 rows
+// of x (xmx, stride mx_row_bytes(hidden)) when xmx is non-null.
+struct RouteSmallParams {
+  const uint16_t* x;
+  uint8_t* xmx;
+  const float* scores;  // [2][T][E]
+  int tokens, n_experts, hidden, top_k;
+  float route_scale;
+  int32_t* idx;
+  float* w;
+  int32_t* sorted_slots;
+  int32_t* slot_pos;
+  GemmTile* tiles;
+  int32_t* tile_count;
+  int max_tiles;
+};
+constexpr int kRouteSmallMaxSlots = 64;
+hipError_t launch_route_small(const RouteSmallParams& p, hipStream_t stream);
+
+// Routed down projection with the combine folded in, for T <= 8 tokens whose
+// T * top_k rows of h fit in LDS: y[t] = y_shared[t] + sum_j w[t][j] o[t][j].
+struct DownCombineParams {
+  const uint16_t* h;           // [T*k][inter] bf16, position order
+  const GemmTile* tiles;
+  const int32_t* tile_count;
+  const int32_t* sorted_slots;
+  const float* topk_w;         // [T][k]
+  const uint8_t* dn_q;
+  const uint8_t* dn_s;
+  const uint16_t* y_shared;    // [T][hidden] or NULL
+  uint16_t* y;                 // [T][hidden]
+  int tokens, top_k, n_experts, hidden, inter;
+};
+constexpr int kDownCombineMaxTokens = 8;
+constexpr int kDownCombineMaxInter = 2560;
+size_t down_combine_lds_bytes(int tokens, int top_k, int inter);
+hipError_t launch_down_combine(const DownCombineParams& p, hipStream_t stream);
+
+// Fused few-token routing: top-k of every token + permutation + tile table (T*k <= 1024).
+hipError_t launch_route_permute_small(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
+                                      int top_k, float route_scale, int32_t* idx, float* w, float* gap,
+                                      int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, int bm,
+                                      int max_tiles, GemmTile* tiles, int32_t* tile_count, hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(const uint16_t* y_slot, const int32_t* slot_pos, const float* w, const uint16_t* y_shared,

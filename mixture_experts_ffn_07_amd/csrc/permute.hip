@@ -16,54 +16,9 @@
 // When T*k fits one chunk all three run in one block of one launch.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "permute_device.h"
 
 namespace moe {
-
-__device__ __forceinline__ int clamp_expert(int e, int n_experts) {
-  return e < 0 ? 0 : (e >= n_experts ? n_experts - 1 : e);
-}
-
-__device__ __forceinline__ int bits_for(int n_experts) {
-  int b = 0;
-  while ((1 << b) < n_experts) ++b;
-  return b;
-}
-
-// Within-wave stable rank of this lane's expert id and the number of lanes
-// sharing it; lanes with ok == false take part in no match.
-__device__ __forceinline__ void wave_match_rank(int e, bool ok, int ebits, int* rank, int* count) {
-  const int lane = threadIdx.x & 63;
-  uint64_t mask = __ballot(ok);
-  for (int b = 0; b < ebits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t m = __ballot(ok && bit);
-    mask &= bit ? m : ~m;
-  }
-  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  *rank = __popcll(mask & lower);
-  *count = __popcll(mask);
-}
-
-// Chunk-local ranks.  cnt: shared [16][E] uint16.  Returns this thread's rank
-// within the chunk (valid only when f < n).
-__device__ __forceinline__ int chunk_rank(const int32_t* __restrict__ idx, int n, int n_experts, int chunk,
-                                          uint16_t* cnt, int* e_out) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 16 * n_experts; i += blockDim.x) cnt[i] = 0;
-  __syncthreads();
-  const int f = chunk * kPermuteChunk + tid;
-  const bool ok = f < n;
-  const int e = ok ? clamp_expert(idx[f], n_experts) : 0;
-  int rk, c;
-  wave_match_rank(e, ok, bits_for(n_experts), &rk, &c);
-  if (ok && rk == 0) cnt[wave * n_experts + e] = (uint16_t)c;
-  __syncthreads();
-  int before = 0;
-  if (ok)
-    for (int w = 0; w < wave; ++w) before += cnt[w * n_experts + e];
-  *e_out = e;
-  return before + rk;
-}
 
 __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __restrict__ idx, int n, int n_experts,
                                                              int32_t* __restrict__ rank,
@@ -78,32 +33,6 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
     for (int w = 0; w < 16; ++w) tot += cnt[w * n_experts + ee];
     chunk_counts[(size_t)blockIdx.x * n_experts + ee] = tot;
   }
-}
-
-// Tile table of a grouped GEMM: expert e's run [off_e, off_e + count_e) cut
-// into tiles of bm rows.  Called by every thread of one block with
-// this thread's (count, offset) for expert tid (count 0 for tid >= E).
-// Offsets and counts are clamped into [0, n_total] and at most max_tiles
-// tiles are written, so an inconsistent caller-supplied offset table cannot
-// lead to an access outside the tile table or the row range.
-__device__ __forceinline__ void write_tile_table(int count, int offset, int n_experts, int bm, int n_total,
-                                                 int max_tiles, GemmTile* __restrict__ tiles,
-                                                 int32_t* __restrict__ tile_count, int* scan_scratch) {
-  const int e = threadIdx.x;
-  offset = min(max(offset, 0), n_total);
-  count = min(max(count, 0), n_total - offset);
-  const int nt = (e < n_experts) ? (count + bm - 1) / bm : 0;
-  int total;
-  const int start = block_exclusive_scan(nt, scan_scratch, &total);
-  for (int i = 0; i < nt && start + i < max_tiles; ++i) {
-    GemmTile t;
-    t.e = e;
-    t.m_begin = offset + i * bm;
-    t.m_end = min(offset + (i + 1) * bm, offset + count);
-    t.pad = 0;
-    tiles[start + i] = t;
-  }
-  if (threadIdx.x == 0) *tile_count = min(total, max_tiles);
 }
 
 __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks,
@@ -150,28 +79,7 @@ __global__ __launch_bounds__(1024) void permute_single_kernel(const int32_t* __r
                                                               GemmTile* __restrict__ tiles,
                                                               int32_t* __restrict__ tile_count) {
   extern __shared__ uint16_t cnt[];  // [16][E] uint16, then [E] int32 offsets
-  __shared__ int scratch[16];
-  int32_t* off_sh = reinterpret_cast<int32_t*>(cnt + ((16 * n_experts + 1) & ~1));
-  int e;
-  const int r = chunk_rank(idx, n, n_experts, 0, cnt, &e);
-  const int ee = threadIdx.x;
-  int total = 0;
-  if (ee < n_experts)
-    for (int w = 0; w < 16; ++w) total += cnt[w * n_experts + ee];
-  const int excl = block_exclusive_scan(ee < n_experts ? total : 0, scratch, nullptr);
-  if (ee < n_experts) {
-    offsets[ee] = excl;
-    off_sh[ee] = excl;
-  }
-  if (ee == 0) offsets[n_experts] = n;
-  __syncthreads();
-  const int f = threadIdx.x;
-  if (f < n) {
-    const int pos = off_sh[e] + r;
-    sorted_slots[pos] = f;
-    slot_pos[f] = pos;
-  }
-  if (tiles) write_tile_table(total, excl, n_experts, bm, n, max_tiles, tiles, tile_count, scratch);
+  permute_block(idx, n, n_experts, cnt, offsets, sorted_slots, slot_pos, bm, max_tiles, tiles, tile_count);
 }
 
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int n_experts, int bm,
@@ -188,29 +96,29 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 }
 
 hipError_t launch_permute(const int32_t* idx, int n, int n_experts, const PermuteScratch& s, int32_t* offsets,
-                          int32_t* sorted_slots, int32_t* slot_pos, int bm, GemmTile* tiles, int32_t* tile_count,
-                          hipStream_t stream) {
+                          int32_t* sorted_slots, int32_t* slot_pos, int bm, int max_tiles, GemmTile* tiles,
+                          int32_t* tile_count, hipStream_t stream) {
   const size_t cnt_bytes = (size_t)16 * n_experts * sizeof(uint16_t);
   if (n <= kPermuteChunk) {
-    const size_t shm = ((cnt_bytes + 3) & ~(size_t)3) + (size_t)n_experts * sizeof(int32_t) + 4;
+    const size_t shm = permute_block_lds_bytes(n_experts);
     hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(1024), shm, stream, idx, n, n_experts, offsets,
-                       sorted_slots, slot_pos, bm, (int)max_gemm_tiles(n, n_experts, bm), tiles, tile_count);
+                       sorted_slots, slot_pos, bm, max_tiles, tiles, tile_count);
     return hipGetLastError();
   }
   const int nchunks = permute_chunks(n);
   hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(1024), cnt_bytes, stream, idx, n, n_experts, s.rank,
                      s.chunk_counts);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, s.chunk_counts, nchunks, n_experts, n,
-                     s.chunk_base, offsets, bm, (int)max_gemm_tiles(n, n_experts, bm), tiles, tile_count);
+                     s.chunk_base, offsets, bm, max_tiles, tiles, tile_count);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, idx, n, n_experts, s.rank,
                      s.chunk_base, sorted_slots, slot_pos);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_table(const int32_t* offsets, int n_experts, int n_total, int bm, GemmTile* tiles,
-                             int32_t* tile_count, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream, offsets, n_experts, bm, n_total,
-                     (int)max_gemm_tiles(n_total, n_experts, bm), tiles, tile_count);
+hipError_t launch_tile_table(const int32_t* offsets, int n_experts, int n_total, int bm, int max_tiles,
+                             GemmTile* tiles, int32_t* tile_count, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream, offsets, n_experts, bm, n_total, max_tiles,
+                     tiles, tile_count);
   return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@
 // K-step give an fp32-accumulated dot product of the exact products.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "permute_device.h"
+#include "topk_device.h"
 
 #include <math.h>
 
@@ -103,100 +105,112 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// (u, e) ranks above (bu, be): larger u, or equal u and lower index.
-__device__ __forceinline__ bool ranks_above(float u, int e, float bu, int be) {
-  return u > bu || (u == bu && e < be);
-}
-
-// One wave per token.  Lane l holds experts l, l+64, ... (at most 16 each).
-// Top-k by k rounds of a wave-wide arg-max under ranks_above; round k+1
-// gives the next score for the tie gap.  NaN scores rank as -inf, so the
-// selection is always k distinct valid experts.
+// One wave per token.
+template <int MPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part, int ksplit,
                                                           const float* __restrict__ bias, int tokens,
                                                           int n_experts, int top_k, float route_scale,
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out, float* __restrict__ gap_out) {
-  constexpr int kMaxPerLane = 16;  // n_experts <= 1024
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= tokens) return;
-  float s[kMaxPerLane], u[kMaxPerLane];
-  uint32_t valid = 0;
+  topk_token<MPL>(part + (size_t)t * n_experts, ksplit, (int64_t)tokens * n_experts, bias, n_experts, top_k,
+                  route_scale, idx_out + (size_t)t * top_k, w_out + (size_t)t * top_k,
+                  gap_out ? gap_out + t : nullptr, nullptr);
+}
+
+// Few tokens: logits as a weight-streaming GEMV on the vector ALUs.  One
+// wave per expert reads its fp32 router row once (1 KB per load
+// instruction across the wave, all loads of a 5120-wide row in flight) and
+// accumulates x . w for every token in fp32, lane partials added by a fixed
+// butterfly.  Equal router rows give bit-equal logits.
+// With `scores` non-null it also writes s = sqrtsoftplus(l) to scores[t][e]
+// and the selection score s + bias[e] to scores[T + t][e] (bias optional),
+// so that the top-k that follows only compares.
+template <int KV>  // 4-float loads per lane held in registers per pass
+__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr, float* __restrict__ logits,
+                                                          int tokens, int n_experts, int hidden,
+                                                          float* __restrict__ scores,
+                                                          const float* __restrict__ bias) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  if (e >= n_experts) return;
+  // raw buffer loads: a vector past the end of the row reads zero, so every
+  // load issues unconditionally
+  const uint32_t row_bytes = (uint32_t)hidden * 4;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wr + (size_t)e * hidden), (short)0, (int)row_bytes,
+                                        0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, (int)((uint32_t)tokens * hidden * 2), 0x00020000);
+  const int nv = hidden / 4;  // 4-float vectors per row
+  for (int t = 0; t < tokens; t += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int v0 = 0; v0 < nv; v0 += 64 * KV) {
+      f32x4_t w[KV];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const int e = lane + 64 * j;
-    s[j] = 0.f;
-    u[j] = -INFINITY;
-    if (e < n_experts) {
-      float l = 0.f;
-      for (int zz = 0; zz < ksplit; ++zz) l += part[((size_t)zz * tokens + t) * n_experts + e];
-      const float sp = fmaxf(l, 0.f) + log1pf(expf(-fabsf(l)));
-      s[j] = sqrtf(sp);
-      float uu = s[j] + (bias ? bias[e] : 0.f);
-      u[j] = (uu != uu) ? -INFINITY : uu;
-      valid |= 1u << j;
-    }
-  }
-  float sel_s[16];
-  int sel_e[16];
-  float u_kth = 0.f, gap = INFINITY;
-  const int rounds = top_k < n_experts ? top_k + 1 : top_k;
-  for (int r = 0; r < rounds; ++r) {
-    float bu = -INFINITY;
-    int be = 0x7fffffff;
+      for (int i = 0; i < KV; ++i) {
+        const int v = v0 + 64 * i + lane;
+        const uint32_t off = v < nv ? (uint32_t)v * 16u : 0x7ffffff0u;
+        w[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+      }
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      if ((valid >> j) & 1u) {
-        const int e = lane + 64 * j;
-        if (ranks_above(u[j], e, bu, be)) {
-          bu = u[j];
-          be = e;
+      for (int tt = 0; tt < 4; ++tt) {
+        if (t + tt >= tokens) break;  // wave-uniform
+        uint32_t xv[KV][2];
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          const int v = v0 + 64 * i + lane;
+          const uint32_t off = v < nv ? ((uint32_t)(t + tt) * hidden + 4u * v) * 2u : 0x7ffffff0u;
+          const auto d = __builtin_amdgcn_raw_buffer_load_b64(rx, (int)off, 0, 0);
+          xv[i][0] = d[0];
+          xv[i][1] = d[1];
+        }
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][0] & 0xffffu)), w[i][0], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][0] >> 16)), w[i][1], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][1] & 0xffffu)), w[i][2], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][1] >> 16)), w[i][3], acc[tt]);
         }
       }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ou = __shfl_xor(bu, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ranks_above(ou, oe, bu, be)) {
-        bu = ou;
-        be = oe;
+    for (int tt = 0; tt < 4; ++tt) {
+      float v = acc[tt];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0 && t + tt < tokens) {
+        if (logits) logits[(size_t)(t + tt) * n_experts + e] = v;
+        if (scores) {
+          const float s = sqrtsoftplus(v);
+          scores[(size_t)(t + tt) * n_experts + e] = s;
+          scores[(size_t)(tokens + t + tt) * n_experts + e] = s + (bias ? bias[e] : 0.f);
+        }
       }
     }
-    if (r == top_k) {
-      gap = u_kth - bu;
-      break;
-    }
-    // winner's unbiased score, broadcast from its owner lane
-    const int jw = be >> 6;
-    float mine = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) mine = (j == jw) ? s[j] : mine;
-    const float sw = __shfl(mine, be & 63, 64);
-    if (lane == (be & 63)) valid &= ~(1u << jw);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (q == r) {
-        sel_s[q] = sw;
-        sel_e[q] = be;
-      }
-    }
-    u_kth = bu;
   }
-  if (lane != 0) return;
-  float total = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (r < top_k) total += sel_s[r];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < top_k) {
-      idx_out[(size_t)t * top_k + r] = sel_e[r];
-      w_out[(size_t)t * top_k + r] = total > 0.f ? route_scale * sel_s[r] / total : route_scale / (float)top_k;
-    }
-  }
-  if (gap_out) gap_out[t] = gap;
+}
+
+// Few tokens (T*k <= 1024): top-k of every token, then the permutation and
+// the grouped-GEMM tile table, in one block of 1024 threads.
+template <int MPL>
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const float* __restrict__ part, int ksplit, const float* __restrict__ bias, int tokens, int n_experts, int top_k,
+    float route_scale, int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ gap_out,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos, int bm,
+    int max_tiles, GemmTile* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+  extern __shared__ uint16_t cnt[];
+  __shared__ int32_t idx_sh[1024];
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < tokens; t += 16)
+    topk_token<MPL>(part + (size_t)t * n_experts, ksplit, (int64_t)tokens * n_experts, bias, n_experts, top_k,
+                    route_scale, idx_out + (size_t)t * top_k, w_out + (size_t)t * top_k,
+                    gap_out ? gap_out + t : nullptr, idx_sh + t * top_k);
+  __syncthreads();
+  permute_block(idx_sh, tokens * top_k, n_experts, cnt, offsets, sorted_slots, slot_pos, bm, max_tiles, tiles,
+                tile_count);
 }
 
 RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
@@ -207,6 +221,7 @@ RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
   const int nchunks = (hidden + 127) / 128;
   int64_t want = (512 + etiles * ttiles - 1) / (etiles * ttiles);  // aim for ~512 blocks
   if (want < 1) want = 1;
+  if (want > 8) want = 8;  // the top-k adds the partials; keep that short
   if (want > nchunks) want = nchunks;
   p.chunks_per_split = (int)((nchunks + want - 1) / want);
   p.ksplit = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
@@ -225,12 +240,39 @@ hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const
   return hipGetLastError();
 }
 
+hipError_t launch_router_gemv(const uint16_t* x, const float* router_w, float* logits, int tokens, int n_experts,
+                              int hidden, float* scores, const float* bias, hipStream_t stream) {
+  hipLaunchKernelGGL(router_gemv_kernel<20>, dim3(n_experts), dim3(64), 0, stream, x, router_w, logits,
+                     tokens, n_experts, hidden, scores, bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_small(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
+                                      int top_k, float route_scale, int32_t* idx, float* w, float* gap,
+                                      int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, int bm,
+                                      int max_tiles, GemmTile* tiles, int32_t* tile_count, hipStream_t stream) {
+  const int nj = (n_experts + 63) / 64;
+  auto kern = nj <= 2 ? route_permute_small_kernel<2>
+              : nj <= 4 ? route_permute_small_kernel<4>
+              : nj <= 8 ? route_permute_small_kernel<8>
+                        : route_permute_small_kernel<16>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(1024), permute_block_lds_bytes(n_experts), stream, part, ksplit, bias, tokens,
+                     n_experts, top_k, route_scale, idx, w, gap, offsets, sorted_slots, slot_pos, bm, max_tiles, tiles,
+                     tile_count);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_topk(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
                               int top_k, float route_scale, int32_t* idx, float* w, float* gap,
                               hipStream_t stream) {
   dim3 grid((tokens + 3) / 4);
-  hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, stream, part, ksplit, bias, tokens, n_experts, top_k,
-                     route_scale, idx, w, gap);
+  const int nj = (n_experts + 63) / 64;
+  auto kern = nj <= 2 ? router_topk_kernel<2>
+              : nj <= 4 ? router_topk_kernel<4>
+              : nj <= 8 ? router_topk_kernel<8>
+                        : router_topk_kernel<16>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, part, ksplit, bias, tokens, n_experts, top_k, route_scale, idx,
+                     w, gap);
   return hipGetLastError();
 }
 

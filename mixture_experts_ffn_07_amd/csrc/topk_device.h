@@ -1,0 +1,134 @@
+// Per-token top-k of the router (one wave per token), shared by the router
+// kernels and the few-token routing kernel.
+//
+// Score s = sqrtsoftplus(l); selection score u = s + bias (bias only
+// chooses, the weights use s); the k experts of largest u, ties to the lower
+// index; weights route_scale * s / sum of the selected s (checkpoint
+// config.json on the "DeepSeek V4.1" atlas page: score_func, route_scale).
+#pragma once
+
+#include <math.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+// sqrtsoftplus(l) = sqrt(log(1 + e^l)), written as sqrt(max(l, 0) + log1p(e^-|l|)).
+__device__ __forceinline__ float sqrtsoftplus(float l) { return sqrtf(fmaxf(l, 0.f) + log1pf(expf(-fabsf(l)))); }
+
+// (u, e) ranks above (bu, be): larger u, or equal u and lower index.
+__device__ __forceinline__ bool ranks_above(float u, int e, float bu, int be) {
+  return u > bu || (u == bu && e < be);
+}
+
+// Top-k of one token by one wave.  Lane l holds experts l, l+64, ... (at
+// most 16 each); logit e is the sum of `ksplit` partials at
+// part[z * part_stride + e], added in z order.  Top-k is k rounds of a
+// wave-wide arg-max under ranks_above; round k+1 gives the next score for
+// the tie gap.  NaN scores rank as -inf, so the selection is always k
+// distinct valid experts.  Lane r < k writes selection r to idx_row/w_row
+// (and idx_lds when non-null); lane 0 writes *gap_out when non-null.
+// With FROM_SCORES, `part` holds the scores s and `sel` the selection scores
+// u of this token (computed by the router kernel) and ksplit/bias are unused.
+template <int kMaxPerLane, bool FROM_SCORES = false>  // ceil(n_experts / 64) rounded up; at most 16
+__device__ __forceinline__ void topk_token(const float* __restrict__ part, int ksplit, int64_t part_stride,
+                                           const float* __restrict__ bias, int n_experts, int top_k,
+                                           float route_scale, int32_t* __restrict__ idx_row,
+                                           float* __restrict__ w_row, float* __restrict__ gap_out,
+                                           int32_t* idx_lds, const float* __restrict__ sel = nullptr) {
+  const int lane = threadIdx.x & 63;
+  float s[kMaxPerLane], u[kMaxPerLane];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    s[j] = 0.f;
+    if (lane + 64 * j < n_experts) valid |= 1u << j;
+  }
+  if constexpr (FROM_SCORES) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = min(lane + 64 * j, n_experts - 1);
+      s[j] = part[e];
+      const float uu = sel[e];
+      u[j] = ((valid >> j) & 1u) && uu == uu ? uu : -INFINITY;
+    }
+  } else {
+  // Partial sums, z in order.  The loads of one z are unconditional (expert
+  // index clamped into range; unused slots are dropped below), so they all
+  // issue before the first wait.
+  const int nj = (n_experts + 63) / 64;
+  for (int zz = 0; zz < ksplit; ++zz) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (j < nj) s[j] += part[zz * part_stride + min(lane + 64 * j, n_experts - 1)];
+  }
+  // u holds the bias until the scores are known
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) u[j] = (bias && j < nj) ? bias[min(lane + 64 * j, n_experts - 1)] : 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    if ((valid >> j) & 1u) {
+      s[j] = sqrtsoftplus(s[j]);
+      const float uu = s[j] + u[j];
+      u[j] = (uu != uu) ? -INFINITY : uu;
+    } else {
+      u[j] = -INFINITY;
+    }
+  }
+  }
+  // selection r is kept by lane r (k <= 16)
+  float my_s = 0.f;
+  int my_e = 0;
+  float u_kth = 0.f, gap = INFINITY;
+  const int rounds = top_k < n_experts ? top_k + 1 : top_k;
+  for (int r = 0; r < rounds; ++r) {
+    float bu = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if ((valid >> j) & 1u) {
+        const int e = lane + 64 * j;
+        if (ranks_above(u[j], e, bu, be)) {
+          bu = u[j];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ou = __shfl_xor(bu, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      if (ranks_above(ou, oe, bu, be)) {
+        bu = ou;
+        be = oe;
+      }
+    }
+    if (r == top_k) {
+      gap = u_kth - bu;
+      break;
+    }
+    // winner's unbiased score, broadcast from its owner lane
+    const int jw = be >> 6;
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) mine = (j == jw) ? s[j] : mine;
+    const float sw = __shfl(mine, be & 63, 64);
+    if (lane == (be & 63)) valid &= ~(1u << jw);
+    if (lane == r) {
+      my_s = sw;
+      my_e = be;
+    }
+    u_kth = bu;
+  }
+  // sum of the selected scores in selection order, then each lane r < k writes selection r
+  float total = 0.f;
+  for (int r = 0; r < top_k; ++r) total += __shfl(my_s, r, 64);
+  if (lane < top_k) {
+    idx_row[lane] = my_e;
+    if (idx_lds) idx_lds[lane] = my_e;
+    w_row[lane] = total > 0.f ? route_scale * my_s / total : route_scale / (float)top_k;
+  }
+  if (gap_out && lane == 0) *gap_out = gap;
+}
+
+}  // namespace moe

@@ -21,7 +21,8 @@ def test_library_loads_and_exports_every_header_function():
     lib = moe.load()
     names = moe.header_functions()
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-                          "moe_layer_forward", "moe_status_str", "moe_last_error", "moe_abi_version"}
+                          "moe_layer_forward", "moe_layer_forward_timed", "moe_status_str", "moe_last_error",
+                          "moe_abi_version"}
     for n in names:
         assert hasattr(lib, n)
     dyn = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -157,6 +158,17 @@ def test_zero_tokens_is_a_no_op():
     assert lib.moe_expert_ffn(r(c), r(w), P, 0, P, P, P, P, P, big, None) == OK
     assert lib.moe_combine(r(c), P, P, P, P, 0, P, None) == OK
     assert lib.moe_layer_forward(r(c), r(w), P, 0, P, None, None, P, big, None) == OK
+
+
+def test_timed_forward_argument_checks():
+    lib = moe.load()
+    c, w, r, big = _cfg(), _weights(), ctypes.byref, 1 << 40
+    ms = (ctypes.c_float * 4)()
+    names = (ctypes.c_char_p * 4)()
+    n = ctypes.c_int32(-1)
+    assert lib.moe_layer_forward_timed(r(c), r(w), P, 8, P, P, big, None, None, names, 4, r(n)) == INVALID
+    assert lib.moe_layer_forward_timed(r(c), r(w), P, 8, P, P, big, None, ms, None, 4, r(n)) == INVALID
+    assert lib.moe_layer_forward_timed(r(c), r(w), P, 8, P, P, big, None, ms, names, -1, r(n)) == INVALID
 
 
 def test_binding_raises_with_status_and_message():

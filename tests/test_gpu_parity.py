@@ -121,10 +121,11 @@ def test_permute_bit_exact(t, e, k, skew):
 # ------------------------------------------------------------------ experts and combine
 
 
-@pytest.mark.parametrize("variant", ["tiny", "ragged_k", "no_shared", "min_dims"])
+@pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims"])
 def test_expert_ffn(variant):
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
+           "decode_t3": base.with_(tokens=3),
            "ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224),
            "no_shared": base.with_(tokens=16, n_shared=0, shared_inter=0),
            "min_dims": base.with_(tokens=20, hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2)}[variant]
@@ -184,6 +185,14 @@ def test_layer_decode_t1_full():
     inp = make_inputs(CONFIGS["decode_t1_h5120_e384"], seed=0, device=DEV)
     stats, ref, _ = _check_layer(inp)
     print("decode_t1:", stats, "experts", ref["idx"].tolist())
+
+
+@pytest.mark.parametrize("tokens", [2, 6, 7])
+def test_layer_decode_few_tokens_full(tokens):
+    """Few-token decode at full size: T <= 6 takes the weight-streaming path, T = 7 the general one."""
+    inp = make_inputs(CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens), seed=3, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print(f"decode T={tokens}:", stats, "near-tie alternatives", len(alt))
 
 
 def _sample(n, count, seed, must=()):
