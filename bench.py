@@ -90,6 +90,9 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
         "combine": n * h * 2 + t * h * 2 * 2 + n * 8,
         # few tokens: routed down projection with the weighted combine and the shared output folded in
         "routed_down_combine": touched * dn_expert + n * i * 2 + n * 8 + t * h * 2 * 2,
+        # few tokens: the shared expert's projections run inside the router and routing launches
+        "router_shared_gate_up": e * h * 4 + t * h * 2 + t * e * 4 + 2 * i_s * h * 2 + t * i_s * 2,
+        "route_shared_down": t * e * 4 + n * 8 + n * 4 * 2 + h * i_s * 2 + t * i_s * 2 + t * h * 2,
         # few-token path: routed and shared experts share a launch, routing is one fused kernel
         "route_permute": t * e * 4 + n * 8 + n * 4 * 2 + (e + 1) * 4,
         "gate_up": touched * gu_expert + 2 * i_s * h * 2 + t * h * 2 + n * i * 2 + t * i_s * 2,

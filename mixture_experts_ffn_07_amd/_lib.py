@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_ffn.so")
+# MOE_FFN_LIB selects another build of the same library (same ABI)
+LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_PKG, "libmoe_ffn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_ffn.h")
 
 MOE_OK = 0

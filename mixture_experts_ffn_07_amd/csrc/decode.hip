@@ -1,9 +1,12 @@
-// Few-token (decode) kernels that sit around the weight-streaming projections:
-//   route_small_kernel   -- one block: two-term MXFP8 form of x for the
-//                           routed gate/up, top-k of every token from the
-//                           scores the router GEMV computed, and (one wave)
-//                           the stable permutation and tile table of the
-//                           T*k <= 64 slots;
+// Few-token (decode) kernels around the routed weight-streaming projection:
+//   decode_front_kernel  -- the router GEMV (scores) beside the shared
+//                           expert's gate/up projection;
+//   decode_mid_kernel    -- the routing block beside the shared expert's
+//                           down projection.  The routing block computes the
+//                           two-term MXFP8 form of x for the routed gate/up,
+//                           the top-k of every token from the scores, and
+//                           (one wave) the stable permutation and tile table
+//                           of the T*k <= 64 slots;
 //   down_combine_kernel  -- T <= 8: routed down projection with the weighted
 //                           combine folded in (token-major: one block per 16
 //                           output columns visits every selected expert and
@@ -15,13 +18,14 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "mx_device.h"
-#include "topk_device.h"
+#include "router_device.h"
+#include "gemv_bf16_device.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------- routing
 template <int MPL>
-__global__ __launch_bounds__(256) void route_small_kernel(RouteSmallParams p) {
+__device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   __shared__ int32_t idx_sh[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = p.tokens * p.top_k;
@@ -88,150 +92,250 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallParams p) {
   if (lane == 0) *p.tile_count = min((int)__popcll(firsts), p.max_tiles);
 }
 
-hipError_t launch_route_small(const RouteSmallParams& p, hipStream_t stream) {
+// Launch 1 of the few-token layer: the shared expert's gate/up blocks
+// (longest first), then the router GEMV, one expert per wave.
+__global__ __launch_bounds__(256) void decode_front_kernel(FrontParams f) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int shared_blocks = f.shared.grid_tiles * f.shared.col_tiles;
+  if ((int)blockIdx.x < shared_blocks) {
+    gemv_bf16_block<true>(f.shared, blockIdx.x, f.rows_cap, f.limit, lds);
+    return;
+  }
+  const int e = ((int)blockIdx.x - shared_blocks) * 4 + (int)(threadIdx.x >> 6);
+  router_gemv_wave(f.x, f.router_w, nullptr, f.tokens, f.n_experts, f.hidden, f.scores, f.bias, e);
+}
+
+// Launch 2: the routing block (block 0), then the shared expert's down
+// projection blocks.
+template <int MPL>
+__global__ __launch_bounds__(256) void decode_mid_kernel(RouteSmallParams p, GemvProblem shared_down, int rows_cap) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  if (blockIdx.x == 0) {
+    route_small_block<MPL>(p);
+    return;
+  }
+  gemv_bf16_block<false>(shared_down, (int)blockIdx.x - 1, rows_cap, 0.f, lds);
+}
+
+hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream) {
+  const int shared_blocks = f.shared.grid_tiles * f.shared.col_tiles;
+  const dim3 grid((unsigned)(shared_blocks + (f.n_experts + 3) / 4));
+  const size_t shm = shared_blocks ? gemv_bf16_lds_bytes(f.rows_cap, f.shared.K) : 0;
+  hipLaunchKernelGGL(decode_front_kernel, grid, dim3(256), shm, stream, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& shared_down, int rows_cap,
+                             hipStream_t stream) {
   const int nj = (p.n_experts + 63) / 64;
-  auto kern = nj <= 2 ? route_small_kernel<2>
-              : nj <= 4 ? route_small_kernel<4>
-              : nj <= 8 ? route_small_kernel<8>
-                        : route_small_kernel<16>;
-  hipLaunchKernelGGL(kern, dim3(1), dim3(256), 0, stream, p);
+  auto kern = nj <= 2 ? decode_mid_kernel<2>
+              : nj <= 4 ? decode_mid_kernel<4>
+              : nj <= 8 ? decode_mid_kernel<8>
+                        : decode_mid_kernel<16>;
+  const int shared_blocks = shared_down.grid_tiles * shared_down.col_tiles;
+  const size_t shm = shared_blocks ? gemv_bf16_lds_bytes(rows_cap, shared_down.K) : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + shared_blocks)), dim3(256), shm, stream, p, shared_down, rows_cap);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- down + combine
 namespace {
 
-constexpr int kDcChunks = 5;  // 128-wide chunks per wave per expert (inter <= 2560)
-
-struct DcBatch {
-  u32x4_t q[kDcChunks];
-  uint32_t s[kDcChunks];
+// The 4 waves split K in groups of G consecutive 128-wide chunks (group j
+// to wave j % 4), so one scale load of 4G bytes covers a group's scales.
+template <int G>
+struct DcShape {
+  static constexpr int kMaxChunks = kDownCombineMaxInter / 128;
+  static constexpr int kGroups = (kMaxChunks + 4 * G - 1) / (4 * G);  // per wave
 };
 
-__device__ __forceinline__ void dc_load(DcBatch& b, const DownCombineParams& p, int tile, int tc, int n0, int col,
-                                        int wave, int grp, const int32_t* tile_e) {
+template <int G>
+struct DcTile {
+  u32x4_t q[DcShape<G>::kGroups][G];
+  uint32_t s[DcShape<G>::kGroups][G];
+};
+
+// Tiles (experts) per batch; two batches are in flight.
+constexpr int kDcTiles = 1;
+template <int G>
+struct DcBatch {
+  DcTile<G> t[kDcTiles];
+};
+
+template <int G>
+__device__ __forceinline__ void dc_load(DcTile<G>& b, const DownCombineParams& p, bool tile_ok, int e, int n0,
+                                        int col, int wave, int grp) {
   const int nchunks = (p.inter + 127) / 128;
-  const bool tile_ok = tile < tc;
-  const int e = tile_ok ? tile_e[tile] : 0;
   const uint32_t qbytes = (uint32_t)p.hidden * (uint32_t)(p.inter / 2);
   const uint32_t sbytes = (uint32_t)p.hidden * (uint32_t)(p.inter / 32);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.dn_q + (int64_t)e * qbytes, qbytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dn_s + (int64_t)e * sbytes, sbytes);
   const uint32_t row = (uint32_t)(n0 + col);
+  const uint32_t qrow = row * (uint32_t)(p.inter / 2), srow = row * (uint32_t)(p.inter / 32);
 #pragma unroll
-  for (int u = 0; u < kDcChunks; ++u) {
-    const int c = wave + 4 * u;
-    const int k0 = c * 128 + grp * 32;
-    const bool ok = tile_ok && c < nchunks && k0 < p.inter;
-    const uint32_t qo = ok ? row * (uint32_t)(p.inter / 2) + (uint32_t)(k0 / 2) : kOob;
-    const uint32_t so = ok ? row * (uint32_t)(p.inter / 32) + (uint32_t)(k0 / 32) : kOob;
-    b.q[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
-    b.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
+  for (int j = 0; j < DcShape<G>::kGroups; ++j) {
+    const int c0 = (wave + 4 * j) * G;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int c = c0 + u;
+      const bool ok = tile_ok && c < nchunks && c * 128 + grp * 32 < p.inter;
+      const uint32_t qo = ok ? qrow + (uint32_t)(c * 64 + grp * 16) : kOob;
+      b.q[j][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
+    }
+    const uint32_t so = (tile_ok && c0 < nchunks) ? srow + (uint32_t)(4 * c0) : kOob;
+    if constexpr (G == 4) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)so, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b.s[j][u] = w[u];
+    } else if constexpr (G == 2) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)so, 0, 0);
+      b.s[j][0] = w[0];
+      b.s[j][1] = w[1];
+    } else {
+      const bool ok = tile_ok && c0 < nchunks && c0 * 128 + grp * 32 < p.inter;
+      const uint32_t sob = ok ? srow + (uint32_t)(4 * c0 + grp) : kOob;
+      b.s[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)sob, 0, 0) << (8 * grp);
+    }
+  }
+}
+
+// Tiles t0 .. t0 + kDcTiles - 1 (loads past the last tile read zero).
+template <int G>
+__device__ __forceinline__ void dc_load_batch(DcBatch<G>& b, const DownCombineParams& p, int t0, int tc,
+                                              const int32_t* tile_e, int n0, int col, int wave, int grp) {
+#pragma unroll
+  for (int i = 0; i < kDcTiles; ++i) {
+    const int t = t0 + i;
+    dc_load<G>(b.t[i], p, t < tc, tile_e[min(t, 63)], n0, col, wave, grp);
   }
 }
 
 }  // namespace
 
-// grid: hidden / 16 blocks of 256 threads.  The 4 waves split the inter
-// dimension; each wave keeps per-token partial sums of w * o for its 16
-// columns, added over the experts in tile (expert id) order; the partials
-// of the 4 lane groups and 4 waves are added in a fixed order at the end,
-// then the shared expert's output.
+// grid: hidden / 16 blocks of 256 threads.  The 4 waves split K; each wave
+// keeps per-token partial sums of w * o for its 16 columns, added over the
+// experts in tile (expert id) order while the next two experts' weights
+// stream in; the partials of the 4 lane groups and 4 waves are added in a
+// fixed order at the end, then the shared expert's output.
+template <int G>
 __global__ __launch_bounds__(256) void down_combine_kernel(DownCombineParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // n staged MXFP8 rows of h
   __shared__ int32_t tile_e[64], tile_b[64], tile_r[64];
   __shared__ int32_t slot_tok[64];
   __shared__ float slot_w[64];
+  __shared__ int32_t tile_n;
   __shared__ float red[4][4][kDownCombineMaxTokens][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int n = p.tokens * p.top_k;
-  const int tc = min(*p.tile_count, 64);
+  const int K = p.inter, stride = mx_row_bytes(K), nblk = K / 32;
+  // tile table and slot table: every load issued before the first use
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
-    if (t < tc) {
-      const GemmTile tl = p.tiles[t];
-      tile_e[t] = min(max(tl.e, 0), p.n_experts - 1);
-      tile_b[t] = min(max(tl.m_begin, 0), n);
-      tile_r[t] = min(max(tl.m_end - tl.m_begin, 0), n - tile_b[t]);
-    }
-    if (t < n) {
-      const int f = min(max(p.sorted_slots[t], 0), n - 1);  // flat slot at position t
-      slot_tok[t] = f / p.top_k;
-      slot_w[t] = p.topk_w[f];
-    }
+    const int tc = *p.tile_count;
+    GemmTile tl = {0, 0, 0, 0};
+    if (t < p.max_tiles) tl = p.tiles[t];
+    const int f = t < n ? p.sorted_slots[t] : 0;  // flat slot at position t
+    const int fc = min(max(f, 0), n - 1);
+    const float w = t < n ? p.topk_w[fc] : 0.f;
+    if (t == 0) tile_n = min(max(tc, 0), min(p.max_tiles, 64));
+    tile_e[t] = min(max(tl.e, 0), p.n_experts - 1);
+    tile_b[t] = min(max(tl.m_begin, 0), n);
+    tile_r[t] = min(max(tl.m_end - tl.m_begin, 0), n - min(max(tl.m_begin, 0), n));
+    slot_tok[t] = fc / p.top_k;
+    slot_w[t] = w;
   }
-  __syncthreads();
-  DcBatch b0, b1;
-  dc_load(b0, p, 0, tc, n0, col, wave, grp, tile_e);
-  dc_load(b1, p, 1, tc, n0, col, wave, grp, tile_e);
-  // stage h (n rows) as two-term MXFP8
-  {
-    const int nblk = p.inter / 32, stride = mx_row_bytes(p.inter);
-    const int total = n * nblk;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, (uint32_t)n * p.inter * 2);
-    for (int i = threadIdx.x; i < total; i += 256) {
-      const int r = i / nblk, b = i - r * nblk;
-      u32x4_t v[4];
+  // first staging pass of h (one 32-value block per thread) before the sync
+  const int items = n * nblk;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, (uint32_t)n * K * 2);
+  u32x4_t hv[4];
+  auto h_issue = [&](int i) {
+    const int r = i / nblk, b = i - r * nblk;
+    const uint32_t off = i < items ? (uint32_t)((r * K + 32 * b) * 2) : kOob;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)((r * p.inter + 32 * b) * 2), 16 * q, 0));
+    for (int q = 0; q < 4; ++q)
+      hv[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 16 * q, 0));
+  };
+  auto h_commit = [&](int i) {
+    if (i < items) {
+      const int r = i / nblk, b = i - r * nblk;
       float xv[32];
-      unpack_bf16x32(v, xv);
+      unpack_bf16x32(hv, xv);
       uint8_t* row = lds + r * stride;
-      mx_convert_block(xv, row + 32 * b, row + p.inter + 32 * b, row + 2 * p.inter + b);
+      mx_convert_block(xv, row + 32 * b, row + K + 32 * b, row + 2 * K + b);
     }
+  };
+  h_issue(threadIdx.x);
+  __syncthreads();
+  const int tc = tile_n;
+  DcBatch<G> b0, b1;
+  dc_load_batch<G>(b0, p, 0, tc, tile_e, n0, col, wave, grp);
+  dc_load_batch<G>(b1, p, kDcTiles, tc, tile_e, n0, col, wave, grp);
+  h_commit(threadIdx.x);
+  for (int i = threadIdx.x + 256; i < items; i += 256) {
+    h_issue(i);
+    h_commit(i);
   }
   __syncthreads();
 
-  const int nchunks = (p.inter + 127) / 128;
-  const int stride = mx_row_bytes(p.inter);
+  const int nchunks = (K + 127) / 128;
   float yp[kDownCombineMaxTokens];
 #pragma unroll
   for (int t = 0; t < kDownCombineMaxTokens; ++t) yp[t] = 0.f;
-  for (int t = 0; t < tc; t += 2) {
+  for (int t = 0; t < tc; t += 2 * kDcTiles) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int tt = t + half;
-      if (tt >= tc) break;
-      const DcBatch& b = half ? b1 : b0;
-      const int m_begin = tile_b[tt], rows = tile_r[tt];
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const int tb = t + half * kDcTiles;
+      if (tb >= tc) break;
+      const DcBatch<G>& bb = half ? b1 : b0;
 #pragma unroll
-      for (int u = 0; u < kDcChunks; ++u) {
-        const int c = wave + 4 * u;
-        if (c >= nchunks) break;
-        const int kb = c * 128;
+      for (int i = 0; i < kDcTiles; ++i) {
+        const int tt = tb + i;
+        if (tt >= tc) break;
+        const DcTile<G>& b = bb.t[i];
+        const int m_begin = tile_b[tt], rows = tile_r[tt];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         const bool r_ok = col < rows;
         const uint8_t* row = lds + (m_begin + (r_ok ? col : 0)) * stride;
-        const bool h0 = r_ok && kb + 16 * grp < p.inter, h1 = r_ok && kb + 64 + 16 * grp < p.inter;
-        const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
-        const u32x4_t a0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + kb + 16 * grp) : z;
-        const u32x4_t a1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + kb + 64 + 16 * grp) : z;
-        const u32x4_t l0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + p.inter + kb + 16 * grp) : z;
-        const u32x4_t l1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + p.inter + kb + 64 + 16 * grp) : z;
-        const int sa = (r_ok && kb + 32 * grp < p.inter) ? (int)row[2 * p.inter + kb / 32 + grp] : 127;
-        const i32x8_t ahi = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
-        acc = mfma_mx(ahi, b.q[u], sa, (int)b.s[u], acc);
-        acc = mfma_mx(alo, b.q[u], sa, (int)b.s[u], acc);
-      }
-      // refill this buffer two tiles ahead (loads past the last tile read zero)
-      if (half) dc_load(b1, p, tt + 2, tc, n0, col, wave, grp, tile_e);
-      else dc_load(b0, p, tt + 2, tc, n0, col, wave, grp, tile_e);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * grp + i;
-        if (r < rows) {
-          const int pos = m_begin + r;
-          const int tok = slot_tok[pos];
-          const float contrib = slot_w[pos] * acc[i];
+        for (int j = 0; j < DcShape<G>::kGroups; ++j) {
 #pragma unroll
-          for (int t2 = 0; t2 < kDownCombineMaxTokens; ++t2) yp[t2] += tok == t2 ? contrib : 0.f;
+          for (int u = 0; u < G; ++u) {
+            const int c = (wave + 4 * j) * G + u;
+            if (c >= nchunks) break;
+            const int kb = c * 128;
+            const bool h0 = r_ok && kb + 16 * grp < K, h1 = r_ok && kb + 64 + 16 * grp < K;
+            const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+            const u32x4_t a0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + kb + 16 * grp) : z;
+            const u32x4_t a1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + kb + 64 + 16 * grp) : z;
+            const u32x4_t l0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 16 * grp) : z;
+            const u32x4_t l1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 64 + 16 * grp) : z;
+            const int sa = (r_ok && kb + 32 * grp < K) ? (int)row[2 * K + kb / 32 + grp] : 127;
+            const int sb = (int)((b.s[j][u] >> (8 * grp)) & 0xffu);
+            const i32x8_t ahi = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
+                                 (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+            acc = mfma_mx(ahi, b.q[j][u], sa, sb, acc);
+            acc = mfma_mx(alo, b.q[j][u], sa, sb, acc);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * grp + q;
+          if (r < rows) {
+            const int pos = m_begin + r;
+            const int tok = slot_tok[pos];
+            const float contrib = slot_w[pos] * acc[q];
+#pragma unroll
+            for (int t2 = 0; t2 < kDownCombineMaxTokens; ++t2) yp[t2] += tok == t2 ? contrib : 0.f;
+          }
         }
       }
+      // refill this buffer two batches ahead
+      if (half) dc_load_batch<G>(b1, p, tb + 2 * kDcTiles, tc, tile_e, n0, col, wave, grp);
+      else dc_load_batch<G>(b0, p, tb + 2 * kDcTiles, tc, tile_e, n0, col, wave, grp);
     }
   }
 #pragma unroll
@@ -254,8 +358,14 @@ size_t down_combine_lds_bytes(int tokens, int top_k, int inter) {
 }
 
 hipError_t launch_down_combine(const DownCombineParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(down_combine_kernel, dim3(p.hidden / 16), dim3(256),
-                     down_combine_lds_bytes(p.tokens, p.top_k, p.inter), stream, p);
+  const size_t shm = down_combine_lds_bytes(p.tokens, p.top_k, p.inter);
+  const dim3 grid(p.hidden / 16);
+  if (p.inter % 512 == 0)
+    hipLaunchKernelGGL((down_combine_kernel<4>), grid, dim3(256), shm, stream, p);
+  else if (p.inter % 256 == 0)
+    hipLaunchKernelGGL((down_combine_kernel<2>), grid, dim3(256), shm, stream, p);
+  else
+    hipLaunchKernelGGL((down_combine_kernel<1>), grid, dim3(256), shm, stream, p);
   return hipGetLastError();
 }
 

@@ -242,6 +242,7 @@ moe::GemvParams routed_gemv(const moe_config* c, const moe_weights* w, const uin
   if (gate_up) {  // A = gathered token rows of x, B = W_gu[e] [2I][H], C = h
     r.gather = sorted;
     r.gather_div = c->top_k;
+    r.gather_len = (int)(T * c->top_k);
     r.A = x;
     r.amx = xmx;
     r.lda = H;
@@ -329,42 +330,13 @@ moe_status run_experts_decode(const moe_config* c, const moe_weights* w, const u
   return MOE_OK;
 }
 
-// Internal side stream of the calling thread for the current device, with
-// fork/join events: the shared expert of the few-token path runs there,
-// beside the router.  Created on first use outside stream capture (default
-// priority, non-blocking) and kept for the life of the process.  NULL when
-// it cannot be created now; the caller then runs everything on its stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ready = false;
-};
-
-SideStream* side_stream(hipStream_t st) {
-  constexpr int kMaxDevices = 64;
-  thread_local SideStream cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = cache[dev];
-  if (ss.ready) return &ss;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
-    if (ss.fork) (void)hipEventDestroy(ss.fork);
-    (void)hipStreamDestroy(ss.s);
-    ss = SideStream{};
-    return nullptr;
-  }
-  ss.ready = true;
-  return &ss;
-}
-
-// Few-token layer: router GEMV (scores) -> one-block routing -> routed
-// gate/up -> routed down with the combine folded in; the shared expert runs
-// on the side stream meanwhile and joins before the down projection.  With
-// a timeline (per-kernel timing) every launch goes to the caller's stream.
+// Few-token layer.  With T * k <= 64 (one-block routing):
+//   1. router GEMV scores beside the shared expert's gate/up,
+//   2. routing block (top-k, permutation, tiles, MXFP8 x) beside the shared down,
+//   3. routed gate/up (MXFP4 x MXFP8),
+//   4. routed down with the combine folded in (or down, then combine).
+// Otherwise the router GEMV writes logits for the fused top-k + permute
+// kernel and the shared expert gets launches of its own.
 moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
                                 uint16_t* y, int32_t* idx, float* wts, void* ws, const WsLayout& L,
                                 hipStream_t st, Timeline* tl) {
@@ -378,22 +350,23 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   hipError_t err;
   moe_status s;
 
-  SideStream* side = (c->n_shared && !tl) ? side_stream(st) : nullptr;
-  if (side) {
-    if ((err = hipEventRecord(side->fork, st)) != hipSuccess) return fail_hip(err, "fork event");
-    if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return fail_hip(err, "fork wait");
-    if ((s = run_shared_decode(c, w, x, T, y_sh, ws, L, side->s, nullptr)) != MOE_OK) return s;
-    if ((err = hipEventRecord(side->join, side->s)) != hipSuccess) return fail_hip(err, "join event");
-  } else if (c->n_shared) {
-    if ((s = run_shared_decode(c, w, x, T, y_sh, ws, L, st, tl)) != MOE_OK) return s;
-  }
-
   uint8_t* xmx = nullptr;
   if (L.route_small) {
     float* scores = at<float>(ws, L.scores);
-    err = moe::launch_router_gemv(x, w->router_w, nullptr, (int)T, E, c->hidden, scores, w->router_bias, st);
-    if (err == hipSuccess) err = mark(tl, "router_logits", st);
-    if (err != hipSuccess) return fail_hip(err, "router launch");
+    moe::FrontParams f{};
+    f.x = x;
+    f.router_w = w->router_w;
+    f.bias = w->router_bias;
+    f.scores = scores;
+    f.tokens = (int)T;
+    f.n_experts = E;
+    f.hidden = c->hidden;
+    if (c->n_shared) f.shared = shared_gemv(c, w, x, T, ws, L, true, y_sh).p[0];
+    f.rows_cap = (int)T;
+    f.limit = c->swiglu_limit;
+    err = moe::launch_decode_front(f, st);
+    if (err == hipSuccess) err = mark(tl, "router_shared_gate_up", st);
+    if (err != hipSuccess) return fail_hip(err, "router/shared gate-up launch");
     xmx = at<uint8_t>(ws, L.xmx);
     moe::RouteSmallParams rp{};
     rp.x = x;
@@ -411,10 +384,13 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     rp.tiles = tiles;
     rp.tile_count = tile_count;
     rp.max_tiles = (int)L.max_tiles;
-    err = moe::launch_route_small(rp, st);
-    if (err == hipSuccess) err = mark(tl, "route_permute", st);
-    if (err != hipSuccess) return fail_hip(err, "routing launch");
+    moe::GemvProblem sd{};
+    if (c->n_shared) sd = shared_gemv(c, w, x, T, ws, L, false, y_sh).p[0];
+    err = moe::launch_decode_mid(rp, sd, (int)T, st);
+    if (err == hipSuccess) err = mark(tl, "route_shared_down", st);
+    if (err != hipSuccess) return fail_hip(err, "routing/shared down launch");
   } else {
+    if (c->n_shared && (s = run_shared_decode(c, w, x, T, y_sh, ws, L, st, tl)) != MOE_OK) return s;
     float* logits = at<float>(ws, L.logits);
     err = moe::launch_router_gemv(x, w->router_w, logits, (int)T, E, c->hidden, nullptr, nullptr, st);
     if (err == hipSuccess) err = mark(tl, "router_logits", st);
@@ -429,7 +405,6 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   err = moe::launch_expert_gemv(routed_gemv(c, w, x, xmx, T, sorted, ws, L, true, y_slot), true, true, st);
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
-  if (side && (err = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return fail_hip(err, "join wait");
 
   if (L.down_combine) {
     moe::DownCombineParams dp{};
@@ -447,6 +422,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     dp.n_experts = E;
     dp.hidden = c->hidden;
     dp.inter = c->inter;
+    dp.max_tiles = (int)L.max_tiles;
     err = moe::launch_down_combine(dp, st);
     if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
     if (err != hipSuccess) return fail_hip(err, "down/combine launch");

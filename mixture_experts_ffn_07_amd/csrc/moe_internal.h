@@ -91,6 +91,7 @@ struct GemvProblem {
   int grid_tiles;              // grid.x blocks reserved for this problem (0: absent)
   const int32_t* gather;       // A row of position p: gather[p] / gather_div, else p
   int gather_div;
+  int gather_len;              // entries of gather (MXFP4 problems read it with clamped indices)
   const uint16_t* A;
   int64_t lda;
   int a_rows;
@@ -113,7 +114,8 @@ struct GemvParams {
   float limit;
 };
 size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4);
-// Both problems of one launch have the same weight format (fp4: MXFP4 in bq/bs, else bf16 in bh).
+// fp4: one MXFP4 problem (p[0]; tiles of at most rows_cap <= 8 rows, grid over
+// 64-column blocks).  Otherwise up to two dense bf16 problems (bh).
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream);
 
 // One-block routing of T tokens with T * top_k <= 64 from the scores of
@@ -135,7 +137,24 @@ struct RouteSmallParams {
   int max_tiles;
 };
 constexpr int kRouteSmallMaxSlots = 64;
-hipError_t launch_route_small(const RouteSmallParams& p, hipStream_t stream);
+
+// Launch 1 of the few-token layer: router GEMV scores (as launch_router_gemv
+// with scores) beside the shared expert's gate/up (dense bf16 problem,
+// grid_tiles = 1; grid_tiles = 0 when there is no shared expert).
+struct FrontParams {
+  const uint16_t* x;
+  const float* router_w;
+  const float* bias;
+  float* scores;
+  int tokens, n_experts, hidden;
+  GemvProblem shared;
+  int rows_cap;
+  float limit;
+};
+hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream);
+// Launch 2: the one-block routing beside the shared expert's down projection.
+hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& shared_down, int rows_cap,
+                             hipStream_t stream);
 
 // Routed down projection with the combine folded in, for T <= 8 tokens whose
 // T * top_k rows of h fit in LDS: y[t] = y_shared[t] + sum_j w[t][j] o[t][j].
@@ -150,6 +169,7 @@ struct DownCombineParams {
   const uint16_t* y_shared;    // [T][hidden] or NULL
   uint16_t* y;                 // [T][hidden]
   int tokens, top_k, n_experts, hidden, inter;
+  int max_tiles;               // entries of tiles (<= 64)
 };
 constexpr int kDownCombineMaxTokens = 8;
 constexpr int kDownCombineMaxInter = 2560;

@@ -1,5 +1,6 @@
-// Per-token top-k of the router (one wave per token), shared by the router
-// kernels and the few-token routing kernel.
+// Router device code shared by the router kernels and the fused few-token
+// kernels: the weight-streaming logit GEMV (one wave per expert) and the
+// per-token top-k (one wave per token).
 //
 // Score s = sqrtsoftplus(l); selection score u = s + bias (bias only
 // chooses, the weights use s); the k experts of largest u, ties to the lower
@@ -129,6 +130,78 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
     w_row[lane] = total > 0.f ? route_scale * my_s / total : route_scale / (float)top_k;
   }
   if (gap_out && lane == 0) *gap_out = gap;
+}
+
+// Few tokens: logits as a weight-streaming GEMV on the vector ALUs.  One
+// wave per expert reads its fp32 router row once (1 KB per load
+// instruction across the wave, all loads of a 5120-wide row in flight) and
+// accumulates x . w for every token in fp32, lane partials added by a fixed
+// butterfly.  Equal router rows give bit-equal logits.
+// With `scores` non-null it also writes s = sqrtsoftplus(l) to scores[t][e]
+// and the selection score s + bias[e] to scores[T + t][e] (bias optional),
+// so that the top-k that follows only compares.
+// The calling wave computes expert e (wave-uniform; nothing for e >= n_experts).
+template <int KV = 20>  // 4-float loads per lane held in registers per pass
+__device__ __forceinline__ void router_gemv_wave(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                 float* __restrict__ logits, int tokens, int n_experts, int hidden,
+                                                 float* __restrict__ scores, const float* __restrict__ bias, int e) {
+  const int lane = threadIdx.x & 63;
+  if (e >= n_experts) return;
+  // raw buffer loads: a vector past the end of the row reads zero, so every
+  // load issues unconditionally
+  const uint32_t row_bytes = (uint32_t)hidden * 4;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wr + (size_t)e * hidden), (short)0, (int)row_bytes,
+                                        0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, (int)((uint32_t)tokens * hidden * 2), 0x00020000);
+  const int nv = hidden / 4;  // 4-float vectors per row
+  for (int t = 0; t < tokens; t += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int v0 = 0; v0 < nv; v0 += 64 * KV) {
+      f32x4_t w[KV];
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int v = v0 + 64 * i + lane;
+        const uint32_t off = v < nv ? (uint32_t)v * 16u : 0x7ffffff0u;
+        w[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (t + tt >= tokens) break;  // wave-uniform
+        uint32_t xv[KV][2];
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          const int v = v0 + 64 * i + lane;
+          const uint32_t off = v < nv ? ((uint32_t)(t + tt) * hidden + 4u * v) * 2u : 0x7ffffff0u;
+          const auto d = __builtin_amdgcn_raw_buffer_load_b64(rx, (int)off, 0, 0);
+          xv[i][0] = d[0];
+          xv[i][1] = d[1];
+        }
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][0] & 0xffffu)), w[i][0], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][0] >> 16)), w[i][1], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][1] & 0xffffu)), w[i][2], acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32((uint16_t)(xv[i][1] >> 16)), w[i][3], acc[tt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      float v = acc[tt];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0 && t + tt < tokens) {
+        if (logits) logits[(size_t)(t + tt) * n_experts + e] = v;
+        if (scores) {
+          const float s = sqrtsoftplus(v);
+          scores[(size_t)(t + tt) * n_experts + e] = s;
+          scores[(size_t)(tokens + t + tt) * n_experts + e] = s + (bias ? bias[e] : 0.f);
+        }
+      }
+    }
+  }
 }
 
 }  // namespace moe
