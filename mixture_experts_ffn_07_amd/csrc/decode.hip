@@ -88,8 +88,15 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
     tl.pad = 0;
     p.tiles[distinct_smaller] = tl;
   }
+  // token of each tile row (row = rank of the slot among its expert's slots;
+  // an expert has at most T <= 8 rows)
+  if (p.tile_rows && lane < n && distinct_smaller < p.max_tiles && dup_before < kTileRows)
+    p.tile_rows[distinct_smaller * kTileRows + dup_before] = lane / p.top_k;
   const uint64_t firsts = __ballot(first);
-  if (lane == 0) *p.tile_count = min((int)__popcll(firsts), p.max_tiles);
+  const int n_tiles = min((int)__popcll(firsts), p.max_tiles);
+  if (lane == 0) *p.tile_count = n_tiles;
+  // the remaining records are written empty, so readers need not load the count
+  if (lane >= n_tiles && lane < p.max_tiles) p.tiles[lane] = GemmTile{0, 0, 0, 0};
 }
 
 // Launch 1 of the few-token layer: the shared expert's gate/up blocks
@@ -141,30 +148,26 @@ hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& share
 // ---------------------------------------------------------------- down + combine
 namespace {
 
-// The 4 waves split K in groups of G consecutive 128-wide chunks (group j
-// to wave j % 4), so one scale load of 4G bytes covers a group's scales.
+// Work unit = (tile, group of G consecutive 128-wide chunks of K); unit u of
+// the block goes to wave u % 4.  A scale load of 4G bytes covers a group's
+// scales.  kDcUnitRegs bounds the registers of the loads a wave keeps in
+// flight, so one round covers 14 units at G = 2 (all 54 of a block at one
+// token with inter 2304).
+constexpr int kDcUnitRegs = 140;
 template <int G>
 struct DcShape {
-  static constexpr int kMaxChunks = kDownCombineMaxInter / 128;
-  static constexpr int kGroups = (kMaxChunks + 4 * G - 1) / (4 * G);  // per wave
+  static constexpr int kUnits = kDcUnitRegs / (5 * G);  // units per wave per round
 };
 
 template <int G>
-struct DcTile {
-  u32x4_t q[DcShape<G>::kGroups][G];
-  uint32_t s[DcShape<G>::kGroups][G];
-};
-
-// Tiles (experts) per batch; two batches are in flight.
-constexpr int kDcTiles = 1;
-template <int G>
-struct DcBatch {
-  DcTile<G> t[kDcTiles];
+struct DcUnit {
+  u32x4_t q[G];
+  uint32_t s[G];
 };
 
 template <int G>
-__device__ __forceinline__ void dc_load(DcTile<G>& b, const DownCombineParams& p, bool tile_ok, int e, int n0,
-                                        int col, int wave, int grp) {
+__device__ __forceinline__ void dc_load_unit(DcUnit<G>& b, const DownCombineParams& p, bool ok, int e, int g,
+                                             int n0, int col, int grp) {
   const int nchunks = (p.inter + 127) / 128;
   const uint32_t qbytes = (uint32_t)p.hidden * (uint32_t)(p.inter / 2);
   const uint32_t sbytes = (uint32_t)p.hidden * (uint32_t)(p.inter / 32);
@@ -172,64 +175,52 @@ __device__ __forceinline__ void dc_load(DcTile<G>& b, const DownCombineParams& p
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dn_s + (int64_t)e * sbytes, sbytes);
   const uint32_t row = (uint32_t)(n0 + col);
   const uint32_t qrow = row * (uint32_t)(p.inter / 2), srow = row * (uint32_t)(p.inter / 32);
+  const int c0 = g * G;
 #pragma unroll
-  for (int j = 0; j < DcShape<G>::kGroups; ++j) {
-    const int c0 = (wave + 4 * j) * G;
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const int c = c0 + u;
-      const bool ok = tile_ok && c < nchunks && c * 128 + grp * 32 < p.inter;
-      const uint32_t qo = ok ? qrow + (uint32_t)(c * 64 + grp * 16) : kOob;
-      b.q[j][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
-    }
-    const uint32_t so = (tile_ok && c0 < nchunks) ? srow + (uint32_t)(4 * c0) : kOob;
-    if constexpr (G == 4) {
-      const u32x4_t w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)so, 0, 0));
-#pragma unroll
-      for (int u = 0; u < 4; ++u) b.s[j][u] = w[u];
-    } else if constexpr (G == 2) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)so, 0, 0);
-      b.s[j][0] = w[0];
-      b.s[j][1] = w[1];
-    } else {
-      const bool ok = tile_ok && c0 < nchunks && c0 * 128 + grp * 32 < p.inter;
-      const uint32_t sob = ok ? srow + (uint32_t)(4 * c0 + grp) : kOob;
-      b.s[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)sob, 0, 0) << (8 * grp);
-    }
+  for (int u = 0; u < G; ++u) {
+    const int c = c0 + u;
+    const bool okc = ok && c < nchunks && c * 128 + grp * 32 < p.inter;
+    const uint32_t qo = okc ? qrow + (uint32_t)(c * 64 + grp * 16) : kOob;
+    b.q[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
   }
-}
-
-// Tiles t0 .. t0 + kDcTiles - 1 (loads past the last tile read zero).
-template <int G>
-__device__ __forceinline__ void dc_load_batch(DcBatch<G>& b, const DownCombineParams& p, int t0, int tc,
-                                              const int32_t* tile_e, int n0, int col, int wave, int grp) {
+  const uint32_t so = (ok && c0 < nchunks) ? srow + (uint32_t)(4 * c0) : kOob;
+  if constexpr (G == 4) {
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)so, 0, 0));
 #pragma unroll
-  for (int i = 0; i < kDcTiles; ++i) {
-    const int t = t0 + i;
-    dc_load<G>(b.t[i], p, t < tc, tile_e[min(t, 63)], n0, col, wave, grp);
+    for (int u = 0; u < 4; ++u) b.s[u] = w[u];
+  } else if constexpr (G == 2) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)so, 0, 0);
+    b.s[0] = w[0];
+    b.s[1] = w[1];
+  } else {
+    const bool okb = ok && c0 < nchunks && c0 * 128 + grp * 32 < p.inter;
+    const uint32_t sob = okb ? srow + (uint32_t)(4 * c0 + grp) : kOob;
+    b.s[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)sob, 0, 0) << (8 * grp);
   }
 }
 
 }  // namespace
 
-// grid: hidden / 16 blocks of 256 threads.  The 4 waves split K; each wave
-// keeps per-token partial sums of w * o for its 16 columns, added over the
-// experts in tile (expert id) order while the next two experts' weights
-// stream in; the partials of the 4 lane groups and 4 waves are added in a
-// fixed order at the end, then the shared expert's output.
+// grid: hidden / 16 blocks of 256 threads (16 output columns each).  Each
+// wave adds w * (partial product of its units) into per-token sums; the
+// sums of the 4 lane groups and 4 waves are added in a fixed order at the
+// end, then the shared expert's output.
 template <int G>
 __global__ __launch_bounds__(256) void down_combine_kernel(DownCombineParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // n staged MXFP8 rows of h
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // n MX rows of h
   __shared__ int32_t tile_e[64], tile_b[64], tile_r[64];
   __shared__ int32_t slot_tok[64];
   __shared__ float slot_w[64];
   __shared__ int32_t tile_n;
   __shared__ float red[4][4][kDownCombineMaxTokens][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int U = DcShape<G>::kUnits;
+  // the wave index and everything derived from it are wave-uniform: keep them scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int n = p.tokens * p.top_k;
-  const int K = p.inter, stride = mx_row_bytes(K), nblk = K / 32;
+  const int K = p.inter, stride = mx_row_bytes(K), nchunks = (K + 127) / 128;
+  const int ngroups = (nchunks + G - 1) / G;
   // tile table and slot table: every load issued before the first use
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
@@ -246,96 +237,92 @@ __global__ __launch_bounds__(256) void down_combine_kernel(DownCombineParams p) 
     slot_tok[t] = fc / p.top_k;
     slot_w[t] = w;
   }
-  // first staging pass of h (one 32-value block per thread) before the sync
-  const int items = n * nblk;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, (uint32_t)n * K * 2);
-  u32x4_t hv[4];
-  auto h_issue = [&](int i) {
-    const int r = i / nblk, b = i - r * nblk;
-    const uint32_t off = i < items ? (uint32_t)((r * K + 32 * b) * 2) : kOob;
+  // the n MX rows of h (contiguous), first pass issued before the sync
+  constexpr int kPiecesPerThread = 4;
+  const int pieces = n * stride / 16;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.hmx, (uint32_t)(n * stride));
+  u32x4_t hv[kPiecesPerThread];
+  auto h_issue = [&](int base) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      hv[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 16 * q, 0));
-  };
-  auto h_commit = [&](int i) {
-    if (i < items) {
-      const int r = i / nblk, b = i - r * nblk;
-      float xv[32];
-      unpack_bf16x32(hv, xv);
-      uint8_t* row = lds + r * stride;
-      mx_convert_block(xv, row + 32 * b, row + K + 32 * b, row + 2 * K + b);
+    for (int j = 0; j < kPiecesPerThread; ++j) {
+      const int i = base + (int)threadIdx.x + 256 * j;
+      hv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ra, (int)(i < pieces ? (uint32_t)(16 * i) : kOob), 0, 0));
     }
   };
-  h_issue(threadIdx.x);
+  auto h_commit = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kPiecesPerThread; ++j) {
+      const int i = base + (int)threadIdx.x + 256 * j;
+      if (i < pieces) *reinterpret_cast<u32x4_t*>(lds + 16 * i) = hv[j];
+    }
+  };
+  h_issue(0);
   __syncthreads();
-  const int tc = tile_n;
-  DcBatch<G> b0, b1;
-  dc_load_batch<G>(b0, p, 0, tc, tile_e, n0, col, wave, grp);
-  dc_load_batch<G>(b1, p, kDcTiles, tc, tile_e, n0, col, wave, grp);
-  h_commit(threadIdx.x);
-  for (int i = threadIdx.x + 256; i < items; i += 256) {
-    h_issue(i);
-    h_commit(i);
-  }
-  __syncthreads();
+  const int tc = __builtin_amdgcn_readfirstlane(tile_n);
+  const int n_units = tc * ngroups;
 
-  const int nchunks = (K + 127) / 128;
   float yp[kDownCombineMaxTokens];
 #pragma unroll
   for (int t = 0; t < kDownCombineMaxTokens; ++t) yp[t] = 0.f;
-  for (int t = 0; t < tc; t += 2 * kDcTiles) {
+  for (int base = 0; base < n_units; base += 4 * U) {
+    DcUnit<G> b[U];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tb = t + half * kDcTiles;
-      if (tb >= tc) break;
-      const DcBatch<G>& bb = half ? b1 : b0;
+    for (int i = 0; i < U; ++i) {
+      const int u = base + wave + 4 * i;
+      const int t = min(u / ngroups, 63);
+      const int e = __builtin_amdgcn_readfirstlane(tile_e[t]);  // same for the whole wave
+      dc_load_unit<G>(b[i], p, u < n_units, e, u - (u / ngroups) * ngroups, n0, col, grp);
+    }
+    if (base == 0) {  // block-uniform: the staged h is needed from here on
+      h_commit(0);
+      for (int hb = 256 * kPiecesPerThread; hb < pieces; hb += 256 * kPiecesPerThread) {
+        h_issue(hb);
+        h_commit(hb);
+      }
+      __syncthreads();
+    }
 #pragma unroll
-      for (int i = 0; i < kDcTiles; ++i) {
-        const int tt = tb + i;
-        if (tt >= tc) break;
-        const DcTile<G>& b = bb.t[i];
-        const int m_begin = tile_b[tt], rows = tile_r[tt];
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const bool r_ok = col < rows;
-        const uint8_t* row = lds + (m_begin + (r_ok ? col : 0)) * stride;
+    for (int i = 0; i < U; ++i) {
+      const int u = base + wave + 4 * i;
+      if (u >= n_units) break;  // wave-uniform
+      const int tt = u / ngroups, g = u - tt * ngroups;
+      const int m_begin = __builtin_amdgcn_readfirstlane(tile_b[tt]);
+      const int rows = __builtin_amdgcn_readfirstlane(tile_r[tt]);
+      const bool r_ok = col < rows;
+      const uint8_t* row = lds + (m_begin + (r_ok ? col : 0)) * stride;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < DcShape<G>::kGroups; ++j) {
+      for (int uc = 0; uc < G; ++uc) {
+        const int c = g * G + uc;
+        if (c >= nchunks) break;
+        const int kb = c * 128;
+        const bool h0 = r_ok && kb + 16 * grp < K, h1 = r_ok && kb + 64 + 16 * grp < K;
+        const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t a0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + kb + 16 * grp) : z;
+        const u32x4_t a1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + kb + 64 + 16 * grp) : z;
+        const u32x4_t l0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 16 * grp) : z;
+        const u32x4_t l1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 64 + 16 * grp) : z;
+        const int sa = (r_ok && kb + 32 * grp < K) ? (int)row[2 * K + kb / 32 + grp] : 127;
+        const int sb = (int)((b[i].s[uc] >> (8 * grp)) & 0xffu);
+        const i32x8_t ahi = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
+                             (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+        acc = mfma_mx(ahi, b[i].q[uc], sa, sb, acc);
+        acc = mfma_mx(alo, b[i].q[uc], sa, sb, acc);
+      }
 #pragma unroll
-          for (int u = 0; u < G; ++u) {
-            const int c = (wave + 4 * j) * G + u;
-            if (c >= nchunks) break;
-            const int kb = c * 128;
-            const bool h0 = r_ok && kb + 16 * grp < K, h1 = r_ok && kb + 64 + 16 * grp < K;
-            const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
-            const u32x4_t a0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + kb + 16 * grp) : z;
-            const u32x4_t a1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + kb + 64 + 16 * grp) : z;
-            const u32x4_t l0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 16 * grp) : z;
-            const u32x4_t l1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 64 + 16 * grp) : z;
-            const int sa = (r_ok && kb + 32 * grp < K) ? (int)row[2 * K + kb / 32 + grp] : 127;
-            const int sb = (int)((b.s[j][u] >> (8 * grp)) & 0xffu);
-            const i32x8_t ahi = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
-                                 (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
-            acc = mfma_mx(ahi, b.q[j][u], sa, sb, acc);
-            acc = mfma_mx(alo, b.q[j][u], sa, sb, acc);
-          }
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * grp + q;
+        if (r < rows) {
+          const int pos = m_begin + r;
+          const int tok = slot_tok[pos];
+          const float contrib = slot_w[pos] * acc[q];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 4 * grp + q;
-          if (r < rows) {
-            const int pos = m_begin + r;
-            const int tok = slot_tok[pos];
-            const float contrib = slot_w[pos] * acc[q];
-#pragma unroll
-            for (int t2 = 0; t2 < kDownCombineMaxTokens; ++t2) yp[t2] += tok == t2 ? contrib : 0.f;
-          }
+          for (int t2 = 0; t2 < kDownCombineMaxTokens; ++t2) yp[t2] += tok == t2 ? contrib : 0.f;
         }
       }
-      // refill this buffer two batches ahead
-      if (half) dc_load_batch<G>(b1, p, tb + 2 * kDcTiles, tc, tile_e, n0, col, wave, grp);
-      else dc_load_batch<G>(b0, p, tb + 2 * kDcTiles, tc, tile_e, n0, col, wave, grp);
     }
   }
 #pragma unroll

@@ -58,7 +58,8 @@ struct MxView {
 // SW = bytes per scale load: 16 (K % 512 == 0), 8 (K % 256 == 0), 4
 // (K % 128 == 0) or 1 (one byte per lane and chunk, any K % 32 == 0).  The
 // wider loads bring the scales of 4, 2 or 1 chunks for all 4 lane groups
-// at once; the row offsets are then multiples of the load width.
+// at once; the row offsets are then multiples of the load width.  SW = 0:
+// the block staged all its rows' scales in LDS once (no scale loads here).
 template <int NB, int SW>
 __device__ __forceinline__ void mx_load(MxBatch<NB>& b, const MxView& v, int c0, int grp) {
 #pragma unroll
@@ -73,7 +74,9 @@ __device__ __forceinline__ void mx_load(MxBatch<NB>& b, const MxView& v, int c0,
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    if constexpr (SW == 16) {
+    if constexpr (SW == 0) {
+      // scales staged in LDS by the block
+    } else if constexpr (SW == 16) {
 #pragma unroll
       for (int h = 0; h < kMxChunks / 4; ++h) {
         const int c = c0 + 4 * h;
@@ -112,9 +115,10 @@ __device__ __forceinline__ void mx_load(MxBatch<NB>& b, const MxView& v, int c0,
 
 // Two block-scaled MFMAs (hi and lo activation terms) per chunk and row set.
 // `row` is this lane's staged MX row (tile row `col`), r_ok = col < rows.
-template <int NB>
+// srow_lds: this lane's row scales in LDS (SW = 0), per NB at stride sl_stride.
+template <int NB, int SW>
 __device__ __forceinline__ void mx_mma(const MxBatch<NB>& b, f32x4_t (&acc)[NB], const uint8_t* row, bool r_ok,
-                                       int c0, const MxView& v, int grp) {
+                                       int c0, const MxView& v, int grp, const uint8_t* srow_lds, int sl_stride) {
   const int K = v.K;
 #pragma unroll
   for (int u = 0; u < kMxChunks; ++u) {
@@ -132,81 +136,70 @@ __device__ __forceinline__ void mx_mma(const MxBatch<NB>& b, f32x4_t (&acc)[NB],
     const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int sb = (int)((b.s[u][nb] >> (8 * grp)) & 0xffu);
+      const int sb = SW == 0 ? (int)srow_lds[nb * sl_stride + kb / 32 + grp]
+                             : (int)((b.s[u][nb] >> (8 * grp)) & 0xffu);
       acc[nb] = mfma_mx(ahi, b.q[u][nb], sa, sb, acc[nb]);
       acc[nb] = mfma_mx(alo, b.q[u][nb], sa, sb, acc[nb]);
     }
   }
 }
 
-// MX staging of the tile's rows into LDS (row stride mx_row_bytes(K)).
-// Copy mode (p.amx): 16-byte pieces of pre-converted rows, 3 per thread per
-// pass.  Convert mode: one 32-value block of bf16 per thread per pass.
+// MX staging of one tile row into LDS (row stride mx_row_bytes(K)), in passes.
+// Copy mode (p.amx): 16-byte pieces of a pre-converted row, 3 per thread per
+// pass.  Convert mode: one 32-value block of bf16 per thread per pass.  The
+// source row `sr` is uniform, so no per-lane row lookup is needed.
 struct MxStage {
   u32x4_t v[4];
 };
 
-__device__ __forceinline__ void mx_stage_issue(const GemvProblem& p, const int (&src)[8], int rows, int pass,
-                                               MxStage& s) {
+template <bool AMX>
+__device__ __forceinline__ int mx_row_passes(const GemvProblem& p) {
+  return AMX ? (mx_row_bytes(p.K) / 16 + 767) / 768 : (p.K / 32 + 255) / 256;
+}
+
+template <bool AMX>
+__device__ __forceinline__ void mx_row_issue(const GemvProblem& p, int sr, int pass, MxStage& s) {
   const int K = p.K, stride = mx_row_bytes(K);
-  if (p.amx) {
-    const int pieces = stride / 16, total = rows * pieces;
+  if constexpr (AMX) {
+    const int pieces = stride / 16;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.amx, (uint32_t)((int64_t)p.a_rows * stride));
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int i = pass * 768 + (int)threadIdx.x + 256 * j;
-      int r = 0;
-#pragma unroll
-      for (int rr = 1; rr < 8; ++rr) r += i >= rr * pieces;
-      int sr = src[0];
-#pragma unroll
-      for (int rr = 1; rr < 8; ++rr) sr = rr == r ? src[rr] : sr;
-      const uint32_t off = i < total ? (uint32_t)(sr * stride + 16 * (i - r * pieces)) : kOob;
+      const int q = pass * 768 + (int)threadIdx.x + 256 * j;
+      const uint32_t off = q < pieces ? (uint32_t)(sr * stride + 16 * q) : kOob;
       s.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0));
     }
   } else {
-    const int nblk = K / 32, total = rows * nblk;
-    const int i = pass * 256 + (int)threadIdx.x;
-    int r = 0;
-#pragma unroll
-    for (int rr = 1; rr < 8; ++rr) r += i >= rr * nblk;
-    int sr = src[0];
-#pragma unroll
-    for (int rr = 1; rr < 8; ++rr) sr = rr == r ? src[rr] : sr;
+    const int nblk = K / 32;
+    const int b = pass * 256 + (int)threadIdx.x;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)p.a_rows * p.lda * 2));
-    const uint32_t off = i < total ? (uint32_t)(((int64_t)sr * p.lda + 32 * (i - r * nblk)) * 2) : kOob;
+    const uint32_t off = b < nblk ? (uint32_t)(((int64_t)sr * p.lda + 32 * b) * 2) : kOob;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       s.v[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 16 * q, 0));
   }
 }
 
-__device__ __forceinline__ void mx_stage_commit(const GemvProblem& p, int rows, int pass, const MxStage& s,
-                                                uint8_t* lds) {
+template <bool AMX>
+__device__ __forceinline__ void mx_row_commit(const GemvProblem& p, int r, int pass, const MxStage& s,
+                                              uint8_t* lds) {
   const int K = p.K, stride = mx_row_bytes(K);
-  if (p.amx) {
-    const int total = rows * (stride / 16);
+  uint8_t* row = lds + r * stride;
+  if constexpr (AMX) {
+    const int pieces = stride / 16;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int i = pass * 768 + (int)threadIdx.x + 256 * j;
-      if (i < total) *reinterpret_cast<u32x4_t*>(lds + 16 * i) = s.v[j];  // rows are contiguous
+      const int q = pass * 768 + (int)threadIdx.x + 256 * j;
+      if (q < pieces) *reinterpret_cast<u32x4_t*>(row + 16 * q) = s.v[j];
     }
   } else {
-    const int nblk = K / 32, total = rows * nblk;
-    const int i = pass * 256 + (int)threadIdx.x;
-    if (i < total) {
-      const int r = i / nblk, b = i - r * nblk;
+    const int b = pass * 256 + (int)threadIdx.x;
+    if (b < K / 32) {
       float x[32];
       unpack_bf16x32(s.v, x);
-      uint8_t* row = lds + r * stride;
       mx_convert_block(x, row + 32 * b, row + K + 32 * b, row + 2 * K + b);
     }
   }
-}
-
-__device__ __forceinline__ int mx_stage_passes(const GemvProblem& p, int rows) {
-  const int K = p.K;
-  return p.amx ? (rows * (mx_row_bytes(K) / 16) + 767) / 768 : (rows * (K / 32) + 255) / 256;
 }
 
 }  // namespace
@@ -231,15 +224,28 @@ __global__ __launch_bounds__(256) void expert_gemv_bf16_kernel(GemvParams prm) {
 // row of each tile row (gathered positions: one more scalar round trip).
 // The first staging pass is issued before the weight prefetch, so the
 // staged rows are in LDS by the time the first weights arrive.
-template <int NB, int SW>
+// AMX: the activation rows come pre-converted (p.amx), else bf16 rows (p.A)
+// are converted while staging.
+template <int NB, int SW, bool AMX>
 __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int rows_cap, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int tile = blockIdx.x % p.grid_tiles;
-  const int n0 = (blockIdx.x / p.grid_tiles) * 64 + wave * 16;
+  const int nblk0 = (blockIdx.x / p.grid_tiles) * 64;  // first output column of the block
+  const int n0 = nblk0 + wave * 16;
   int e = 0, m_begin, rows;
-  if (p.tiles) {
+  int src[kTileRows];
+  if (p.tile_rows) {
+    // every tile record is written (unused ones empty): record and rows are
+    // independent scalar loads, no count needed
+    const GemmTile tl = p.tiles[tile];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = p.tile_rows[tile * kTileRows + r];
+    e = tl.e;
+    m_begin = tl.m_begin;
+    rows = min(tl.m_end, tl.m_begin + rows_cap) - m_begin;
+  } else if (p.tiles) {
     const int tc = *p.tile_count;
     const GemmTile tl = p.tiles[tile];
     if (tile >= tc) return;
@@ -251,15 +257,17 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
     rows = min(rows_cap, p.M - m_begin);
   }
   if (rows <= 0) return;
-  int src[8];
-  if (p.gather) {
+  if (p.tile_rows) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) src[r] = p.gather[min(max(m_begin + r, 0), p.gather_len - 1)];
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(src[r], 0), p.a_rows - 1);
+  } else if (p.gather) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) src[r] = min(max(src[r] / p.gather_div, 0), p.a_rows - 1);
+    for (int r = 0; r < kTileRows; ++r) src[r] = p.gather[min(max(m_begin + r, 0), p.gather_len - 1)];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(src[r] / p.gather_div, 0), p.a_rows - 1);
   } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) src[r] = min(max(m_begin + r, 0), p.a_rows - 1);
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(m_begin + r, 0), p.a_rows - 1);
   }
 
   const int K = p.K;
@@ -278,18 +286,48 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
     v.srow[nb] = n_ok ? r * (uint32_t)(K / 32) : kOob;
   }
 
+  // staging loads (activation rows; with SW = 0 also the scales of the
+  // block's 64 rows per gate/up half) go out before the weight prefetch
+  const int a_bytes = rows_cap * mx_row_bytes(K);
+  const int sl_stride = 64 * (K / 32);  // LDS bytes of one half's scales
   MxStage st;
-  mx_stage_issue(p, src, rows, 0, st);
-  __builtin_amdgcn_sched_barrier(0);  // staging loads go out before the weight prefetch
+  mx_row_issue<AMX>(p, src[0], 0, st);
+  constexpr int kScalePieces = SW == 0 ? 5 * NB : 1;  // 16-byte pieces per thread (K <= 5120 with SW = 0)
+  u32x4_t sv[kScalePieces];
+  if constexpr (SW == 0) {
+    const int pieces = sl_stride / 16;  // per half
+#pragma unroll
+    for (int j = 0; j < kScalePieces; ++j) {
+      const int i = (int)threadIdx.x + 256 * j;
+      const int nb = i / pieces, q = i - nb * pieces;
+      const uint32_t off = (nb < NB && q < pieces)
+                               ? (uint32_t)(nblk0 + nb * p.b_row_second) * (uint32_t)(K / 32) + 16u * q
+                               : kOob;
+      sv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(v.s, (int)off, 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   MxBatch<NB> b0, b1;
   mx_load<NB, SW>(b0, v, 0, grp);
   mx_load<NB, SW>(b1, v, kMxChunks, grp);
   __builtin_amdgcn_sched_barrier(0);
-  mx_stage_commit(p, rows, 0, st, lds);
-  const int passes = mx_stage_passes(p, rows);
-  for (int pass = 1; pass < passes; ++pass) {
-    mx_stage_issue(p, src, rows, pass, st);
-    mx_stage_commit(p, rows, pass, st, lds);
+  mx_row_commit<AMX>(p, 0, 0, st, lds);
+  if constexpr (SW == 0) {
+    const int pieces = sl_stride / 16;
+#pragma unroll
+    for (int j = 0; j < kScalePieces; ++j) {
+      const int i = (int)threadIdx.x + 256 * j;
+      if (i < NB * pieces) *reinterpret_cast<u32x4_t*>(lds + a_bytes + 16 * i) = sv[j];
+    }
+  }
+  const int passes = mx_row_passes<AMX>(p);
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) {
+    if (r >= rows) break;  // block-uniform
+    for (int pass = r == 0 ? 1 : 0; pass < passes; ++pass) {
+      mx_row_issue<AMX>(p, src[r], pass, st);
+      mx_row_commit<AMX>(p, r, pass, st, lds);
+    }
   }
   __syncthreads();
 
@@ -298,15 +336,229 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bool r_ok = col < rows;
   const uint8_t* row = lds + (r_ok ? col : 0) * mx_row_bytes(K);
+  const uint8_t* srow_lds = lds + a_bytes + (wave * 16 + col) * (K / 32);
   constexpr int CB = kMxChunks;
   for (int c = 0; c < v.nchunks; c += 2 * CB) {
-    mx_mma<NB>(b0, acc, row, r_ok, c, v, grp);
+    mx_mma<NB, SW>(b0, acc, row, r_ok, c, v, grp, srow_lds, sl_stride);
     if (c + CB >= v.nchunks) break;
     mx_load<NB, SW>(b0, v, c + 2 * CB, grp);
-    mx_mma<NB>(b1, acc, row, r_ok, c + CB, v, grp);
+    mx_mma<NB, SW>(b1, acc, row, r_ok, c + CB, v, grp, srow_lds, sl_stride);
     mx_load<NB, SW>(b1, v, c + 3 * CB, grp);
   }
+  if (NB == 2 && p.cmx) {
+    // two-term MXFP8 output rows (stride mx_row_bytes(N)): the block's 64
+    // columns are two 32-value blocks per row, gathered through LDS
+    __shared__ float hout[kTileRows][64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * grp + i;
+      if (r < rows && r < kTileRows) hout[r][wave * 16 + col] = clamped_swiglu(acc[0][i], acc[NB - 1][i], limit);
+    }
+    __syncthreads();
+    const int t = threadIdx.x, r = t >> 1, c0 = nblk0 + 32 * (t & 1);
+    if (t < 2 * kTileRows && r < rows && c0 < p.N) {
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = hout[r][32 * (t & 1) + j];
+      uint8_t* dst = p.cmx + (int64_t)(m_begin + r) * mx_row_bytes(p.N);
+      mx_convert_block(x, dst + c0, dst + p.N + c0, dst + 2 * p.N + c0 / 32);
+    }
+    return;
+  }
   if (!n_ok) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * grp + i;
+    if (r < rows) {
+      const float o = NB == 2 ? clamped_swiglu(acc[0][i], acc[NB - 1][i], limit) : acc[0][i];
+      p.C[(int64_t)(m_begin + r) * p.ldc + n0 + col] = f32_to_bf16(o);
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------- MXFP4 split-K kernel
+// Block = one tile x 16 output columns.  Its W waves split K into
+// contiguous ranges of CPW 128-wide chunks and each wave issues all the
+// weight loads of its range at once (CPW * NB 16-byte loads per lane).  The
+// block stages the tile's activation rows and its weight rows' scales in
+// LDS; the partial tiles of the waves are added in wave order through LDS.
+// Many light blocks keep more memory requests in flight across the chip
+// than a few deep ones: a streaming read of 75 MB takes ~20 us with 216
+// four-wave blocks and ~14-15 us with 1000 or more.
+template <int CPW>
+__device__ __forceinline__ int splitk_waves(int K) {
+  return ((K + 127) / 128 + CPW - 1) / CPW;
+}
+
+__device__ __forceinline__ size_t splitk_scale_bytes(int nb, int K) { return (size_t)nb * 16 * (K / 32); }
+
+template <int NB, int CPW, bool AMX>
+__global__ __launch_bounds__(512) void expert_gemv_splitk_kernel(GemvProblem p, int rows_cap, float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nthreads = blockDim.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tile = blockIdx.x % p.grid_tiles;
+  const int n0 = (blockIdx.x / p.grid_tiles) * 16;
+  int e = 0, m_begin, rows;
+  int src[kTileRows];
+  if (p.tile_rows) {
+    const GemmTile tl = p.tiles[tile];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = p.tile_rows[tile * kTileRows + r];
+    e = tl.e;
+    m_begin = tl.m_begin;
+    rows = min(tl.m_end, tl.m_begin + rows_cap) - m_begin;
+  } else if (p.tiles) {
+    const int tc = *p.tile_count;
+    const GemmTile tl = p.tiles[tile];
+    if (tile >= tc) return;
+    e = tl.e;
+    m_begin = tl.m_begin;
+    rows = min(tl.m_end, tl.m_begin + rows_cap) - m_begin;
+  } else {
+    m_begin = tile * rows_cap;
+    rows = min(rows_cap, p.M - m_begin);
+  }
+  if (rows <= 0) return;
+  if (p.tile_rows) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(src[r], 0), p.a_rows - 1);
+  } else if (p.gather) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = p.gather[min(max(m_begin + r, 0), p.gather_len - 1)];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(src[r] / p.gather_div, 0), p.a_rows - 1);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) src[r] = min(max(m_begin + r, 0), p.a_rows - 1);
+  }
+
+  const int K = p.K, nchunks = (K + 127) / 128, stride = mx_row_bytes(K), ks = K / 32;
+  const int a_bytes = rows_cap * stride;
+  const int s_bytes = (int)splitk_scale_bytes(NB, K);
+  uint8_t* s_lds = lds + a_bytes;                                   // [NB][16 rows][ks]
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + a_bytes + ((s_bytes + 15) & ~15));  // [W-1][NB][64]
+  const uint32_t qbytes = (uint32_t)(p.b_expert_rows * (K / 2));
+  const uint32_t sbytes = (uint32_t)(p.b_expert_rows * ks);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, qbytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sbytes, sbytes);
+
+  // staging loads first: scales of the block's rows and the first pass of
+  // activation row 0 (one 16-byte piece or one 32-value block per thread)
+  const int s_pieces = s_bytes / 16;
+  const int si = threadIdx.x;
+  u32x4_t sv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = si + nthreads * j;
+    const int half = i / (s_pieces / NB), q = i - half * (s_pieces / NB);
+    const uint32_t off = i < s_pieces ? (uint32_t)((n0 + half * p.b_row_second) * ks + 16 * q) : kOob;
+    sv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+  }
+  // activation rows: AMX copies 16-byte pieces, else converts 32-value blocks
+  const int units = AMX ? stride / 16 : ks;  // per row
+  const __amdgpu_buffer_rsrc_t ra = AMX ? make_rsrc(p.amx, (uint32_t)((int64_t)p.a_rows * stride))
+                                        : make_rsrc(p.A, (uint32_t)((int64_t)p.a_rows * p.lda * 2));
+  u32x4_t av[4];
+  auto a_issue_row = [&](int sr, int unit) {
+    if constexpr (AMX) {
+      const uint32_t off = unit < units ? (uint32_t)(sr * stride + 16 * unit) : kOob;
+      av[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0));
+    } else {
+      const uint32_t off = unit < units ? (uint32_t)(((int64_t)sr * p.lda + 32 * unit) * 2) : kOob;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        av[qq] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 16 * qq, 0));
+    }
+  };
+  auto a_commit = [&](int r, int unit) {
+    if (unit >= units) return;
+    uint8_t* row = lds + r * stride;
+    if constexpr (AMX) {
+      *reinterpret_cast<u32x4_t*>(row + 16 * unit) = av[0];
+    } else {
+      float x[32];
+      unpack_bf16x32(av, x);
+      mx_convert_block(x, row + 32 * unit, row + K + 32 * unit, row + 2 * K + unit);
+    }
+  };
+  a_issue_row(src[0], threadIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // this wave's weights: chunks [c_begin, c_begin + CPW)
+  const int c_begin = wave * CPW;
+  u32x4_t q[CPW][NB];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int c = c_begin + u;
+    const bool ok = c < nchunks && c * 128 + grp * 32 < K;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t qo = ok ? (uint32_t)(n0 + col + nb * p.b_row_second) * (uint32_t)(K / 2) + (uint32_t)(c * 64 + grp * 16)
+                             : kOob;
+      q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = si + nthreads * j;
+    if (i < s_pieces) *reinterpret_cast<u32x4_t*>(s_lds + 16 * i) = sv[j];
+  }
+  a_commit(0, threadIdx.x);
+  // remaining activation pieces (row 0 beyond the first pass, rows 1..)
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) {
+    if (r >= rows) break;  // block-uniform
+    for (int unit = (r == 0 ? nthreads : 0) + (int)threadIdx.x; unit - (int)threadIdx.x < units; unit += nthreads) {
+      a_issue_row(src[r], unit);
+      a_commit(r, unit);
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool r_ok = col < rows;
+  const uint8_t* row = lds + (r_ok ? col : 0) * stride;
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int c = c_begin + u;
+    if (c >= nchunks) break;  // wave-uniform
+    const int kb = c * 128;
+    const bool h0 = r_ok && kb + 16 * grp < K, h1 = r_ok && kb + 64 + 16 * grp < K;
+    const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t a0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + kb + 16 * grp) : z;
+    const u32x4_t a1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + kb + 64 + 16 * grp) : z;
+    const u32x4_t l0 = h0 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 16 * grp) : z;
+    const u32x4_t l1 = h1 ? *reinterpret_cast<const u32x4_t*>(row + K + kb + 64 + 16 * grp) : z;
+    const int sa = (r_ok && kb + 32 * grp < K) ? (int)row[2 * K + kb / 32 + grp] : 127;
+    const i32x8_t ahi = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8_t alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bool sok = kb + 32 * grp < K;
+      const int sb = sok ? (int)s_lds[(nb * 16 + col) * ks + kb / 32 + grp] : 127;
+      acc[nb] = mfma_mx(ahi, q[u][nb], sa, sb, acc[nb]);
+      acc[nb] = mfma_mx(alo, q[u][nb], sa, sb, acc[nb]);
+    }
+  }
+  const int nwaves = nthreads >> 6;
+  if (wave > 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) red[((wave - 1) * NB + nb) * 64 + lane] = acc[nb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < nwaves; ++w) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] += red[((w - 1) * NB + nb) * 64 + lane];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * grp + i;
@@ -324,29 +576,69 @@ size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4) {
 
 namespace {
 
-template <int NB>
+// Scales staged in LDS (SW = 0): the block's 64 rows per half, up to K = 5120
+// (5 16-byte pieces per thread per half), when rows and scales fit in 64 KB.
+constexpr size_t kMxMaxLds = 64 * 1024;
+size_t mx_scale_lds_bytes(int nb, int K) { return (size_t)nb * 64 * (K / 32); }
+
+template <int NB, bool AMX>
 hipError_t launch_mx(const GemvProblem& p, int rows_cap, float limit, hipStream_t stream) {
   const dim3 grid((unsigned)(p.grid_tiles * ((p.N + 63) / 64)));
   const size_t shm = gemv_lds_bytes(rows_cap, p.K, true);
-  if (p.K % 512 == 0)
-    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 16>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+  const size_t shm_s = shm + mx_scale_lds_bytes(NB, p.K);
+  if (p.K <= 5120 && p.K % 128 == 0 && shm_s <= kMxMaxLds)
+    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 0, AMX>), grid, dim3(256), shm_s, stream, p, rows_cap, limit);
+  else if (p.K % 512 == 0)
+    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 16, AMX>), grid, dim3(256), shm, stream, p, rows_cap, limit);
   else if (p.K % 256 == 0)
-    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 8>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 8, AMX>), grid, dim3(256), shm, stream, p, rows_cap, limit);
   else if (p.K % 128 == 0)
-    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 4>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 4, AMX>), grid, dim3(256), shm, stream, p, rows_cap, limit);
   else
-    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 1>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+    hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 1, AMX>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+  return hipGetLastError();
+}
+
+template <int NB, int CPW, bool AMX>
+hipError_t launch_splitk(const GemvProblem& p, int rows_cap, float limit, hipStream_t stream) {
+  const int waves = ((p.K + 127) / 128 + CPW - 1) / CPW;
+  const dim3 grid((unsigned)(p.grid_tiles * (p.N / 16)));
+  const size_t s_bytes = ((size_t)NB * 16 * (p.K / 32) + 15) & ~size_t(15);
+  const size_t shm = gemv_lds_bytes(rows_cap, p.K, true) + s_bytes + (size_t)(waves - 1) * NB * 64 * 16;
+  hipLaunchKernelGGL((expert_gemv_splitk_kernel<NB, CPW, AMX>), grid, dim3(64 * waves), shm, stream, p, rows_cap,
+                     limit);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Split-K few-token projection: usable when the rows of a tile, the block's
+// scales and the wave partials fit in 64 KB and K needs at most 8 waves.
+bool splitk_supported(int rows_cap, int K, bool swiglu) {
+  const int nb = swiglu ? 2 : 1, cpw = swiglu ? kSplitKChunksGateUp : kSplitKChunksDown;
+  const int waves = ((K + 127) / 128 + cpw - 1) / cpw;
+  const size_t shm = gemv_lds_bytes(rows_cap, K, true) + (size_t)nb * 16 * (K / 32) + 16 + (size_t)(waves - 1) * nb * 1024;
+  return rows_cap <= kTileRows && waves <= 8 && shm <= 64 * 1024;
+}
+
+hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, float limit, bool swiglu,
+                                     hipStream_t stream) {
+  if (p.grid_tiles == 0 || p.N == 0) return hipSuccess;
+  if (swiglu)
+    return p.amx ? launch_splitk<2, kSplitKChunksGateUp, true>(p, rows_cap, limit, stream)
+                 : launch_splitk<2, kSplitKChunksGateUp, false>(p, rows_cap, limit, stream);
+  return launch_splitk<1, kSplitKChunksDown, false>(p, rows_cap, limit, stream);
+}
+
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream) {
   if (fp4) {
     // one problem per launch (p[1] unused)
     if (prm.p[0].grid_tiles == 0 || prm.p[0].N == 0) return hipSuccess;
-    return swiglu ? launch_mx<2>(prm.p[0], prm.rows_cap, prm.limit, stream)
-                  : launch_mx<1>(prm.p[0], prm.rows_cap, prm.limit, stream);
+    // pre-converted rows occur only for the gate/up projection
+    if (swiglu)
+      return prm.p[0].amx ? launch_mx<2, true>(prm.p[0], prm.rows_cap, prm.limit, stream)
+                          : launch_mx<2, false>(prm.p[0], prm.rows_cap, prm.limit, stream);
+    return launch_mx<1, false>(prm.p[0], prm.rows_cap, prm.limit, stream);
   }
   int k_max = prm.p[0].K;
   if (prm.p[1].grid_tiles > 0 && prm.p[1].K > k_max) k_max = prm.p[1].K;

@@ -35,6 +35,9 @@ inline int permute_chunks(int64_t n) { return (int)((n + kPermuteChunk - 1) / kP
 struct GemmTile {
   int e, m_begin, m_end, pad;
 };
+// Few-token tiles also carry the source row (token) of each of their at most
+// kTileRows rows: tile_rows[tile * kTileRows + r].
+constexpr int kTileRows = 8;
 inline int64_t max_gemm_tiles(int64_t n, int n_experts, int bm) {
   return (n + bm - 1) / bm + (n < n_experts ? n : n_experts);
 }
@@ -92,6 +95,7 @@ struct GemvProblem {
   const int32_t* gather;       // A row of position p: gather[p] / gather_div, else p
   int gather_div;
   int gather_len;              // entries of gather (MXFP4 problems read it with clamped indices)
+  const int32_t* tile_rows;    // MXFP4 problems: source row of each tile row (overrides gather), or NULL
   const uint16_t* A;
   int64_t lda;
   int a_rows;
@@ -107,6 +111,8 @@ struct GemvProblem {
   int col_tiles;               // N / 16
   uint16_t* C;
   int64_t ldc;
+  uint8_t* cmx;                // MXFP4 gate/up with rows_cap <= kTileRows: write the output rows in
+                               // two-term MXFP8 form (stride mx_row_bytes(N)) instead of C
 };
 struct GemvParams {
   GemvProblem p[2];
@@ -117,6 +123,15 @@ size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4);
 // fp4: one MXFP4 problem (p[0]; tiles of at most rows_cap <= 8 rows, grid over
 // 64-column blocks).  Otherwise up to two dense bf16 problems (bh).
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream);
+
+// MXFP4 few-token projection, split-K form: one block per (tile, 16 output
+// columns), its waves splitting K into ranges of kSplitKChunks* 128-wide
+// chunks.  Problem as for launch_expert_gemv with fp4 (no MXFP8 output).
+constexpr int kSplitKChunksGateUp = 10;
+constexpr int kSplitKChunksDown = 5;
+bool splitk_supported(int rows_cap, int K, bool swiglu);
+hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, float limit, bool swiglu,
+                                     hipStream_t stream);
 
 // One-block routing of T tokens with T * top_k <= 64 from the scores of
 // launch_router_gemv: top-k and weights, the stable permutation and the
@@ -134,6 +149,7 @@ struct RouteSmallParams {
   int32_t* slot_pos;
   GemmTile* tiles;
   int32_t* tile_count;
+  int32_t* tile_rows;  // [max_tiles][kTileRows], optional
   int max_tiles;
 };
 constexpr int kRouteSmallMaxSlots = 64;
@@ -159,7 +175,7 @@ hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& share
 // Routed down projection with the combine folded in, for T <= 8 tokens whose
 // T * top_k rows of h fit in LDS: y[t] = y_shared[t] + sum_j w[t][j] o[t][j].
 struct DownCombineParams {
-  const uint16_t* h;           // [T*k][inter] bf16, position order
+  const uint8_t* hmx;          // [T*k] rows of h in two-term MXFP8 form (stride mx_row_bytes(inter)), position order
   const GemmTile* tiles;
   const int32_t* tile_count;
   const int32_t* sorted_slots;
