@@ -20,6 +20,7 @@
 #include "mx_device.h"
 #include "router_device.h"
 #include "gemv_bf16_device.h"
+#include "gemv_valu_device.h"
 
 namespace moe {
 
@@ -64,17 +65,17 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   const int e = lane < n ? idx_sh[lane] : 0x7fffffff;
   int pos = 0, dup_before = 0, count = 0;
   for (int j = 0; j < n; ++j) {
-    const int ej = __shfl(e, j, 64);
+    const int ej = __builtin_amdgcn_readlane(e, j);
     pos += (ej < e) || (ej == e && j < lane);
     dup_before += (ej == e && j < lane);
     count += (ej == e);
   }
   const bool first = lane < n && dup_before == 0;  // first slot of its expert
+  const uint64_t firsts = __ballot(first);
   int distinct_smaller = 0;
   for (int j = 0; j < n; ++j) {
-    const int ej = __shfl(e, j, 64);
-    const bool fj = __shfl((int)first, j, 64) != 0;
-    distinct_smaller += (fj && ej < e);
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    distinct_smaller += (((firsts >> j) & 1ull) && ej < e);
   }
   if (lane < n) {
     p.sorted_slots[pos] = lane;
@@ -92,7 +93,6 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   // an expert has at most T <= 8 rows)
   if (p.tile_rows && lane < n && distinct_smaller < p.max_tiles && dup_before < kTileRows)
     p.tile_rows[distinct_smaller * kTileRows + dup_before] = lane / p.top_k;
-  const uint64_t firsts = __ballot(first);
   const int n_tiles = min((int)__popcll(firsts), p.max_tiles);
   if (lane == 0) *p.tile_count = n_tiles;
   // the remaining records are written empty, so readers need not load the count
@@ -124,6 +124,107 @@ __global__ __launch_bounds__(256) void decode_mid_kernel(RouteSmallParams p, Gem
   gemv_bf16_block<false>(shared_down, (int)blockIdx.x - 1, rows_cap, 0.f, lds);
 }
 
+// T <= kValuMaxTokens, hidden and shared inter <= 5120: the same two launches
+// with every weight row streamed by one wave on the vector ALUs.
+// Launch 1: the shared gate/up row pairs (gate row n and up row I_s + n per
+// wave, then the clamped SwiGLU), then the router rows (scores s and u).
+__global__ __launch_bounds__(256) void decode_front_valu_kernel(FrontValuParams f) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x rows [T][hidden] bf16
+  uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = f.hidden, T = f.tokens, Is = f.shared_inter;
+  const int shared_blocks = f.sh_gu ? (Is + 3) / 4 : 0;
+  float out2[2][kValuMaxTokens];
+  if ((int)blockIdx.x < shared_blocks) {
+    const int nrow = (int)blockIdx.x * 4 + wave;  // gate/up pair
+    const bool ok = nrow < Is;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.sh_gu, (uint32_t)((int64_t)2 * Is * H * 2));
+    const uint32_t off[2] = {ok ? (uint32_t)nrow * (uint32_t)H * 2u : kOob,
+                             ok ? (uint32_t)(Is + nrow) * (uint32_t)H * 2u : kOob};
+    ValuRows<8, 10, 2> st;
+    valu_issue<8, 10, 2>(st, rw, off, H);
+    valu_stage_rows(f.x, H, T, H, x_lds);
+    __syncthreads();
+    valu_compute<8, 10, 2, kValuMaxTokens>(st, x_lds, H, T, H, out2);
+    if (lane == 0 && ok)
+      for (int t = 0; t < T; ++t)
+        f.h_sh[(int64_t)t * Is + nrow] = f32_to_bf16(clamped_swiglu(out2[0][t], out2[1][t], f.limit));
+    return;
+  }
+  const int e = ((int)blockIdx.x - shared_blocks) * 4 + wave;
+  const bool ok = e < f.n_experts;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.router_w, (uint32_t)((int64_t)f.n_experts * H * 4));
+  const uint32_t off[1] = {ok ? (uint32_t)e * (uint32_t)H * 4u : kOob};
+  ValuRows<4, 20, 1> st;
+  valu_issue<4, 20, 1>(st, rw, off, H);
+  valu_stage_rows(f.x, H, T, H, x_lds);
+  __syncthreads();
+  float out1[1][kValuMaxTokens];
+  valu_compute<4, 20, 1, kValuMaxTokens>(st, x_lds, H, T, H, out1);
+  if (lane == 0 && ok) {
+    const float b = f.bias ? f.bias[e] : 0.f;
+    for (int t = 0; t < T; ++t) {
+      const float s = sqrtsoftplus(out1[0][t]);
+      f.scores[(int64_t)t * f.n_experts + e] = s;
+      f.scores[(int64_t)(T + t) * f.n_experts + e] = s + b;
+    }
+  }
+}
+
+// Launch 2: the routing block (block 0), then the shared down rows (two per
+// wave) from the SwiGLU rows of launch 1.
+template <int MPL, int KVD>
+__global__ __launch_bounds__(256) void decode_mid_valu_kernel(RouteSmallParams p, MidValuParams m) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // h_sh rows [T][shared_inter] bf16
+  if (blockIdx.x == 0) {
+    route_small_block<MPL>(p);
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = m.hidden, Is = m.shared_inter, T = m.tokens;
+  const int n = (((int)blockIdx.x - 1) * 4 + wave) * 2;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.sh_dn, (uint32_t)((int64_t)H * Is * 2));
+  const uint32_t off[2] = {n < H ? (uint32_t)n * (uint32_t)Is * 2u : kOob,
+                           n + 1 < H ? (uint32_t)(n + 1) * (uint32_t)Is * 2u : kOob};
+  ValuRows<8, KVD, 2> st;
+  valu_issue<8, KVD, 2>(st, rw, off, Is);
+  uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
+  valu_stage_rows(m.h_sh, Is, T, Is, h_lds);
+  __syncthreads();
+  float out[2][kValuMaxTokens];
+  valu_compute<8, KVD, 2, kValuMaxTokens>(st, h_lds, Is, T, Is, out);
+  if (lane == 0)
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (n + r < H) m.y_sh[(int64_t)t * H + n + r] = f32_to_bf16(out[r][t]);
+}
+
+bool decode_valu_supported(int tokens, int hidden, int shared_inter) {
+  return tokens <= kValuMaxTokens && hidden <= 5120 && shared_inter <= 5120;
+}
+
+hipError_t launch_decode_front_valu(const FrontValuParams& f, hipStream_t stream) {
+  const int shared_blocks = f.sh_gu ? (f.shared_inter + 3) / 4 : 0;
+  const dim3 grid((unsigned)(shared_blocks + (f.n_experts + 3) / 4));
+  hipLaunchKernelGGL(decode_front_valu_kernel, grid, dim3(256), (size_t)f.tokens * f.hidden * 2, stream, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mid_valu(const RouteSmallParams& p, const MidValuParams& m, hipStream_t stream) {
+  const int nj = (p.n_experts + 63) / 64;
+  const bool small = m.shared_inter <= 2560;  // 5 vectors of 8 per lane cover a row
+  auto kern = nj <= 2   ? (small ? decode_mid_valu_kernel<2, 5> : decode_mid_valu_kernel<2, 10>)
+              : nj <= 4 ? (small ? decode_mid_valu_kernel<4, 5> : decode_mid_valu_kernel<4, 10>)
+              : nj <= 6 ? (small ? decode_mid_valu_kernel<6, 5> : decode_mid_valu_kernel<6, 10>)
+              : nj <= 8 ? (small ? decode_mid_valu_kernel<8, 5> : decode_mid_valu_kernel<8, 10>)
+                        : (small ? decode_mid_valu_kernel<16, 5> : decode_mid_valu_kernel<16, 10>);
+  const int shared_blocks = m.sh_dn ? (m.hidden + 7) / 8 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + shared_blocks)), dim3(256),
+                     (size_t)m.tokens * (m.shared_inter > 0 ? m.shared_inter : 8) * 2, stream, p, m);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream) {
   const int shared_blocks = f.shared.grid_tiles * f.shared.col_tiles;
   const dim3 grid((unsigned)(shared_blocks + (f.n_experts + 3) / 4));
@@ -137,6 +238,7 @@ hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& share
   const int nj = (p.n_experts + 63) / 64;
   auto kern = nj <= 2 ? decode_mid_kernel<2>
               : nj <= 4 ? decode_mid_kernel<4>
+              : nj <= 6 ? decode_mid_kernel<6>
               : nj <= 8 ? decode_mid_kernel<8>
                         : decode_mid_kernel<16>;
   const int shared_blocks = shared_down.grid_tiles * shared_down.col_tiles;

@@ -1,0 +1,114 @@
+// Weight-streaming GEMV on the vector ALUs for one or two tokens: one wave
+// computes NR whole output rows.  At this size the projections are pure
+// weight streaming, and many waves that each read one contiguous row with
+// all of its loads in flight keep more memory requests outstanding across the
+// chip than a few waves streaming long ranges (a 75 MB read: ~20 us from 864
+// streaming waves, ~14 us from a few thousand light ones).  The arithmetic,
+// 2 flops per weight, is far below the vector-ALU rate.
+//
+// Each lane takes the 16-byte weight vectors v = lane, lane + 64, ... of its
+// rows (KV per row, issued together; raw buffer loads past the row read
+// zero), multiplies them in fp32 with the matching activation elements of
+// the T rows staged in LDS (bf16), and the lanes' sums are added in a fixed
+// order (wave_sum_f32), so the result does not depend on scheduling.
+#pragma once
+
+#include "moe_device.h"
+#include "mx_device.h"
+
+namespace moe {
+
+constexpr int kValuMaxTokens = 2;
+
+// EPV weights per 16-byte vector: 8 (bf16) or 4 (fp32).
+template <int EPV, int KV, int NR>
+struct ValuRows {
+  u32x4_t w[NR][KV];
+};
+
+// Issue the weight loads of rows at byte offsets row_off[r] of `rw`
+// (a row is K weights).
+template <int EPV, int KV, int NR>
+__device__ __forceinline__ void valu_issue(ValuRows<EPV, KV, NR>& st, const __amdgpu_buffer_rsrc_t& rw,
+                                           const uint32_t (&row_off)[NR], int K) {
+  const int lane = threadIdx.x & 63;
+  const int nv = K / EPV;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int v = lane + 64 * i;
+      const uint32_t off = v < nv ? row_off[r] + 16u * (uint32_t)v : kOob;
+      st.w[r][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+    }
+}
+
+// out[r][t] = sum_k W[r][k] * x[t][k] for t < T (TM >= T), x_lds: T rows of
+// K bf16 at stride x_stride elements.  Every lane ends with the full sums.
+template <int EPV, int KV, int NR, int TM>
+__device__ __forceinline__ void valu_compute(const ValuRows<EPV, KV, NR>& st, const uint16_t* x_lds, int x_stride,
+                                             int T, int K, float (&out)[NR][TM]) {
+  const int lane = threadIdx.x & 63;
+  const int nv = K / EPV;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) out[r][t] = 0.f;
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    const int v = min(lane + 64 * i, nv - 1);  // past the row the weights are zero; keep the read in range
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t >= T) break;
+      float xv[EPV];
+      if constexpr (EPV == 8) {
+        const u32x4_t xx = *reinterpret_cast<const u32x4_t*>(x_lds + t * x_stride + 8 * v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[2 * q] = __uint_as_float(xx[q] << 16);
+          xv[2 * q + 1] = __uint_as_float(xx[q] & 0xffff0000u);
+        }
+      } else {
+        const uint2 xx = *reinterpret_cast<const uint2*>(x_lds + t * x_stride + 4 * v);
+        xv[0] = __uint_as_float(xx.x << 16);
+        xv[1] = __uint_as_float(xx.x & 0xffff0000u);
+        xv[2] = __uint_as_float(xx.y << 16);
+        xv[3] = __uint_as_float(xx.y & 0xffff0000u);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float a = out[r][t];
+        if constexpr (EPV == 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a = fmaf(__uint_as_float(st.w[r][i][q] << 16), xv[2 * q], a);
+            a = fmaf(__uint_as_float(st.w[r][i][q] & 0xffff0000u), xv[2 * q + 1], a);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a = fmaf(__uint_as_float(st.w[r][i][q]), xv[q], a);
+        }
+        out[r][t] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) out[r][t] = wave_sum_f32(out[r][t]);
+}
+
+// Stage T rows of K bf16 (row stride ld elements in global memory) into LDS
+// at stride K; 16-byte pieces, all threads of the block.
+__device__ __forceinline__ void valu_stage_rows(const uint16_t* src, int64_t ld, int T, int K, uint16_t* x_lds) {
+  const int per_row = K / 8, total = T * per_row;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((int64_t)T * ld * 2));
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int t = i / per_row, q = i - t * per_row;
+    const u32x4_t v =
+        __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(((int64_t)t * ld + 8 * q) * 2), 0, 0));
+    *reinterpret_cast<u32x4_t*>(x_lds + t * K + 8 * q) = v;
+  }
+}
+
+}  // namespace moe

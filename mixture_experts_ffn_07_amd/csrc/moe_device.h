@@ -63,6 +63,49 @@ __device__ __forceinline__ float clamped_swiglu(float g, float u, float limit) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
+// Wave-wide max / min without LDS traffic: DPP permutations within each row
+// of 16 lanes (pairs, quads, half-row mirror, row mirror), then the four row
+// results read into scalar registers.  The result is wave-uniform.  All 64
+// lanes must be active.
+__device__ __forceinline__ int dpp_quad_1032(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_quad_2301(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_row_half_mirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_row_mirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true); }
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(dpp_quad_1032(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_quad_2301(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_row_half_mirror(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_row_mirror(__float_as_int(v))));
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_quad_1032(v));
+  v = min(v, dpp_quad_2301(v));
+  v = min(v, dpp_row_half_mirror(v));
+  v = min(v, dpp_row_mirror(v));
+  const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+// Wave-wide float sum in a fixed association (pairs, quads, half rows, rows,
+// then (row0 + row1) + (row2 + row3)): the same bits on every run.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __int_as_float(dpp_quad_1032(__float_as_int(v)));
+  v += __int_as_float(dpp_quad_2301(__float_as_int(v)));
+  v += __int_as_float(dpp_row_half_mirror(__float_as_int(v)));
+  v += __int_as_float(dpp_row_mirror(__float_as_int(v)));
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Inclusive prefix sum over a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -48,6 +48,8 @@ constexpr int64_t kMaxTokens = int64_t(1) << 22;
 constexpr int64_t kDecodeMaxTokens = 8;
 constexpr size_t kDecodeMaxLds = 64 * 1024;
 constexpr int kMaxDim = 65536;
+// few tokens: routed gate/up by the split-K kernel (else the 64-column kernel)
+constexpr bool kSplitKGateUp = false;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -122,6 +124,7 @@ struct WsLayout {
   int64_t max_tiles = 0, shared_tiles = 0;
   bool route_small = false;   // decode with T * k <= 64: scores from the router GEMV, one-block routing
   bool down_combine = false;  // decode: routed down projection with the combine folded in
+  bool splitk_gu = false;     // decode: routed gate/up by the split-K MXFP4 kernel
   bool splitk_dn = false;     // decode: routed down by the split-K MXFP4 kernel
   Region logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh;
@@ -146,8 +149,9 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
                      moe::down_combine_lds_bytes((int)tokens, c->top_k, c->inter) <= kDecodeMaxLds;
     // the split-K down projection plus a separate combine measured faster than
     // the fused down+combine kernel (11.8 + 4.1 us against 19.8 us at T = 1)
+    L.splitk_gu = kSplitKGateUp && moe::splitk_supported((int)tokens, c->hidden, true);
     L.splitk_dn = moe::splitk_supported((int)tokens, c->inter, false);
-    L.down_combine = L.down_combine && !L.splitk_dn;
+    L.down_combine = L.down_combine && !L.splitk_dn && !L.splitk_gu;
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
@@ -358,20 +362,37 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   moe_status s;
 
   uint8_t* xmx = nullptr;
+  const bool valu = L.route_small && moe::decode_valu_supported((int)T, c->hidden, c->n_shared ? c->shared_inter : 0);
   if (L.route_small) {
     float* scores = at<float>(ws, L.scores);
-    moe::FrontParams f{};
-    f.x = x;
-    f.router_w = w->router_w;
-    f.bias = w->router_bias;
-    f.scores = scores;
-    f.tokens = (int)T;
-    f.n_experts = E;
-    f.hidden = c->hidden;
-    if (c->n_shared) f.shared = shared_gemv(c, w, x, T, ws, L, true, y_sh).p[0];
-    f.rows_cap = (int)T;
-    f.limit = c->swiglu_limit;
-    err = moe::launch_decode_front(f, st);
+    if (valu) {
+      moe::FrontValuParams f{};
+      f.x = x;
+      f.router_w = w->router_w;
+      f.bias = w->router_bias;
+      f.scores = scores;
+      f.sh_gu = c->n_shared ? w->sh_gu : nullptr;
+      f.h_sh = c->n_shared ? at<uint16_t>(ws, L.h_sh) : nullptr;
+      f.shared_inter = c->n_shared ? c->shared_inter : 0;
+      f.tokens = (int)T;
+      f.n_experts = E;
+      f.hidden = c->hidden;
+      f.limit = c->swiglu_limit;
+      err = moe::launch_decode_front_valu(f, st);
+    } else {
+      moe::FrontParams f{};
+      f.x = x;
+      f.router_w = w->router_w;
+      f.bias = w->router_bias;
+      f.scores = scores;
+      f.tokens = (int)T;
+      f.n_experts = E;
+      f.hidden = c->hidden;
+      if (c->n_shared) f.shared = shared_gemv(c, w, x, T, ws, L, true, y_sh).p[0];
+      f.rows_cap = (int)T;
+      f.limit = c->swiglu_limit;
+      err = moe::launch_decode_front(f, st);
+    }
     if (err == hipSuccess) err = mark(tl, "router_shared_gate_up", st);
     if (err != hipSuccess) return fail_hip(err, "router/shared gate-up launch");
     xmx = at<uint8_t>(ws, L.xmx);
@@ -392,9 +413,20 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     rp.tile_count = tile_count;
     rp.tile_rows = at<int32_t>(ws, L.tile_rows);
     rp.max_tiles = (int)L.max_tiles;
-    moe::GemvProblem sd{};
-    if (c->n_shared) sd = shared_gemv(c, w, x, T, ws, L, false, y_sh).p[0];
-    err = moe::launch_decode_mid(rp, sd, (int)T, st);
+    if (valu) {
+      moe::MidValuParams m{};
+      m.sh_dn = c->n_shared ? w->sh_dn : nullptr;
+      m.h_sh = c->n_shared ? at<uint16_t>(ws, L.h_sh) : nullptr;
+      m.y_sh = y_sh;
+      m.shared_inter = c->n_shared ? c->shared_inter : 0;
+      m.tokens = (int)T;
+      m.hidden = c->hidden;
+      err = moe::launch_decode_mid_valu(rp, m, st);
+    } else {
+      moe::GemvProblem sd{};
+      if (c->n_shared) sd = shared_gemv(c, w, x, T, ws, L, false, y_sh).p[0];
+      err = moe::launch_decode_mid(rp, sd, (int)T, st);
+    }
     if (err == hipSuccess) err = mark(tl, "route_shared_down", st);
     if (err != hipSuccess) return fail_hip(err, "routing/shared down launch");
   } else {
@@ -412,8 +444,12 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
 
   moe::GemvParams gu = routed_gemv(c, w, x, xmx, T, sorted, ws, L, true, y_slot);
   if (L.route_small) gu.p[0].tile_rows = at<int32_t>(ws, L.tile_rows);
-  if (L.down_combine) gu.p[0].cmx = at<uint8_t>(ws, L.hmx);  // h in MXFP8 form for the down step
-  err = moe::launch_expert_gemv(gu, true, true, st);
+  if (L.splitk_gu) {
+    err = moe::launch_expert_gemv_splitk(gu.p[0], gu.rows_cap, gu.limit, true, st);
+  } else {
+    if (L.down_combine) gu.p[0].cmx = at<uint8_t>(ws, L.hmx);  // h in MXFP8 form for the down step
+    err = moe::launch_expert_gemv(gu, true, true, st);
+  }
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
 

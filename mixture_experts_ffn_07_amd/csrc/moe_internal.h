@@ -168,6 +168,29 @@ struct FrontParams {
   float limit;
 };
 hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream);
+// T <= 2 forms of the two launches: every weight row streamed by one wave
+// on the vector ALUs (gemv_valu_device.h).  sh_gu / sh_dn NULL without a
+// shared expert.
+struct FrontValuParams {
+  const uint16_t* x;
+  const float* router_w;
+  const float* bias;
+  float* scores;           // [2][T][E]
+  const uint16_t* sh_gu;   // [2 I_s][H] bf16
+  uint16_t* h_sh;          // [T][I_s] bf16
+  int shared_inter;
+  int tokens, n_experts, hidden;
+  float limit;
+};
+struct MidValuParams {
+  const uint16_t* sh_dn;   // [H][I_s] bf16
+  const uint16_t* h_sh;    // [T][I_s]
+  uint16_t* y_sh;          // [T][H]
+  int shared_inter, tokens, hidden;
+};
+bool decode_valu_supported(int tokens, int hidden, int shared_inter);
+hipError_t launch_decode_front_valu(const FrontValuParams& f, hipStream_t stream);
+hipError_t launch_decode_mid_valu(const RouteSmallParams& p, const MidValuParams& m, hipStream_t stream);
 // Launch 2: the one-block routing beside the shared expert's down projection.
 hipError_t launch_decode_mid(const RouteSmallParams& p, const GemvProblem& shared_down, int rows_cap,
                              hipStream_t stream);

@@ -189,6 +189,7 @@ hipError_t launch_route_permute_small(const float* part, int ksplit, const float
   const int nj = (n_experts + 63) / 64;
   auto kern = nj <= 2 ? route_permute_small_kernel<2>
               : nj <= 4 ? route_permute_small_kernel<4>
+              : nj <= 6 ? route_permute_small_kernel<6>
               : nj <= 8 ? route_permute_small_kernel<8>
                         : route_permute_small_kernel<16>;
   hipLaunchKernelGGL(kern, dim3(1), dim3(1024), permute_block_lds_bytes(n_experts), stream, part, ksplit, bias, tokens,
@@ -204,6 +205,7 @@ hipError_t launch_router_topk(const float* part, int ksplit, const float* bias, 
   const int nj = (n_experts + 63) / 64;
   auto kern = nj <= 2 ? router_topk_kernel<2>
               : nj <= 4 ? router_topk_kernel<4>
+              : nj <= 6 ? router_topk_kernel<6>
               : nj <= 8 ? router_topk_kernel<8>
                         : router_topk_kernel<16>;
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, part, ksplit, bias, tokens, n_experts, top_k, route_scale, idx,

@@ -77,53 +77,73 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
     }
   }
   }
-  // selection r is kept by lane r (k <= 16)
+  // Each lane sorts its slots once by (u desc, index asc) with an odd-even
+  // transposition network (taken and unused slots rank last); a round then
+  // takes the wave's best list head (max score, then lowest index among the
+  // lanes holding it, with DPP reductions) and only the owner lane advances
+  // its list.  Selection r is kept by lane r (k <= 16).
+  float su[kMaxPerLane], ss[kMaxPerLane];
+  int se[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const bool v = (valid >> j) & 1u;
+    su[j] = v ? u[j] : -INFINITY;
+    se[j] = v ? lane + 64 * j : 0x7fffffff;
+    ss[j] = s[j];
+  }
+#pragma unroll
+  for (int pass = 0; pass < kMaxPerLane; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < kMaxPerLane; i += 2) {
+      const bool sw = (su[i + 1] > su[i]) | ((su[i + 1] == su[i]) & (se[i + 1] < se[i]));
+      const float tu = su[i], ts = ss[i];
+      const int te = se[i];
+      su[i] = sw ? su[i + 1] : su[i];
+      se[i] = sw ? se[i + 1] : se[i];
+      ss[i] = sw ? ss[i + 1] : ss[i];
+      su[i + 1] = sw ? tu : su[i + 1];
+      se[i + 1] = sw ? te : se[i + 1];
+      ss[i + 1] = sw ? ts : ss[i + 1];
+    }
+  }
+  float hu = su[0], hs = ss[0];
+  int he = se[0], ptr = 0;
   float my_s = 0.f;
   int my_e = 0;
   float u_kth = 0.f, gap = INFINITY;
   const int rounds = top_k < n_experts ? top_k + 1 : top_k;
   for (int r = 0; r < rounds; ++r) {
-    float bu = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      if ((valid >> j) & 1u) {
-        const int e = lane + 64 * j;
-        if (ranks_above(u[j], e, bu, be)) {
-          bu = u[j];
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ou = __shfl_xor(bu, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ranks_above(ou, oe, bu, be)) {
-        bu = ou;
-        be = oe;
-      }
-    }
+    const float M = wave_max_f32(hu);
+    const int ew = wave_min_i32(hu == M ? he : 0x7fffffff);
     if (r == top_k) {
-      gap = u_kth - bu;
+      gap = u_kth - M;
       break;
     }
-    // winner's unbiased score, broadcast from its owner lane
-    const int jw = be >> 6;
-    float mine = 0.f;
+    const int owner = ew & 63;  // expert e lives in lane e % 64
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hs), owner));
+    if (lane == owner) {
+      ++ptr;
+      float nu = -INFINITY, ns = 0.f;
+      int ne = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) mine = (j == jw) ? s[j] : mine;
-    const float sw = __shfl(mine, be & 63, 64);
-    if (lane == (be & 63)) valid &= ~(1u << jw);
+      for (int j = 1; j < kMaxPerLane; ++j) {
+        nu = (j == ptr) ? su[j] : nu;
+        ne = (j == ptr) ? se[j] : ne;
+        ns = (j == ptr) ? ss[j] : ns;
+      }
+      hu = nu;
+      he = ne;
+      hs = ns;
+    }
     if (lane == r) {
       my_s = sw;
-      my_e = be;
+      my_e = ew;
     }
-    u_kth = bu;
+    u_kth = M;
   }
   // sum of the selected scores in selection order, then each lane r < k writes selection r
   float total = 0.f;
-  for (int r = 0; r < top_k; ++r) total += __shfl(my_s, r, 64);
+  for (int r = 0; r < top_k; ++r) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), r));
   if (lane < top_k) {
     idx_row[lane] = my_e;
     if (idx_lds) idx_lds[lane] = my_e;
@@ -189,9 +209,7 @@ __device__ __forceinline__ void router_gemv_wave(const uint16_t* __restrict__ x,
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      float v = acc[tt];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      const float v = wave_sum_f32(acc[tt]);
       if (lane == 0 && t + tt < tokens) {
         if (logits) logits[(size_t)(t + tt) * n_experts + e] = v;
         if (scores) {
