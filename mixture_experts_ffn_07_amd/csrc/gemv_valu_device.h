@@ -98,6 +98,35 @@ __device__ __forceinline__ void valu_compute(const ValuRows<EPV, KV, NR>& st, co
     for (int t = 0; t < TM; ++t) out[r][t] = wave_sum_f32(out[r][t]);
 }
 
+// One MXFP4 block (32 E2M1 codes in a 16-byte vector, element 2i in the low
+// nibble of byte i) times 32 bf16 activations at x (LDS, 16-byte aligned),
+// added to acc.  Each code pair becomes two bf16 values times the block
+// scale (v_cvt_scalef32_pk_bf16_fp4, exact), multiplied with the matching
+// activation pair by one v_dot2 with fp32 accumulation.
+//
+// The activation vector goes through an empty asm register constraint first:
+// without it, this hipcc folds the element extraction away and feeds dword 0
+// of the 16-byte vector to all four v_dot2c of it (visible in the assembly;
+// the results are wrong).
+template <int SEL>
+__device__ __forceinline__ float mx4_dot_pair(uint32_t codes, float scale, uint32_t xi, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, SEL),
+                                         __builtin_bit_cast(bf16x2_t, xi), acc, false);
+}
+
+__device__ __forceinline__ float mx4_dot32(const u32x4_t& q, float scale, const uint16_t* x, float acc) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    u32x4_t xx = *reinterpret_cast<const u32x4_t*>(x + 8 * d);
+    asm("" : "+v"(xx));
+    acc = mx4_dot_pair<0>(q[d], scale, xx[0], acc);
+    acc = mx4_dot_pair<1>(q[d], scale, xx[1], acc);
+    acc = mx4_dot_pair<2>(q[d], scale, xx[2], acc);
+    acc = mx4_dot_pair<3>(q[d], scale, xx[3], acc);
+  }
+  return acc;
+}
+
 // Stage T rows of K bf16 (row stride ld elements in global memory) into LDS
 // at stride K; 16-byte pieces, all threads of the block.
 __device__ __forceinline__ void valu_stage_rows(const uint16_t* src, int64_t ld, int T, int K, uint16_t* x_lds) {

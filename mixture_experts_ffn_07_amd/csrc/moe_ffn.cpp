@@ -126,6 +126,8 @@ struct WsLayout {
   bool down_combine = false;  // decode: routed down projection with the combine folded in
   bool splitk_gu = false;     // decode: routed gate/up by the split-K MXFP4 kernel
   bool splitk_dn = false;     // decode: routed down by the split-K MXFP4 kernel
+  bool valu_gu = false;       // decode, T <= 2: routed gate/up one wave per column on the vector ALUs
+  bool valu_dn = false;       // decode, T <= 2: routed down + combine one wave per column on the vector ALUs
   Region logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh;
   size_t total = 0;
@@ -152,6 +154,9 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     L.splitk_gu = kSplitKGateUp && moe::splitk_supported((int)tokens, c->hidden, true);
     L.splitk_dn = moe::splitk_supported((int)tokens, c->inter, false);
     L.down_combine = L.down_combine && !L.splitk_dn && !L.splitk_gu;
+    L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden);
+    L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter);
+    if (L.valu_gu || L.valu_dn) L.down_combine = false;  // h stays bf16
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
@@ -444,7 +449,20 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
 
   moe::GemvParams gu = routed_gemv(c, w, x, xmx, T, sorted, ws, L, true, y_slot);
   if (L.route_small) gu.p[0].tile_rows = at<int32_t>(ws, L.tile_rows);
-  if (L.splitk_gu) {
+  if (L.valu_gu) {
+    moe::GateUpValuParams g{};
+    g.x = x;
+    g.tiles = tiles;
+    g.tile_rows = at<int32_t>(ws, L.tile_rows);
+    g.gu_q = w->gu_q;
+    g.gu_s = w->gu_s;
+    g.h = at<uint16_t>(ws, L.h);
+    g.tokens = (int)T;
+    g.hidden = c->hidden;
+    g.inter = c->inter;
+    g.limit = c->swiglu_limit;
+    err = moe::launch_gate_up_valu(g, (int)L.max_tiles, st);
+  } else if (L.splitk_gu) {
     err = moe::launch_expert_gemv_splitk(gu.p[0], gu.rows_cap, gu.limit, true, st);
   } else {
     if (L.down_combine) gu.p[0].cmx = at<uint8_t>(ws, L.hmx);  // h in MXFP8 form for the down step
@@ -453,6 +471,25 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
 
+  if (L.valu_dn) {
+    moe::DownValuParams dv{};
+    dv.h = at<uint16_t>(ws, L.h);
+    dv.idx = idx;
+    dv.topk_w = wts;
+    dv.slot_pos = slot_pos;
+    dv.dn_q = w->dn_q;
+    dv.dn_s = w->dn_s;
+    dv.y_shared = y_sh;
+    dv.y = y;
+    dv.tokens = (int)T;
+    dv.top_k = c->top_k;
+    dv.hidden = c->hidden;
+    dv.inter = c->inter;
+    err = moe::launch_down_combine_valu(dv, st);
+    if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
+    if (err != hipSuccess) return fail_hip(err, "down/combine launch");
+    return MOE_OK;
+  }
   if (L.down_combine) {
     moe::DownCombineParams dp{};
     dp.hmx = at<uint8_t>(ws, L.hmx);

@@ -216,6 +216,37 @@ constexpr int kDownCombineMaxInter = 2560;
 size_t down_combine_lds_bytes(int tokens, int top_k, int inter);
 hipError_t launch_down_combine(const DownCombineParams& p, hipStream_t stream);
 
+// Routed projections for T <= 2 tokens on the vector ALUs, one wave per
+// output column (expert_valu.hip).  gate/up: one block row per tile record
+// of the one-block routing (tiles, tile_rows; empty records are skipped),
+// h[pos] = SwiGLU.  down: every slot's h row against row n of its expert's
+// W_dn, weighted and added to the shared expert's output: y directly.
+struct GateUpValuParams {
+  const uint16_t* x;          // [T][H] bf16
+  const GemmTile* tiles;      // [max_tiles]
+  const int32_t* tile_rows;   // [max_tiles][kTileRows]
+  const uint8_t* gu_q;        // [E][2I][H/2]
+  const uint8_t* gu_s;        // [E][2I][H/32]
+  uint16_t* h;                // [T*k][I] bf16, row = position
+  int tokens, hidden, inter;
+  float limit;
+};
+struct DownValuParams {
+  const uint16_t* h;          // [T*k][I] bf16, row = position
+  const int32_t* idx;         // [T][k]
+  const float* topk_w;        // [T][k]
+  const int32_t* slot_pos;    // [T*k]
+  const uint8_t* dn_q;        // [E][H][I/2]
+  const uint8_t* dn_s;        // [E][H][I/32]
+  const uint16_t* y_shared;   // [T][H] or NULL
+  uint16_t* y;                // [T][H]
+  int tokens, top_k, hidden, inter;
+};
+bool gate_up_valu_supported(int tokens, int hidden);
+bool down_valu_supported(int tokens, int top_k, int inter);
+hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream);
+hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream);
+
 // Fused few-token routing: top-k of every token + permutation + tile table (T*k <= 1024).
 hipError_t launch_route_permute_small(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
                                       int top_k, float route_scale, int32_t* idx, float* w, float* gap,

@@ -226,6 +226,34 @@ def test_layer_small_token_counts(tokens):
     _check_layer(inp)
 
 
+@pytest.mark.parametrize("tokens", [1, 2])
+@pytest.mark.parametrize("variant", ["min_dims", "ragged_k", "no_shared", "k1", "all_experts", "k16", "wide_h",
+                                     "too_wide_h", "scale_plus_one", "zero_routed", "v4pro_dims"])
+def test_layer_one_two_tokens(tokens, variant):
+    """One and two tokens take the vector-ALU routed projections; shapes around their limits."""
+    base = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens)
+    cfg = {"min_dims": base.with_(hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2),
+           "ragged_k": base.with_(hidden=160, inter=96, shared_inter=224),
+           "no_shared": base.with_(n_shared=0, shared_inter=0),
+           "k1": base.with_(top_k=1),
+           "all_experts": base.with_(n_experts=8, top_k=8),  # both tokens pick every expert: 2-row tiles
+           "k16": base.with_(top_k=16),
+           "wide_h": base.with_(hidden=8192, inter=64, shared_inter=64, n_experts=8),
+           "too_wide_h": base.with_(hidden=8224, inter=64, shared_inter=64, n_experts=8),
+           "scale_plus_one": base,
+           "zero_routed": base,
+           "v4pro_dims": CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens, hidden=7168, inter=3072,
+                                                                 shared_inter=3072, n_experts=16)}[variant]
+    inp = make_inputs(cfg, seed=13 + tokens, device=DEV)
+    if variant == "scale_plus_one":
+        inp.dn_s += 1
+        inp.gu_s += 1
+    if variant == "zero_routed":
+        inp.dn_q.zero_()
+    stats, _, alt = _check_layer(inp)
+    print(f"T={tokens} {variant}:", stats, "near-tie alternatives", len(alt))
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7, 8, 16])
 def test_layer_top_k_range(k):
     inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=12, top_k=k), seed=3, device=DEV)
