@@ -2,24 +2,28 @@
 //
 // At T <= 2 the routed experts are pure MXFP4 weight streaming (the layer's
 // cost is the weight bytes: Strata DEEPSEEK41 notes, opening paragraph and
-// the "Where it goes" table).  Here each wave owns CPW output columns and
-// issues every weight load of them at once: a 16-byte vector of E2M1 codes
-// is exactly one 32-element E8M0 block, so lane l takes vectors l, l + 64,
-// ... of the column's rows laid end to end, with one scale byte each.  Many
-// light waves keep more requests in flight than a few long streams (a 75 MB
-// streaming read: ~20 us from 864 long waves, ~14 us from a few thousand
-// light ones).  Each vector is dequantised to bf16 pairs and multiplied with
-// the activations staged in LDS by v_dot2 (mx4_dot32); lanes' partial sums
-// are added in a fixed order.
+// the "Where it goes" table).  A 16-byte vector of E2M1 codes is exactly one
+// 32-element E8M0 block, so a wave reads one output column's weight rows laid
+// end to end: lane l takes vectors l, l + 64, ... with one scale byte each,
+// all issued at once.  Each vector is dequantised to bf16 pairs and
+// multiplied with the activations staged in LDS by v_dot2 (mx4_dot32); the
+// lanes' partial sums are added in a fixed order.
 //
-//   gate/up: work = (selected expert, column j): rows j (gate) and I + j (up)
-//            of W_gu[e] against the expert's token rows of x; writes
-//            h[pos] = SwiGLU_clamped(gate, up) in bf16.
-//   down:    work = output column n: row n of W_dn[e_s] for every slot s
-//            (token t, choice j) against h of that slot; the weighted sum
-//            over the slots plus the shared expert's output is y[t][n]
-//            (the combine folded in: DeepSeek-V4 report, MoE section, the
-//            gate-weighted sum of the routed outputs plus the shared one).
+// Grid-stride loop: a block stages the activations once, then each wave
+// walks columns wave_id, wave_id + W, ... (W = waves in the grid) with two
+// register buffers: the next column's loads are in flight while the current
+// one is multiplied, so the memory pipe does not idle behind the arithmetic
+// and the last columns do not wait for a second round of waves.  Loads for a
+// column past the end use out-of-range offsets or repeat a valid address,
+// so the loop body has no branches around loads and its waits stay exact.
+//
+//   gate/up: column (tile, j): rows j (gate) and I + j (up) of W_gu[e]
+//            against the tile's token rows of x; h[pos] = SwiGLU_clamped.
+//   down:    column n: row n of W_dn[e_s] for every slot s (token t, choice
+//            j) against h of that slot; the weighted sum over the slots plus
+//            the shared expert's output is y[t][n] (the combine folded in:
+//            DeepSeek-V4 report, MoE section, the gate-weighted sum of the
+//            routed outputs plus the shared one).
 #include "gemv_valu_device.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -30,100 +34,144 @@ namespace moe {
 namespace {
 
 constexpr int kValuBlock = 256;  // threads per block (4 waves)
+constexpr int kValuWaves = kValuBlock / 64;
+constexpr int kMaxLiveTiles = 64;  // tile records of the one-block routing (T * k <= 64), one per lane
 
-// 16-byte h pieces each thread of the down kernel stages (n * I / 8 in all)
-constexpr int down_staging_pieces(int jm) { return jm >= 14 ? 16 : 8; }
+template <int JM>
+struct ColBuf {
+  u32x4_t q[JM];
+  uint32_t s[JM];
+  uint32_t ysh;  // down: lane t < T holds the shared expert's y[t][col] (bf16 bits)
+};
 
-// gate/up: grid (ceil(I / (4 * CPW)), max_tiles).  JM >= ceil(2 * (H/32) / 64).
-template <int JM, int CPW>
-__global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x rows of the tile [rows][H] bf16
-  uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.y;
-  const GemmTile tl = p.tiles[tile];
-  int src[kValuMaxTokens];
-#pragma unroll
-  for (int r = 0; r < kValuMaxTokens; ++r) src[r] = p.tile_rows[tile * kTileRows + r];
-  const int rows = min(tl.m_end - tl.m_begin, p.tokens);
-  if (rows <= 0) return;  // unused tile record
-  const int H = p.hidden, I = p.inter, VR = H / 32;
+// ---------------------------------------------------------------- gate/up
+// A column: live tile `tile` (-1 past the end), its record and column j.
+struct GuItem {
+  int4 rec;  // {expert, first position, rows, src0 | src1 << 16}
+  int tile, j;
+};
 
-  // activation staging loads first: they return before the weights
-  constexpr int kXs = 8;  // 16-byte pieces per thread: T <= 2, H <= 8192
-  const int per_row = H / 8, pieces = rows * per_row;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(p.tokens * H * 2));
-  u32x4_t xs[kXs];
-#pragma unroll
-  for (int i = 0; i < kXs; ++i) {
-    const int q = (int)threadIdx.x + kValuBlock * i;
-    const int r = q >= per_row ? 1 : 0, c = q - r * per_row;
-    const int sr = min(max(r ? src[1] : src[0], 0), p.tokens - 1);
-    const uint32_t off = q < pieces ? (uint32_t)((sr * H + 8 * c) * 2) : kOob;
-    xs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
-  }
-
-  // weight loads: column j's gate row then up row, 2 * VR vectors
-  const int e = tl.e;
+template <int JM>
+__device__ __forceinline__ void gu_issue(ColBuf<JM>& b, const uint8_t* gu_q, const uint8_t* gu_s, const GuItem& it,
+                                         int H, int I, int lane) {
+  const int VR = H / 32;
   const uint32_t qbytes = (uint32_t)(2 * I * (H / 2)), sbytes = (uint32_t)(2 * I * VR);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.gu_q + (int64_t)e * qbytes, qbytes);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.gu_s + (int64_t)e * sbytes, sbytes);
-  const int j0 = ((int)blockIdx.x * (kValuBlock / 64) + wave) * CPW;
-  u32x4_t q[CPW][JM];
-  uint32_t sc[CPW][JM];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(gu_q + (int64_t)it.rec.x * qbytes, qbytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(gu_s + (int64_t)it.rec.x * sbytes, sbytes);
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int j = j0 + c;
-#pragma unroll
-    for (int jj = 0; jj < JM; ++jj) {
-      const int v = lane + 64 * jj;
-      const bool up = v >= VR;
-      const int b = v - (up ? VR : 0);
-      const bool ok = j < I && v < 2 * VR;
-      const uint32_t row = (uint32_t)(j + (up ? I : 0));
-      q[c][jj] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(ok ? row * (uint32_t)(H / 2) + 16u * b : kOob), 0, 0));
-      sc[c][jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? row * (uint32_t)VR + b : kOob), 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kXs; ++i) {
-    const int qq = (int)threadIdx.x + kValuBlock * i;
-    if (qq < pieces) *reinterpret_cast<u32x4_t*>(x_lds + 8 * qq) = xs[i];
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    float g[kValuMaxTokens], u[kValuMaxTokens];
-#pragma unroll
-    for (int r = 0; r < kValuMaxTokens; ++r) g[r] = u[r] = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < JM; ++jj) {
-      const int v = lane + 64 * jj;
-      const bool up = v >= VR;
-      const int b = min(v - (up ? VR : 0), VR - 1);  // past the pair the codes are zero
-      const float scale = e8m0_scale_operand(sc[c][jj]);
-#pragma unroll
-      for (int r = 0; r < kValuMaxTokens; ++r) {
-        if (r >= rows) break;  // block-uniform
-        const float d = mx4_dot32(q[c][jj], scale, x_lds + r * H + 32 * b, 0.f);
-        g[r] += up ? 0.f : d;
-        u[r] += up ? d : 0.f;
-      }
-    }
-    const int j = j0 + c;
-#pragma unroll
-    for (int r = 0; r < kValuMaxTokens; ++r) {
-      if (r >= rows) break;
-      const float gs = wave_sum_f32(g[r]), us = wave_sum_f32(u[r]);
-      if (lane == 0 && j < I) p.h[(int64_t)(tl.m_begin + r) * I + j] = f32_to_bf16(clamped_swiglu(gs, us, p.limit));
-    }
+  for (int jj = 0; jj < JM; ++jj) {
+    const int v = lane + 64 * jj;
+    const bool up = v >= VR;
+    const int bb = v - (up ? VR : 0);
+    const bool ok = it.tile >= 0 && v < 2 * VR;
+    const uint32_t row = (uint32_t)(it.j + (up ? I : 0));
+    const uint32_t qo = row * (uint32_t)(H / 2) + 16u * (uint32_t)bb;
+    const uint32_t so = row * (uint32_t)VR + (uint32_t)bb;
+    b.q[jj] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(ok ? qo : kOob), 0, 0));
+    b.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? so : kOob), 0, 0);
   }
 }
 
-// down + combine: grid ceil(H / (4 * CPW)).  JM >= ceil(n * (I/32) / 64).
-template <int JM, int CPW>
+template <int JM, int TM>
+__global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuParams p, int max_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x rows [T][H] bf16
+  uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = p.tokens, H = p.hidden, I = p.inter, VR = H / 32;
+
+  // tile records: lane t < max_tiles loads record t and its first two token
+  // rows (one round trip, every wave for itself); the live ones are moved to
+  // the lowest lanes in order, so lane i holds live tile i
+  const bool in = lane < max_tiles;
+  const GemmTile tl = in ? p.tiles[lane] : GemmTile{0, 0, 0, 0};
+  const int r0 = in ? p.tile_rows[lane * kTileRows] : 0, r1 = in ? p.tile_rows[lane * kTileRows + 1] : 0;
+  // x staging loads go out together with the records
+  const int x_pieces = T * (H / 8);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(T * H * 2));
+  auto x_off = [&](int q) {
+    const int t = q / (H / 8), c = q - t * (H / 8);
+    return (uint32_t)((t * H + 8 * c) * 2);
+  };
+  StageBatch<4> xb;
+  stage_issue<4>(xb, rx, x_pieces, 0, x_off);
+
+  const int rows = min(tl.m_end - tl.m_begin, T);
+  const bool live = in && rows > 0;
+  const uint64_t live_mask = __ballot(live);
+  const int n_live = __popcll(live_mask);
+  const int rank = __popcll(live_mask & ((1ull << lane) - 1ull));
+  const int dst = 4 * (live ? rank : n_live + (lane - rank));
+  const int c_e = __builtin_amdgcn_ds_permute(dst, tl.e);
+  const int c_m = __builtin_amdgcn_ds_permute(dst, tl.m_begin);
+  const int c_r = __builtin_amdgcn_ds_permute(dst, rows);
+  const int c_s = __builtin_amdgcn_ds_permute(dst, min(max(r0, 0), T - 1) | (min(max(r1, 0), T - 1) << 16));
+  const int total = n_live * I;
+  const int W = (int)gridDim.x * kValuWaves;
+  const int wg = (int)blockIdx.x * kValuWaves + wave;
+
+  auto item = [&](int it) {
+    GuItem g;
+    const bool ok = it < total;
+    const int ti = ok ? it / I : 0;
+    g.tile = ok ? ti : -1;
+    g.j = ok ? it - ti * I : 0;
+    g.rec.x = __builtin_amdgcn_readlane(c_e, ti);
+    g.rec.y = __builtin_amdgcn_readlane(c_m, ti);
+    g.rec.z = __builtin_amdgcn_readlane(c_r, ti);
+    g.rec.w = __builtin_amdgcn_readlane(c_s, ti);
+    return g;
+  };
+  ColBuf<JM> b0, b1;
+  GuItem g0 = item(wg);
+  gu_issue<JM>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
+
+  stage_commit<4>(xb, x_pieces, 0, lds);
+  stage_pieces<4>(rx, x_pieces, lds, x_off, 4 * kValuBlock);  // T = 2 rows beyond the first batch
+  __syncthreads();
+  if (wg >= total) return;
+
+  auto compute = [&](const ColBuf<JM>& b, const GuItem& g) {
+    float gs[TM], us[TM];
+#pragma unroll
+    for (int r = 0; r < TM; ++r) gs[r] = us[r] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < JM; ++jj) {
+      // one vector at a time: hoisting every vector's LDS reads ahead of the
+      // arithmetic would double the registers and halve the waves per SIMD
+      __builtin_amdgcn_sched_barrier(0);
+      const int v = lane + 64 * jj;
+      const bool up = v >= VR;
+      const int bb = min(v - (up ? VR : 0), VR - 1);  // past the pair the codes are zero
+      const float scale = e8m0_scale_operand(b.s[jj]);
+#pragma unroll
+      for (int r = 0; r < TM; ++r) {
+        if (r >= g.rec.z) break;  // wave-uniform
+        const int src = r ? (g.rec.w >> 16) : (g.rec.w & 0xffff);
+        const float d = mx4_dot32(b.q[jj], scale, x_lds + src * H + 32 * bb, 0.f);
+        gs[r] += up ? 0.f : d;
+        us[r] += up ? d : 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      if (r >= g.rec.z) break;
+      const float gsum = wave_sum_f32(gs[r]), usum = wave_sum_f32(us[r]);
+      if (lane == 0) p.h[(int64_t)(g.rec.y + r) * I + g.j] = f32_to_bf16(clamped_swiglu(gsum, usum, p.limit));
+    }
+  };
+
+  for (int it = wg; it < total; it += 2 * W) {
+    const GuItem g1 = item(it + W);
+    gu_issue<JM>(b1, p.gu_q, p.gu_s, g1, H, I, lane);
+    compute(b0, g0);
+    g0 = item(it + 2 * W);
+    gu_issue<JM>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
+    if (g1.tile >= 0) compute(b1, g1);
+  }
+}
+
+// ---------------------------------------------------------------- down + combine
+template <int JM, int TM>
 __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // h of every slot [n][I] bf16
   uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
@@ -135,92 +183,92 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
   const int my_e = p.idx[ls];
   const int my_p = p.slot_pos[ls];
   const float my_w = p.topk_w[ls];
-  const int n0 = ((int)blockIdx.x * (kValuBlock / 64) + wave) * CPW;
 
-  // the shared expert's outputs of this wave's columns: lane t < T, column c
-  float ysh[CPW];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c)
-    ysh[c] = (p.y_shared && lane < T && n0 + c < H) ? bf16_to_f32(p.y_shared[(int64_t)lane * H + n0 + c]) : 0.f;
-
-  // h staging loads (slot order), before the weights
-  constexpr int kHs = down_staging_pieces(JM);
-  const int per_row = I / 8, pieces = n * per_row;
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.h, (uint32_t)(n * I * 2));
-  u32x4_t hs[kHs];
-#pragma unroll
-  for (int i = 0; i < kHs; ++i) {
-    const int qq = (int)threadIdx.x + kValuBlock * i;
-    const int s = min(qq / per_row, n - 1), c = qq - s * per_row;
-    const int pos = __shfl(my_p, s);
-    const uint32_t off = qq < pieces ? (uint32_t)((pos * I + 8 * c) * 2) : kOob;
-    hs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)off, 0, 0));
-  }
-
-  // weights: vector v = lane + 64 jj is block b of slot s's row n
+  // vector v = lane + 64 jj is block vb of slot vs's row (vs = -1: past the
+  // last slot, its load repeats a valid address and its product is dropped)
   int vs[JM], vb[JM];
+  float vw[JM];
   const uint8_t* qrow[JM];
   const uint8_t* srow[JM];
 #pragma unroll
   for (int jj = 0; jj < JM; ++jj) {
     const int v = lane + 64 * jj;
     const int s = min(v / VR, n - 1);
-    vs[jj] = v < n * VR ? s : -1;  // -1: past the last slot (its load repeats a valid address)
+    vs[jj] = v < n * VR ? s : -1;
     vb[jj] = v - s * VR < VR ? v - s * VR : VR - 1;
+    vw[jj] = __shfl(my_w, s);
     const int64_t er = (int64_t)__shfl(my_e, s) * H;
     qrow[jj] = p.dn_q + er * (I / 2) + 16 * vb[jj];
     srow[jj] = p.dn_s + er * VR + vb[jj];
   }
-  u32x4_t q[CPW][JM];
-  uint32_t sc[CPW][JM];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int64_t nc = min(n0 + c, H - 1);
+  const int W = (int)gridDim.x * kValuWaves;
+  const int wg = (int)blockIdx.x * kValuWaves + wave;
+  // a column past the end re-reads column H - 1 (cached) and is not stored
+  const __amdgpu_buffer_rsrc_t rsh = make_rsrc(p.y_shared, p.y_shared ? (uint32_t)(T * H * 2) : 0u);
+  auto issue = [&](ColBuf<JM>& b, int col) {
+    const int64_t c = min(col, H - 1);
 #pragma unroll
     for (int jj = 0; jj < JM; ++jj) {
-      q[c][jj] = *reinterpret_cast<const u32x4_t*>(qrow[jj] + nc * (I / 2));
-      sc[c][jj] = srow[jj][nc * VR];
+      b.q[jj] = *reinterpret_cast<const u32x4_t*>(qrow[jj] + c * (I / 2));
+      b.s[jj] = srow[jj][c * VR];
     }
-  }
-#pragma unroll
-  for (int i = 0; i < kHs; ++i) {
-    const int qq = (int)threadIdx.x + kValuBlock * i;
-    if (qq < pieces) *reinterpret_cast<u32x4_t*>(h_lds + 8 * qq) = hs[i];
-  }
-  __syncthreads();
+    b.ysh = __builtin_amdgcn_raw_buffer_load_b16(rsh, (int)(lane < T ? (uint32_t)((lane * H + c) * 2) : kOob), 0, 0);
+  };
 
-  float wsl[JM];
+  // h staging (slot order): the first batch goes out before the first
+  // column's weights and is stored while they are in flight
+  const int per_row = I / 8, h_pieces = n * per_row;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.h, (uint32_t)(n * I * 2));
+  auto h_off = [&](int q) {
+    const int s = q / per_row, c = q - s * per_row;
+    return (uint32_t)((__shfl(my_p, s) * I + 8 * c) * 2);
+  };
+  StageBatch<8> hb;
+  stage_issue<8>(hb, rh, h_pieces, 0, h_off);
+  ColBuf<JM> b0, b1;
+  issue(b0, wg);
+  stage_commit<8>(hb, h_pieces, 0, lds);
+  stage_pieces<8>(rh, h_pieces, lds, h_off, 8 * kValuBlock);
+  __syncthreads();
+  if (wg >= H) return;
+
+  auto compute = [&](const ColBuf<JM>& b, int col) {
+    float acc[TM];
 #pragma unroll
-  for (int jj = 0; jj < JM; ++jj) wsl[jj] = __shfl(my_w, max(vs[jj], 0));
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    float acc[kValuMaxTokens];
-#pragma unroll
-    for (int t = 0; t < kValuMaxTokens; ++t) acc[t] = 0.f;
+    for (int t = 0; t < TM; ++t) acc[t] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < JM; ++jj) {
+      __builtin_amdgcn_sched_barrier(0);  // one vector at a time (registers)
       const int s = max(vs[jj], 0);
-      const float d = mx4_dot32(q[c][jj], e8m0_scale_operand(sc[c][jj]), h_lds + s * I + 32 * vb[jj], 0.f);
-      const float wd = vs[jj] >= 0 ? wsl[jj] * d : 0.f;
+      const float d = mx4_dot32(b.q[jj], e8m0_scale_operand(b.s[jj]), h_lds + s * I + 32 * vb[jj], 0.f);
+      const float wd = vs[jj] >= 0 ? vw[jj] * d : 0.f;
       const int t = s / k;
 #pragma unroll
-      for (int tt = 0; tt < kValuMaxTokens; ++tt) acc[tt] += t == tt ? wd : 0.f;
+      for (int tt = 0; tt < TM; ++tt) acc[tt] += t == tt ? wd : 0.f;
     }
     float r = 0.f;
 #pragma unroll
-    for (int t = 0; t < kValuMaxTokens; ++t) {
+    for (int t = 0; t < TM; ++t) {
       const float st = wave_sum_f32(acc[t]);
       r = lane == t ? st : r;
     }
-    if (lane < T && n0 + c < H) p.y[(int64_t)lane * H + n0 + c] = f32_to_bf16(r + ysh[c]);
+    if (lane < T) p.y[(int64_t)lane * H + col] = f32_to_bf16(r + bf16_to_f32((uint16_t)b.ysh));
+  };
+
+  for (int col = wg; col < H; col += 2 * W) {
+    issue(b1, col + W);
+    compute(b0, col);
+    issue(b0, col + 2 * W);
+    if (col + W < H) compute(b1, col + W);
   }
 }
 
 // instantiated vector counts per lane; the smallest >= the need is used
 constexpr int kGateUpJm[] = {2, 4, 5, 7, 8};
 constexpr int kDownJm[] = {2, 4, 7, 9, 14};
-constexpr int kGateUpCpw = 2;
-constexpr int kDownCpw = 1;
+// blocks per CU of the grid-stride loops (all resident at once)
+constexpr int kGateUpBlocksPerCu = 2;
+constexpr int kDownBlocksPerCu = 2;
 
 int gate_up_jm(int hidden) {
   const int need = (2 * (hidden / 32) + 63) / 64;
@@ -236,47 +284,82 @@ int down_jm(int slots, int inter) {
   return 0;
 }
 
+using GateUpKernel = void (*)(GateUpValuParams, int);
+using DownKernel = void (*)(DownValuParams);
+
+template <int TM>
+GateUpKernel pick_gate_up_t(int jm) {
+  switch (jm) {
+    case 2: return gate_up_valu_kernel<2, TM>;
+    case 4: return gate_up_valu_kernel<4, TM>;
+    case 5: return gate_up_valu_kernel<5, TM>;
+    case 7: return gate_up_valu_kernel<7, TM>;
+    case 8: return gate_up_valu_kernel<8, TM>;
+    default: return nullptr;
+  }
+}
+GateUpKernel pick_gate_up(int jm, int tokens) { return tokens == 1 ? pick_gate_up_t<1>(jm) : pick_gate_up_t<2>(jm); }
+
+template <int TM>
+DownKernel pick_down_t(int jm) {
+  switch (jm) {
+    case 2: return down_combine_valu_kernel<2, TM>;
+    case 4: return down_combine_valu_kernel<4, TM>;
+    case 7: return down_combine_valu_kernel<7, TM>;
+    case 9: return down_combine_valu_kernel<9, TM>;
+    case 14: return down_combine_valu_kernel<14, TM>;
+    default: return nullptr;
+  }
+}
+DownKernel pick_down(int jm, int tokens) { return tokens == 1 ? pick_down_t<1>(jm) : pick_down_t<2>(jm); }
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+int valu_grid(int64_t columns, int blocks_per_cu) {
+  const int64_t want = (int64_t)blocks_per_cu * device_cus();
+  const int64_t need = (columns + kValuWaves - 1) / kValuWaves;
+  return (int)(need < want ? need : want);
+}
+
 }  // namespace
 
-bool gate_up_valu_supported(int tokens, int hidden) {
-  return tokens >= 1 && tokens <= kValuMaxTokens && hidden % 32 == 0 && hidden <= 8192 && gate_up_jm(hidden) > 0;
+bool gate_up_valu_supported(int tokens, int hidden, int max_tiles) {
+  return tokens >= 1 && tokens <= kValuMaxTokens && hidden % 32 == 0 && hidden <= 8192 &&
+         max_tiles <= kMaxLiveTiles && gate_up_jm(hidden) > 0;
 }
 
 bool down_valu_supported(int tokens, int top_k, int inter) {
   const int n = tokens * top_k;
-  if (tokens < 1 || tokens > kValuMaxTokens || inter % 32 != 0 || (int64_t)n * inter * 2 > 64 * 1024) return false;
-  const int jm = down_jm(n, inter);
-  return jm > 0 && (int64_t)n * (inter / 8) <= (int64_t)down_staging_pieces(jm) * kValuBlock;
+  return tokens >= 1 && tokens <= kValuMaxTokens && inter % 32 == 0 && (int64_t)n * inter * 2 <= 64 * 1024 &&
+         down_jm(n, inter) > 0;
 }
 
 hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream) {
-  constexpr int cols = (kValuBlock / 64) * kGateUpCpw;
-  const dim3 grid((p.inter + cols - 1) / cols, max_tiles);
+  const dim3 grid(valu_grid((int64_t)max_tiles * p.inter, kGateUpBlocksPerCu));
   const size_t lds = (size_t)p.tokens * p.hidden * 2;
-  switch (gate_up_jm(p.hidden)) {
-    case 2: hipLaunchKernelGGL((gate_up_valu_kernel<2, kGateUpCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((gate_up_valu_kernel<4, kGateUpCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 5: hipLaunchKernelGGL((gate_up_valu_kernel<5, kGateUpCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 7: hipLaunchKernelGGL((gate_up_valu_kernel<7, kGateUpCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 8: hipLaunchKernelGGL((gate_up_valu_kernel<8, kGateUpCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  auto kern = pick_gate_up(gate_up_jm(p.hidden), p.tokens);
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p, max_tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream) {
-  constexpr int cols = (kValuBlock / 64) * kDownCpw;
-  const dim3 grid((p.hidden + cols - 1) / cols);
+  const dim3 grid(valu_grid(p.hidden, kDownBlocksPerCu));
   const int n = p.tokens * p.top_k;
   const size_t lds = (size_t)n * p.inter * 2;
-  switch (down_jm(n, p.inter)) {
-    case 2: hipLaunchKernelGGL((down_combine_valu_kernel<2, kDownCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((down_combine_valu_kernel<4, kDownCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 7: hipLaunchKernelGGL((down_combine_valu_kernel<7, kDownCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 9: hipLaunchKernelGGL((down_combine_valu_kernel<9, kDownCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    case 14: hipLaunchKernelGGL((down_combine_valu_kernel<14, kDownCpw>), grid, dim3(kValuBlock), lds, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  auto kern = pick_down(down_jm(n, p.inter), p.tokens);
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -127,17 +127,56 @@ __device__ __forceinline__ float mx4_dot32(const u32x4_t& q, float scale, const 
   return acc;
 }
 
-// Stage T rows of K bf16 (row stride ld elements in global memory) into LDS
-// at stride K; 16-byte pieces, all threads of the block.
-__device__ __forceinline__ void valu_stage_rows(const uint16_t* src, int64_t ld, int T, int K, uint16_t* x_lds) {
-  const int per_row = K / 8, total = T * per_row;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((int64_t)T * ld * 2));
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int t = i / per_row, q = i - t * per_row;
-    const u32x4_t v =
-        __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(((int64_t)t * ld + 8 * q) * 2), 0, 0));
-    *reinterpret_cast<u32x4_t*>(x_lds + t * K + 8 * q) = v;
+// Copying `pieces` 16-byte pieces into LDS (dst + 16 * q) with all threads
+// of the block; piece q is read from byte offset off(q) of `rs`.  A batch
+// holds NP pieces per thread, loaded before any is stored, so it costs one
+// round trip; issue and commit are separate so that other loads can be
+// issued in between.
+template <int NP>
+struct StageBatch {
+  u32x4_t v[NP];
+};
+
+template <int NP, typename Off>
+__device__ __forceinline__ void stage_issue(StageBatch<NP>& b, const __amdgpu_buffer_rsrc_t& rs, int pieces, int q0,
+                                            Off off) {
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int q = q0 + (int)threadIdx.x + (int)blockDim.x * i;
+    b.v[i] = __builtin_bit_cast(u32x4_t,
+                                __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(q < pieces ? off(q) : kOob), 0, 0));
   }
+}
+
+template <int NP>
+__device__ __forceinline__ void stage_commit(const StageBatch<NP>& b, int pieces, int q0, uint8_t* dst) {
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int q = q0 + (int)threadIdx.x + (int)blockDim.x * i;
+    if (q < pieces) *reinterpret_cast<u32x4_t*>(dst + 16 * q) = b.v[i];
+  }
+}
+
+// pieces [q_begin, pieces), batch by batch
+template <int NP, typename Off>
+__device__ __forceinline__ void stage_pieces(const __amdgpu_buffer_rsrc_t& rs, int pieces, uint8_t* dst, Off off,
+                                             int q_begin = 0) {
+  for (int q0 = q_begin; q0 < pieces; q0 += NP * (int)blockDim.x) {
+    StageBatch<NP> b;
+    stage_issue<NP>(b, rs, pieces, q0, off);
+    stage_commit<NP>(b, pieces, q0, dst);
+  }
+}
+
+// Stage T rows of K bf16 (row stride ld elements in global memory) into LDS
+// at stride K.
+__device__ __forceinline__ void valu_stage_rows(const uint16_t* src, int64_t ld, int T, int K, uint16_t* x_lds) {
+  const int per_row = K / 8;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((int64_t)T * ld * 2));
+  stage_pieces<4>(rs, T * per_row, reinterpret_cast<uint8_t*>(x_lds), [&](int q) {
+    const int t = q / per_row, c = q - t * per_row;
+    return (uint32_t)(((int64_t)t * ld + 8 * c) * 2);
+  });
 }
 
 }  // namespace moe

@@ -154,9 +154,7 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     L.splitk_gu = kSplitKGateUp && moe::splitk_supported((int)tokens, c->hidden, true);
     L.splitk_dn = moe::splitk_supported((int)tokens, c->inter, false);
     L.down_combine = L.down_combine && !L.splitk_dn && !L.splitk_gu;
-    L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden);
     L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter);
-    if (L.valu_gu || L.valu_dn) L.down_combine = false;  // h stays bf16
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
@@ -168,6 +166,10 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     const int64_t per_expert = (tokens + L.bm - 1) / L.bm;
     const int64_t bound = (n < E ? n : E) * per_expert;
     if (bound < L.max_tiles) L.max_tiles = bound;
+  }
+  if (L.decode) {
+    L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden, (int)L.max_tiles);
+    if (L.valu_gu || L.valu_dn) L.down_combine = false;  // h stays bf16
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
   const int64_t nchunks = moe::permute_chunks(n);
@@ -403,7 +405,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     xmx = at<uint8_t>(ws, L.xmx);
     moe::RouteSmallParams rp{};
     rp.x = x;
-    rp.xmx = xmx;
+    rp.xmx = L.valu_gu ? nullptr : xmx;  // the vector-ALU gate/up reads bf16 x
     rp.scores = scores;
     rp.tokens = (int)T;
     rp.n_experts = E;

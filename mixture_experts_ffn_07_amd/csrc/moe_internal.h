@@ -242,7 +242,7 @@ struct DownValuParams {
   uint16_t* y;                // [T][H]
   int tokens, top_k, hidden, inter;
 };
-bool gate_up_valu_supported(int tokens, int hidden);
+bool gate_up_valu_supported(int tokens, int hidden, int max_tiles);
 bool down_valu_supported(int tokens, int top_k, int inter);
 hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream);
 hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream);
