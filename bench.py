@@ -93,6 +93,12 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
         # few tokens: the shared expert's projections run inside the router and routing launches
         "router_shared_gate_up": e * h * 4 + t * h * 2 + t * e * 4 + 2 * i_s * h * 2 + t * i_s * 2,
         "route_shared_down": t * e * 4 + n * 8 + n * 4 * 2 + h * i_s * 2 + t * i_s * 2 + t * h * 2,
+        # one or two tokens, streaming form: router scores alone, routing beside the shared gate/up,
+        # the shared down projection beside the routed gate/up
+        "router_scores": e * h * 4 + t * h * 2 + 2 * t * e * 4,
+        "route_shared_gate_up": 2 * t * e * 4 + n * 8 + n * 4 * 2 + 2 * i_s * h * 2 + t * h * 2 + t * i_s * 2,
+        "routed_gate_up_shared_down": touched * gu_expert + t * h * 2 + n * i * 2 + h * i_s * 2 + t * i_s * 2
+        + t * h * 2,
         # few-token path: routed and shared experts share a launch, routing is one fused kernel
         "route_permute": t * e * 4 + n * 8 + n * 4 * 2 + (e + 1) * 4,
         "gate_up": touched * gu_expert + 2 * i_s * h * 2 + t * h * 2 + n * i * 2 + t * i_s * 2,
@@ -187,7 +193,10 @@ def main():
     def step_eager(s):
         moe.moe_layer_forward(c, weights[s], x, t, y, None, None, ws)
 
-    graphs = None
+    # HIP graphs: one graph per weight set (one step) and one graph of a whole
+    # cycle over the sets, replayed back to back as a model-level graph would
+    # run consecutive layers; a step is still one whole layer forward
+    graphs = cycle = None
     if not args.no_graph:
         graphs = []
         side = torch.cuda.Stream()
@@ -201,15 +210,25 @@ def main():
             with torch.cuda.graph(g):
                 step_eager(s)
             graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for s in range(sets):
+                step_eager(s)
         torch.cuda.synchronize()
 
     def run(n_steps, offset=0):
-        for i in range(n_steps):
+        i = 0
+        while i < n_steps:
             s = (i + offset) % sets
-            if graphs is not None:
+            if cycle is not None and s == 0 and n_steps - i >= sets:
+                cycle.replay()
+                i += sets
+            elif graphs is not None:
                 graphs[s].replay()
+                i += 1
             else:
                 step_eager(s)
+                i += 1
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -267,7 +286,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
                    "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)", "router_weights": "fp32",
-                   "weight_sets_cycled": sets, "launch": "hipgraph" if graphs is not None else "eager",
+                   "weight_sets_cycled": sets, "launch": "hipgraph (one graph per cycle over the weight sets)" if graphs is not None else "eager",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,

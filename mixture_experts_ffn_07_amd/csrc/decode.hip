@@ -30,6 +30,9 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   __shared__ int32_t idx_sh[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = p.tokens * p.top_k;
+  // the routing is a chain of dependent wave reductions on a CU shared with
+  // streaming waves: highest issue priority for this block's waves
+  __builtin_amdgcn_s_setprio(3);
 
   // x -> MXFP8 rows: one thread per block of 32 values, loads first
   if (p.xmx) {
@@ -200,6 +203,36 @@ __global__ __launch_bounds__(256) void decode_mid_valu_kernel(RouteSmallParams p
         if (n + r < H) m.y_sh[(int64_t)t * H + n + r] = f32_to_bf16(out[r][t]);
 }
 
+// Launch 2 of the streaming few-token layer (T <= kValuMaxTokens; launch 1 is
+// the router GEMV writing the scores): block 0 routes, the other blocks
+// compute the shared gate/up row pairs, so the routing latency hides behind
+// the shared expert's weight stream.
+template <int MPL>
+__global__ __launch_bounds__(256) void decode_route_shared_gu_kernel(FrontValuParams f, RouteSmallParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x rows [T][hidden] bf16
+  if (blockIdx.x == 0) {
+    route_small_block<MPL>(p);
+    return;
+  }
+  uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = f.hidden, T = f.tokens, Is = f.shared_inter;
+  const int nrow = ((int)blockIdx.x - 1) * 4 + wave;  // gate/up pair
+  const bool ok = nrow < Is;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.sh_gu, (uint32_t)((int64_t)2 * Is * H * 2));
+  const uint32_t off[2] = {ok ? (uint32_t)nrow * (uint32_t)H * 2u : kOob,
+                           ok ? (uint32_t)(Is + nrow) * (uint32_t)H * 2u : kOob};
+  ValuRows<8, 10, 2> st;
+  valu_issue<8, 10, 2>(st, rw, off, H);
+  valu_stage_rows(f.x, H, T, H, x_lds);
+  __syncthreads();
+  float out2[2][kValuMaxTokens];
+  valu_compute<8, 10, 2, kValuMaxTokens>(st, x_lds, H, T, H, out2);
+  if (lane == 0 && ok)
+    for (int t = 0; t < T; ++t)
+      f.h_sh[(int64_t)t * Is + nrow] = f32_to_bf16(clamped_swiglu(out2[0][t], out2[1][t], f.limit));
+}
+
 bool decode_valu_supported(int tokens, int hidden, int shared_inter) {
   return tokens <= kValuMaxTokens && hidden <= 5120 && shared_inter <= 5120;
 }
@@ -222,6 +255,19 @@ hipError_t launch_decode_mid_valu(const RouteSmallParams& p, const MidValuParams
   const int shared_blocks = m.sh_dn ? (m.hidden + 7) / 8 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)(1 + shared_blocks)), dim3(256),
                      (size_t)m.tokens * (m.shared_inter > 0 ? m.shared_inter : 8) * 2, stream, p, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_route_shared_gu(const FrontValuParams& f, const RouteSmallParams& p, hipStream_t stream) {
+  const int nj = (p.n_experts + 63) / 64;
+  auto kern = nj <= 2   ? decode_route_shared_gu_kernel<2>
+              : nj <= 4 ? decode_route_shared_gu_kernel<4>
+              : nj <= 6 ? decode_route_shared_gu_kernel<6>
+              : nj <= 8 ? decode_route_shared_gu_kernel<8>
+                        : decode_route_shared_gu_kernel<16>;
+  const int shared_blocks = f.sh_gu ? (f.shared_inter + 3) / 4 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + shared_blocks)), dim3(256), (size_t)f.tokens * f.hidden * 2, stream,
+                     f, p);
   return hipGetLastError();
 }
 

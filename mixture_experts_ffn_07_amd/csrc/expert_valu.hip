@@ -72,9 +72,10 @@ __device__ __forceinline__ void gu_issue(ColBuf<JM>& b, const uint8_t* gu_q, con
   }
 }
 
+// blocks blk of nblk run the gate/up loop; lds holds x rows [T][H] bf16
 template <int JM, int TM>
-__global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuParams p, int max_tiles) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x rows [T][H] bf16
+__device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, int max_tiles, int blk, int nblk,
+                                                    uint8_t* lds) {
   uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.tokens, H = p.hidden, I = p.inter, VR = H / 32;
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuPara
   const int c_r = __builtin_amdgcn_ds_permute(dst, rows);
   const int c_s = __builtin_amdgcn_ds_permute(dst, min(max(r0, 0), T - 1) | (min(max(r1, 0), T - 1) << 16));
   const int total = n_live * I;
-  const int W = (int)gridDim.x * kValuWaves;
-  const int wg = (int)blockIdx.x * kValuWaves + wave;
+  const int W = nblk * kValuWaves;
+  const int wg = blk * kValuWaves + wave;
 
   auto item = [&](int it) {
     GuItem g;
@@ -168,6 +169,69 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuPara
     gu_issue<JM>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
     if (g1.tile >= 0) compute(b1, g1);
   }
+}
+
+template <int JM, int TM>
+__global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuParams p, int max_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  gate_up_valu_blocks<JM, TM>(p, max_tiles, (int)blockIdx.x, (int)gridDim.x, lds);
+}
+
+// ---------------------------------------------------------------- shared expert down
+// Rows n of W_sd (bf16 [H][I_s]) against h_sh (T rows staged in LDS):
+// y_sh[t][n], one row per wave at a time, grid-stride with two buffers.
+template <int KVD, int TM>
+__device__ __forceinline__ void shared_down_blocks(const MidValuParams& m, int blk, int nblk, uint8_t* lds) {
+  uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = m.hidden, Is = m.shared_inter, T = m.tokens;
+  const int W = nblk * kValuWaves, wg = blk * kValuWaves + wave;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.sh_dn, (uint32_t)((int64_t)H * Is * 2));
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(m.h_sh, (uint32_t)(T * Is * 2));
+  const int pieces = T * (Is / 8);
+  auto h_off = [&](int q) {
+    const int t = q / (Is / 8), c = q - t * (Is / 8);
+    return (uint32_t)((t * Is + 8 * c) * 2);
+  };
+  StageBatch<4> hb;
+  stage_issue<4>(hb, rh, pieces, 0, h_off);
+  auto issue = [&](ValuRows<8, KVD, 1>& b, int n) {
+    const uint32_t off[1] = {n < H ? (uint32_t)n * (uint32_t)Is * 2u : kOob};
+    valu_issue<8, KVD, 1>(b, rw, off, Is);
+  };
+  auto compute = [&](const ValuRows<8, KVD, 1>& b, int n) {
+    float out[1][TM];
+    valu_compute<8, KVD, 1, TM>(b, h_lds, Is, T, Is, out);
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        if (t < T) m.y_sh[(int64_t)t * H + n] = f32_to_bf16(out[0][t]);
+  };
+  ValuRows<8, KVD, 1> b0, b1;
+  issue(b0, wg);
+  stage_commit<4>(hb, pieces, 0, lds);
+  stage_pieces<4>(rh, pieces, lds, h_off, 4 * kValuBlock);
+  __syncthreads();
+  for (int n = wg; n < H; n += 2 * W) {
+    issue(b1, n + W);
+    compute(b0, n);
+    issue(b0, n + 2 * W);
+    if (n + W < H) compute(b1, n + W);
+  }
+}
+
+// Launch 3 of the streaming few-token layer: blocks [0, gu_blocks) run the
+// routed gate/up loop, the rest the shared expert's down loop; the two are
+// independent and stream together.
+template <int JM, int TM, int KVD>
+__global__ __launch_bounds__(kValuBlock) void gate_up_shared_down_kernel(GateUpValuParams p, int max_tiles,
+                                                                         MidValuParams m, int gu_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int b = (int)blockIdx.x;
+  if (b < gu_blocks)
+    gate_up_valu_blocks<JM, TM>(p, max_tiles, b, gu_blocks, lds);
+  else
+    shared_down_blocks<KVD, TM>(m, b - gu_blocks, (int)gridDim.x - gu_blocks, lds);
 }
 
 // ---------------------------------------------------------------- down + combine
@@ -269,6 +333,7 @@ constexpr int kDownJm[] = {2, 4, 7, 9, 14};
 // blocks per CU of the grid-stride loops (all resident at once)
 constexpr int kGateUpBlocksPerCu = 2;
 constexpr int kDownBlocksPerCu = 2;
+constexpr int kSharedDownBlocksPerCu = 1;
 
 int gate_up_jm(int hidden) {
   const int need = (2 * (hidden / 32) + 63) / 64;
@@ -285,6 +350,24 @@ int down_jm(int slots, int inter) {
 }
 
 using GateUpKernel = void (*)(GateUpValuParams, int);
+using GateUpSdKernel = void (*)(GateUpValuParams, int, MidValuParams, int);
+
+template <int TM, int KVD>
+GateUpSdKernel pick_gate_up_sd_t(int jm) {
+  switch (jm) {
+    case 2: return gate_up_shared_down_kernel<2, TM, KVD>;
+    case 4: return gate_up_shared_down_kernel<4, TM, KVD>;
+    case 5: return gate_up_shared_down_kernel<5, TM, KVD>;
+    case 7: return gate_up_shared_down_kernel<7, TM, KVD>;
+    case 8: return gate_up_shared_down_kernel<8, TM, KVD>;
+    default: return nullptr;
+  }
+}
+GateUpSdKernel pick_gate_up_sd(int jm, int tokens, int kvd) {
+  if (kvd == 5) return tokens == 1 ? pick_gate_up_sd_t<1, 5>(jm) : pick_gate_up_sd_t<2, 5>(jm);
+  if (kvd == 10) return tokens == 1 ? pick_gate_up_sd_t<1, 10>(jm) : pick_gate_up_sd_t<2, 10>(jm);
+  return nullptr;
+}
 using DownKernel = void (*)(DownValuParams);
 
 template <int TM>
@@ -350,6 +433,24 @@ hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStre
   auto kern = pick_gate_up(gate_up_jm(p.hidden), p.tokens);
   if (!kern) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p, max_tiles);
+  return hipGetLastError();
+}
+
+bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter) {
+  return gate_up_valu_supported(tokens, hidden, max_tiles) && shared_inter > 0 && shared_inter % 8 == 0 &&
+         shared_inter <= 10 * 8 * 64;
+}
+
+hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, const MidValuParams& m,
+                                      hipStream_t stream) {
+  const int gu_blocks = valu_grid((int64_t)max_tiles * p.inter, kGateUpBlocksPerCu);
+  const int sd_blocks = valu_grid(m.hidden, kSharedDownBlocksPerCu);
+  const int kvd = m.shared_inter <= 5 * 8 * 64 ? 5 : 10;
+  auto kern = pick_gate_up_sd(gate_up_jm(p.hidden), p.tokens, kvd);
+  if (!kern) return hipErrorInvalidValue;
+  const size_t lx = (size_t)p.tokens * p.hidden * 2, lh = (size_t)m.tokens * m.shared_inter * 2;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gu_blocks + sd_blocks)), dim3(kValuBlock), lx > lh ? lx : lh, stream, p,
+                     max_tiles, m, gu_blocks);
   return hipGetLastError();
 }
 

@@ -128,6 +128,8 @@ struct WsLayout {
   bool splitk_dn = false;     // decode: routed down by the split-K MXFP4 kernel
   bool valu_gu = false;       // decode, T <= 2: routed gate/up one wave per column on the vector ALUs
   bool valu_dn = false;       // decode, T <= 2: routed down + combine one wave per column on the vector ALUs
+  bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
+                              // down; routed down + combine
   Region logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh;
   size_t total = 0;
@@ -170,6 +172,10 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   if (L.decode) {
     L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden, (int)L.max_tiles);
     if (L.valu_gu || L.valu_dn) L.down_combine = false;  // h stays bf16
+    L.stream4 = L.valu_gu && L.valu_dn &&
+              moe::decode_valu_supported((int)tokens, c->hidden, c->n_shared ? c->shared_inter : 0) &&
+              (c->n_shared == 0 ||
+               moe::gate_up_shared_down_supported((int)tokens, c->hidden, (int)L.max_tiles, c->shared_inter));
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
   const int64_t nchunks = moe::permute_chunks(n);
@@ -345,6 +351,99 @@ moe_status run_experts_decode(const moe_config* c, const moe_weights* w, const u
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");
   if (c->n_shared == 1) return run_shared_decode(c, w, x, T, y_shared, ws, L, st, tl);
+  return MOE_OK;
+}
+
+// Few-token layer, T <= 2, streaming form (see launch_decode_route_shared_gu).
+moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
+                                 uint16_t* y, int32_t* idx, float* wts, void* ws, const WsLayout& L, hipStream_t st,
+                                 Timeline* tl) {
+  const int E = c->n_experts;
+  uint16_t* y_sh = c->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;
+  uint16_t* h_sh = c->n_shared ? at<uint16_t>(ws, L.h_sh) : nullptr;
+  int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  moe::GemmTile* tiles = at<moe::GemmTile>(ws, L.tiles);
+
+  moe::FrontValuParams f{};
+  f.x = x;
+  f.router_w = w->router_w;
+  f.bias = w->router_bias;
+  f.scores = at<float>(ws, L.scores);
+  f.sh_gu = c->n_shared ? w->sh_gu : nullptr;
+  f.h_sh = h_sh;
+  f.shared_inter = c->n_shared ? c->shared_inter : 0;
+  f.tokens = (int)T;
+  f.n_experts = E;
+  f.hidden = c->hidden;
+  f.limit = c->swiglu_limit;
+  moe::RouteSmallParams rp{};
+  rp.x = x;
+  rp.xmx = nullptr;
+  rp.scores = f.scores;
+  rp.tokens = (int)T;
+  rp.n_experts = E;
+  rp.hidden = c->hidden;
+  rp.top_k = c->top_k;
+  rp.route_scale = c->route_scale;
+  rp.idx = idx;
+  rp.w = wts;
+  rp.sorted_slots = at<int32_t>(ws, L.sorted);
+  rp.slot_pos = slot_pos;
+  rp.tiles = tiles;
+  rp.tile_count = at<int32_t>(ws, L.tile_count);
+  rp.tile_rows = at<int32_t>(ws, L.tile_rows);
+  rp.max_tiles = (int)L.max_tiles;
+  hipError_t err =
+      moe::launch_router_gemv(x, w->router_w, nullptr, (int)T, E, c->hidden, f.scores, w->router_bias, st);
+  if (err == hipSuccess) err = mark(tl, "router_scores", st);
+  if (err != hipSuccess) return fail_hip(err, "router launch");
+  err = moe::launch_decode_route_shared_gu(f, rp, st);
+  if (err == hipSuccess) err = mark(tl, "route_shared_gate_up", st);
+  if (err != hipSuccess) return fail_hip(err, "routing/shared gate-up launch");
+
+  moe::GateUpValuParams g{};
+  g.x = x;
+  g.tiles = tiles;
+  g.tile_rows = rp.tile_rows;
+  g.gu_q = w->gu_q;
+  g.gu_s = w->gu_s;
+  g.h = at<uint16_t>(ws, L.h);
+  g.tokens = (int)T;
+  g.hidden = c->hidden;
+  g.inter = c->inter;
+  g.limit = c->swiglu_limit;
+  if (c->n_shared) {
+    moe::MidValuParams m{};
+    m.sh_dn = w->sh_dn;
+    m.h_sh = h_sh;
+    m.y_sh = y_sh;
+    m.shared_inter = c->shared_inter;
+    m.tokens = (int)T;
+    m.hidden = c->hidden;
+    err = moe::launch_gate_up_shared_down(g, (int)L.max_tiles, m, st);
+    if (err == hipSuccess) err = mark(tl, "routed_gate_up_shared_down", st);
+  } else {
+    err = moe::launch_gate_up_valu(g, (int)L.max_tiles, st);
+    if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
+  }
+  if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+
+  moe::DownValuParams dv{};
+  dv.h = g.h;
+  dv.idx = idx;
+  dv.topk_w = wts;
+  dv.slot_pos = slot_pos;
+  dv.dn_q = w->dn_q;
+  dv.dn_s = w->dn_s;
+  dv.y_shared = y_sh;
+  dv.y = y;
+  dv.tokens = (int)T;
+  dv.top_k = c->top_k;
+  dv.hidden = c->hidden;
+  dv.inter = c->inter;
+  err = moe::launch_down_combine_valu(dv, st);
+  if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
+  if (err != hipSuccess) return fail_hip(err, "down/combine launch");
   return MOE_OK;
 }
 
@@ -704,6 +803,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  if (L.stream4) return layer_forward_decode4(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
   if (L.decode) return layer_forward_decode(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
   if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
   if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;

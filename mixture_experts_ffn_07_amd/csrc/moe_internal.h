@@ -246,6 +246,15 @@ bool gate_up_valu_supported(int tokens, int hidden, int max_tiles);
 bool down_valu_supported(int tokens, int top_k, int inter);
 hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream);
 hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream);
+// The streaming few-token layer (T <= 2), four launches:
+//   1. router GEMV writing the scores (launch_router_gemv);
+//   2. the routing block beside the shared gate/up;
+//   3. routed gate/up beside the shared down projection;
+//   4. routed down with the combine (launch_down_combine_valu).
+hipError_t launch_decode_route_shared_gu(const FrontValuParams& f, const RouteSmallParams& p, hipStream_t stream);
+bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter);
+hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, const MidValuParams& m,
+                                      hipStream_t stream);
 
 // Fused few-token routing: top-k of every token + permutation + tile table (T*k <= 1024).
 hipError_t launch_route_permute_small(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
