@@ -842,11 +842,14 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   }
 }
 
-int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4) {
+int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4, bool k_pipelined) {
   const int kTiledRows = 16 * (fp4 ? tiled_m<true>() : tiled_m<false>());
-  // rows per group on average decides the row-tile height; 128-row tiles go
-  // to the LDS-tiled kernel, which needs enough of them to fill the chip
-  // (its blocks are 128 output columns wide)
+  // MXFP4 weights with every K a multiple of 128: the pipelined kernel at any
+  // row count (it streams each expert's weights once per tile and measured
+  // faster than 16-row tiles even at 1-5 rows per expert).  Otherwise rows
+  // per group on average decides: 128-row tiles go to the LDS-tiled kernel,
+  // which needs enough of them to fill the chip.
+  if (fp4 && k_pipelined) return kTiledRows / 16;
   const int64_t avg = n_groups > 0 ? (n_rows + n_groups - 1) / n_groups : n_rows;
   const int64_t tiles = (n_rows + kTiledRows - 1) / kTiledRows;
   return (avg > 16 && tiles >= 16) ? kTiledRows / 16 : 1;

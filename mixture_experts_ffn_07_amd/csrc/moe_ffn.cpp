@@ -140,8 +140,8 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   const int64_t n = tokens * c->top_k;
   const int E = c->n_experts;
   L.router = moe::router_plan(tokens, E, c->hidden);
-  L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E), true);
-  L.shared_mt = moe::expert_gemm_mt(tokens, 1, false);
+  L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E), true, c->hidden % 128 == 0 && c->inter % 128 == 0);
+  L.shared_mt = moe::expert_gemm_mt(tokens, 1, false, false);
   const int k_fp4 = c->hidden > c->inter ? c->hidden : c->inter;
   const int k_bf16 = c->n_shared ? (c->hidden > c->shared_inter ? c->hidden : c->shared_inter) : 0;
   L.decode = tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&

@@ -82,8 +82,9 @@ struct GemmParams {
   int64_t ldc;
   float limit;
 };
-// rows per tile / 16 for the grouped GEMM (MXFP4 or bf16 weights)
-int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4);
+// rows per tile / 16 for the grouped GEMM (MXFP4 or bf16 weights);
+// k_pipelined: every K of the problem is a multiple of 128
+int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4, bool k_pipelined);
 hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, bool fp4, int mt, int64_t grid_tiles,
                               hipStream_t stream);
 

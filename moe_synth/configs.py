@@ -53,6 +53,11 @@ CONFIGS = {
     # full-size prefill, 4096 tokens
     "prefill_t4096_h5120_e384": LayerConfig("prefill_t4096_h5120_e384", 4096, 5120, 384, 6, 2304, 1, 2304,
                                             cfg_id=4),
+    # speculative-verify decode: one sequence with a 5-token draft block, and 64 sequences of 5
+    "verify_t5_h5120_e384": LayerConfig("verify_t5_h5120_e384", 5, 5120, 384, 6, 2304, 1, 2304, cfg_id=6),
+    "verify_t320_h5120_e384": LayerConfig("verify_t320_h5120_e384", 320, 5120, 384, 6, 2304, 1, 2304, cfg_id=7),
+    # DeepSeek-V4-Pro MoE dimensions (hidden 7168, expert width 3072), one decode token
+    "pro_t1_h7168_e384": LayerConfig("pro_t1_h7168_e384", 1, 7168, 384, 6, 3072, 1, 3072, cfg_id=8),
     # skewed routing on the drafter-style MoE, 16384 tokens
     "skew_t16384_h5120_e128": LayerConfig("skew_t16384_h5120_e128", 16384, 5120, 128, 3, 2304, 1, 2304,
                                           bias="zipf", cfg_id=5),

@@ -203,7 +203,8 @@ def _sample(n, count, seed, must=()):
 
 
 @pytest.mark.parametrize("name,count", [("decode_t64_h5120_e384", 12), ("prefill_t4096_h5120_e384", 10),
-                                        ("skew_t16384_h5120_e128", 10)])
+                                        ("skew_t16384_h5120_e128", 10), ("verify_t5_h5120_e384", 5),
+                                        ("verify_t320_h5120_e384", 12), ("pro_t1_h7168_e384", 1)])
 def test_layer_full_size_sampled(name, count):
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, seed=0, device=DEV)
