@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed forwards per weight set for kernel times")
-    ap.add_argument("--cpu-sample", type=int, default=8, help="decode tokens the CPU oracle runs (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="decode tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy 3x (reference for hardware byte counters)")
