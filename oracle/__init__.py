@@ -13,6 +13,8 @@ exactly), directly from the definitions, with no tiling, fusion or reordering.
 from .moe_oracle import (  # noqa: F401
     E2M1_CODE_BITS,
     bf16_bits_to_f64,
+    f64_to_bf16_bits,
+    rmsnorm,
     e2m1_value,
     e2m1_table,
     e8m0_value,

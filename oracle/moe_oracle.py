@@ -44,7 +44,13 @@ notes of the repository):
 * MXFP4 layout: element 2i of a row in the low nibble of byte i, element
   2i+1 in the high nibble; one E8M0 byte per 32 consecutive elements of a row,
   stored as a separate [rows, K/32] array.
-* y = shared(x) + sum_j w_j * expert_{idx_j}(x); no residual, no norm.
+* y = shared(x) + sum_j w_j * expert_{idx_j}(x); no residual.
+* Optional pre-FFN norm (off unless a gain vector is given): the MAX API's
+  ``DeepseekV41Config`` has ``rms_norm_eps`` = 1e-20 and the atlas page's
+  ``config.json`` ``norm_eps`` = 1e-20, while the architecture sheet lists the
+  norm type as not disclosed.  Reading: RMSNorm over the hidden dimension,
+  x_n = x / sqrt(mean(x^2) + eps) * gamma with a bf16 gain gamma, its output
+  rounded to bf16 (nearest, ties to even) before the router and the experts.
 """
 
 from __future__ import annotations
@@ -66,6 +72,28 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     """Exact value of bf16 bit patterns: bf16 is the high half of binary32."""
     b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    """bf16 bit patterns of the values nearest to ``v`` (ties to an even significand).
+
+    A normal bf16 has 8 significant bits: with v = m * 2^e, 0.5 <= |m| < 1,
+    the rounded value is rint(m * 2^8) * 2^(e - 8), ``rint`` rounding halves to
+    even.  Zeros stay zeros; values outside the normal range are not needed.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    r = np.ldexp(np.rint(m * 256.0), e - 8)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def rmsnorm(x_bits, gamma_bits, eps: float) -> np.ndarray:
+    """RMSNorm of each row of bf16 ``x_bits`` with bf16 gain ``gamma_bits``,
+    rounded to bf16 bits: x / sqrt(mean(x^2) + eps) * gamma (reading above)."""
+    x = bf16_bits_to_f64(x_bits)
+    g = bf16_bits_to_f64(gamma_bits)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return f64_to_bf16_bits(x * r * g)
 
 
 def e2m1_value(code: int) -> float:
@@ -307,7 +335,7 @@ def combine(y_slot, slot_pos, w, y_shared, top_k: int) -> np.ndarray:
 
 def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn,
                   top_k: int, route_scale: float, swiglu_limit: float,
-                  tokens=None, selections=None) -> dict:
+                  tokens=None, selections=None, norm_gamma=None, norm_eps: float = 1e-20) -> dict:
     """The whole layer for the rows ``tokens`` of ``x_bits`` (all rows if None).
 
     ``gu_q`` ... ``dn_s`` only need to support ``[e]`` (per-expert arrays of
@@ -315,12 +343,17 @@ def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, 
     expert.  ``selections`` optionally replaces the routed selection of each
     row by one of the oracle's own ``valid_selections``.
 
+    With ``norm_gamma`` (bf16 bits [H]) the rows are first RMS-normalised
+    (``rmsnorm``) and the layer runs on the result.
+
     Returns the router outputs, the permutation, ``h_slot`` [T*k, I] and
     ``y_slot`` [T*k, H] in position order, ``y_shared`` [T, H] and ``y`` [T, H].
     """
     x_bits = np.asarray(x_bits)
     if tokens is not None:
         x_bits = x_bits[np.asarray(tokens)]
+    if norm_gamma is not None:
+        x_bits = rmsnorm(x_bits, norm_gamma, norm_eps)
     t_count, hidden = x_bits.shape
     r = route(x_bits, router_w, router_bias, top_k, route_scale)
     idx, w = r["idx"], r["w"]

@@ -4,8 +4,10 @@ Sources of truth used here: the sizes the pages print (tests/golden/page_sizes.j
 textbook values of the number formats (OCP Microscaling v1.0 E2M1 and E8M0),
 closed forms and identities of softplus and silu, brute force over all k-subsets
 for top-k, exact invariants of the layer (zero input, zero routed weights, a
-scale byte raised by one), and a hand-worked two-expert layer
-(tests/golden/two_expert_example.json).
+scale byte raised by one), a hand-worked two-expert layer
+(tests/golden/two_expert_example.json), and for the optional pre-FFN RMSNorm
+torch's float64 rms_norm, its fp32->bf16 cast, hand-worked rows and scale
+invariance.
 """
 
 import itertools
@@ -451,3 +453,91 @@ def test_zipf_bias_gives_twentyfold_hot_expert():
     load = np.bincount(r["idx"].reshape(-1), minlength=cfg.n_experts)
     ratio = load.max() / load.mean()
     assert 16.0 <= ratio <= 24.0, ratio
+
+
+# ---------------------------------------------------------------- pre-FFN RMSNorm (eps 1e-20)
+
+def _bf16_bits(values):
+    """bf16 bits of values that are exact in bf16 (checked)."""
+    t = torch.tensor(values, dtype=torch.float32)
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.float(), t)
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch_cast_and_ties_to_even():
+    """fp64 -> bf16 rounding against torch's fp32 -> bf16 cast (nearest, ties to
+    even) on fp32-exact values, plus hand-made ties."""
+    g = np.random.default_rng(3)
+    v = (g.standard_normal(20000) * np.exp2(g.integers(-20, 20, 20000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_bits(v.astype(np.float64)), want)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0, -0.0])
+    got = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(ties))
+    assert got.tolist() == [1.0, 1 + 2.0 ** -6, -1.0, 0.0, 0.0]
+    assert oracle.f64_to_bf16_bits(np.array([-0.0]))[0] == 0x8000
+
+
+def test_rmsnorm_hand_example():
+    """x = (3, 4): mean square 12.5, so x/rms = (0.848528.., 1.131370..); the bf16
+    neighbours are 217/256 and 145/128.  With gain (2, 1/2): 1.697.. -> 217/128,
+    0.5657.. -> 145/256."""
+    x = _bf16_bits([[3.0, 4.0]])
+    one = _bf16_bits([1.0, 1.0])
+    out = oracle.bf16_bits_to_f64(oracle.rmsnorm(x, one, 1e-20))
+    assert out.tolist() == [[217 / 256, 145 / 128]]
+    out = oracle.bf16_bits_to_f64(oracle.rmsnorm(x, _bf16_bits([2.0, 0.5]), 1e-20))
+    assert out.tolist() == [[217 / 128, 145 / 256]]
+
+
+def test_rmsnorm_special_rows():
+    """A constant row maps to +-gain, a zero row to zero (eps keeps it finite), a
+    one-hot row of width n to sqrt(n) at its place."""
+    h = 64
+    one = _bf16_bits([1.0] * h)
+    rows = _bf16_bits([[0.375] * h, [-96.0] * h, [0.0] * h, [0.0] * 5 + [7.0] + [0.0] * (h - 6)])
+    out = oracle.bf16_bits_to_f64(oracle.rmsnorm(rows, one, 1e-20))
+    assert np.all(out[0] == 1.0) and np.all(out[1] == -1.0) and np.all(out[2] == 0.0)
+    assert out[3, 5] == 8.0 and np.count_nonzero(out[3]) == 1   # sqrt(64) = 8
+
+
+def test_rmsnorm_matches_torch_and_invariants():
+    """Against torch's rms_norm in float64 (within half a bf16 step), exact under a
+    power-of-two rescale of the input, linear in a power-of-two gain, and of unit
+    RMS with unit gain (within bf16 rounding)."""
+    g = np.random.default_rng(4)
+    t, h = 16, 512
+    xf = (g.standard_normal((t, h)) * np.exp2(g.integers(-6, 6, (t, 1)))).astype(np.float32)
+    x = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    gam = torch.from_numpy((1 + 0.1 * g.standard_normal(h)).astype(np.float32)).to(torch.bfloat16)
+    gbits = gam.view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_bits_to_f64(oracle.rmsnorm(x, gbits, 1e-20))
+    ref = torch.nn.functional.rms_norm(
+        torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double(), (h,),
+        weight=gam.double(), eps=1e-20).numpy()
+    half_step = np.exp2(np.floor(np.log2(np.abs(ref))) - 8)
+    assert np.all(np.abs(got - ref) <= half_step * (1 + 1e-9))
+    x4 = oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(x) * 4.0)
+    assert np.array_equal(oracle.rmsnorm(x4, gbits, 1e-20), oracle.rmsnorm(x, gbits, 1e-20))
+    g2 = oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(gbits) * 0.5)
+    assert np.array_equal(oracle.bf16_bits_to_f64(oracle.rmsnorm(x, g2, 1e-20)), got * 0.5)
+    unit = oracle.bf16_bits_to_f64(oracle.rmsnorm(x, _bf16_bits([1.0] * h), 1e-20))
+    assert np.allclose(np.sqrt(np.mean(unit ** 2, axis=1)), 1.0, atol=2 ** -8)
+
+
+def test_layer_with_norm_is_scale_invariant_and_normalises_first():
+    """With the norm on, the layer output does not change when the input is scaled
+    by a power of two, and equals the norm-free layer on a row already normalised."""
+    inp = _tiny_inputs()
+    a = inp.oracle_args()
+    h = inp.cfg.hidden
+    gbits = torch.from_numpy(np.random.default_rng(5).normal(1, 0.1, h).astype(np.float32)) \
+        .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    base = oracle.layer_forward(**a, norm_gamma=gbits, norm_eps=1e-20)
+    a8 = dict(a, x_bits=oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(a["x_bits"]) * 8.0))
+    scaled = oracle.layer_forward(**a8, norm_gamma=gbits, norm_eps=1e-20)
+    assert np.array_equal(base["y"], scaled["y"]) and np.array_equal(base["idx"], scaled["idx"])
+    plain = oracle.layer_forward(**dict(a, x_bits=oracle.rmsnorm(a["x_bits"], gbits, 1e-20)))
+    assert np.array_equal(base["y"], plain["y"])
+    raw = oracle.layer_forward(**a)
+    assert not np.array_equal(base["y"], raw["y"])
