@@ -79,11 +79,13 @@ def f64_to_bf16_bits(v) -> np.ndarray:
 
     A normal bf16 has 8 significant bits: with v = m * 2^e, 0.5 <= |m| < 1,
     the rounded value is rint(m * 2^8) * 2^(e - 8), ``rint`` rounding halves to
-    even.  Zeros stay zeros; values outside the normal range are not needed.
+    even.  Below 2^-126 bf16 is subnormal with the fixed step 2^-133.  Zeros
+    keep their sign; overflow past the largest bf16 is not needed here.
     """
     v = np.asarray(v, dtype=np.float64)
     m, e = np.frexp(v)
-    r = np.ldexp(np.rint(m * 256.0), e - 8)
+    r = np.where(np.abs(v) < 2.0 ** -126, np.rint(v * 2.0 ** 133) * 2.0 ** -133,
+                 np.ldexp(np.rint(m * 256.0), e - 8))
     return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 

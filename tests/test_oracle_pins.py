@@ -470,6 +470,9 @@ def test_bf16_rounding_matches_torch_cast_and_ties_to_even():
     even) on fp32-exact values, plus hand-made ties."""
     g = np.random.default_rng(3)
     v = (g.standard_normal(20000) * np.exp2(g.integers(-20, 20, 20000))).astype(np.float32)
+    # fp32 subnormals and the smallest normals, where bf16 steps by 2^-133
+    sub = g.integers(-(1 << 24), 1 << 24, 4000).astype(np.int64)
+    v = np.concatenate([v, (sub * 2.0 ** -149).astype(np.float32)])
     want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.f64_to_bf16_bits(v.astype(np.float64)), want)
     ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0, -0.0])
