@@ -96,6 +96,9 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
         # one or two tokens, streaming form: router scores alone, routing beside the shared gate/up,
         # the shared down projection beside the routed gate/up
         "router_scores": e * h * 4 + t * h * 2 + 2 * t * e * 4,
+        # pre-FFN RMSNorm: inside the router launch (x, gain, normalised rows out), or a launch of its own
+        "norm_router_scores": e * h * 4 + t * h * 2 + h * 2 + t * h * 2 + 2 * t * e * 4,
+        "rmsnorm": 2 * t * h * 2 + h * 2,
         "route_shared_gate_up": 2 * t * e * 4 + n * 8 + n * 4 * 2 + 2 * i_s * h * 2 + t * h * 2 + t * i_s * 2,
         "routed_gate_up_shared_down": touched * gu_expert + t * h * 2 + n * i * 2 + h * i_s * 2 + t * i_s * 2
         + t * h * 2,
@@ -286,6 +289,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
                    "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)", "router_weights": "fp32",
+                   "pre_ffn_rmsnorm": bool(cfg.norm),
                    "weight_sets_cycled": sets, "launch": "hipgraph (one graph per cycle over the weight sets)" if graphs is not None else "eager",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -20,6 +20,13 @@
  *     o_e     = h W_d^T
  *     y[t]    = o_shared(x[t]) + sum_j w[t,j] * o_{idx_j}(x[t])
  *
+ *   With a norm gain gamma (moe_weights.norm_gamma non-NULL), the layer
+ *   first replaces each row by its RMSNorm (eps = moe_config.norm_eps,
+ *   1e-20 in DeepseekV41Config's rms_norm_eps and config.json's norm_eps):
+ *     x[t,h] <- bf16( x[t,h] / sqrt(mean_h' x[t,h']^2 + eps) * gamma[h] )
+ *   rounded once, to nearest even.  The norm type is not disclosed on the
+ *   'DeepSeek-V4.1-Flash' architecture sheet; RMSNorm is the reading taken.
+ *
  * Conventions that hold for every entry point:
  *
  *   Memory.  Every tensor pointer is a DEVICE pointer owned by the caller
@@ -65,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -90,6 +97,8 @@ typedef struct moe_config {
   float route_scale;     /* rho: 1.5, multiplies the routed weights only */
   float swiglu_limit;    /* L: 10.0 */
   int32_t score_func;    /* 0 = sqrtsoftplus (the only one) */
+  float norm_eps;        /* eps of the pre-FFN RMSNorm, 1e-20; read only when a norm gain is given,
+                            then finite and > 0 */
 } moe_config;
 
 /* Weights: device pointers, layouts as in the header comment. */
@@ -102,11 +111,23 @@ typedef struct moe_weights {
   const uint8_t* dn_s;       /* [E][H][I/32]  E8M0 scales                         */
   const uint16_t* sh_gu;     /* [2I_s][H] bf16, gate rows then up rows; NULL iff n_shared == 0 */
   const uint16_t* sh_dn;     /* [H][I_s] bf16; NULL iff n_shared == 0             */
+  const uint16_t* norm_gamma; /* [H] bf16 gain of the pre-FFN RMSNorm, or NULL: no norm.
+                                 Read by moe_layer_forward(_timed) only. */
 } moe_weights;
 
 /* Bytes of workspace every entry point below needs for `tokens` tokens
  * (the maximum over them).  Returns 0 for an invalid config. */
 size_t moe_workspace_bytes(const moe_config* cfg, int64_t tokens);
+
+/* Pre-FFN RMSNorm of T rows: x_norm[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)
+ * * gamma), eps = cfg->norm_eps, rounded once to nearest even (the layer
+ * formula above).  x, x_norm: bf16 [T][H]; gamma: bf16 [H].  x_norm may be
+ * x itself (in place); other overlaps are unspecified.  Needs no workspace.
+ * Checked as above, plus: gamma non-NULL and 16-byte aligned, norm_eps
+ * finite and > 0.  The other entry points take x as given: to run them on
+ * normalised rows, call this first (moe_layer_forward does it itself). */
+moe_status moe_rmsnorm(const moe_config* cfg, const uint16_t* gamma, const uint16_t* x, int64_t tokens,
+                       uint16_t* x_norm, void* stream);
 
 /* Router: logits, sqrtsoftplus scores, top-k, weights.
  * x: bf16 [T][H].  Outputs: topk_idx int32 [T][k] in selection order,
@@ -146,8 +167,10 @@ moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int3
                        const float* topk_w, const uint16_t* y_shared, int64_t tokens,
                        uint16_t* y, void* stream);
 
-/* The whole layer: y bf16 [T][H] from x bf16 [T][H].  topk_idx_out [T][k]
- * and topk_w_out [T][k] receive the routing when non-NULL. */
+/* The whole layer: y bf16 [T][H] from x bf16 [T][H], with the RMSNorm in
+ * front when w->norm_gamma is non-NULL (then norm_eps is checked as for
+ * moe_rmsnorm; x itself is not modified).  topk_idx_out [T][k] and
+ * topk_w_out [T][k] receive the routing when non-NULL. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     moe_layer_forward,
     moe_layer_forward_timed,
     moe_permute,
+    moe_rmsnorm,
     moe_route,
     moe_workspace_bytes,
     weights_from,

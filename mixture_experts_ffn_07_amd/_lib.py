@@ -27,13 +27,14 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 class MoeConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("score_func", ctypes.c_int32)]
+                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("score_func", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gu_q", ctypes.c_void_p),
                 ("gu_s", ctypes.c_void_p), ("dn_q", ctypes.c_void_p), ("dn_s", ctypes.c_void_p),
-                ("sh_gu", ctypes.c_void_p), ("sh_dn", ctypes.c_void_p)]
+                ("sh_gu", ctypes.c_void_p), ("sh_dn", ctypes.c_void_p), ("norm_gamma", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -58,6 +59,7 @@ def load() -> ctypes.CDLL:
     cfgp, wp = ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights)
     sig = {
         "moe_workspace_bytes": (sz, [cfgp, i64]),
+        "moe_rmsnorm": (ctypes.c_int, [cfgp, vp, vp, i64, vp, vp]),
         "moe_route": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "moe_permute": (ctypes.c_int, [cfgp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "moe_expert_ffn": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, vp, vp, vp, sz, vp]),
@@ -103,25 +105,28 @@ def _check(fn: str, status: int) -> None:
 
 
 def make_config(hidden, n_experts, top_k, inter, n_shared=1, shared_inter=None, route_scale=1.5,
-                swiglu_limit=10.0, score_func=0) -> MoeConfig:
+                swiglu_limit=10.0, score_func=0, norm_eps=1e-20) -> MoeConfig:
     return MoeConfig(hidden, n_experts, top_k, inter, n_shared, inter if shared_inter is None else shared_inter,
-                     route_scale, swiglu_limit, score_func)
+                     route_scale, swiglu_limit, score_func, norm_eps)
 
 
 def config_from(cfg) -> MoeConfig:
     """MoeConfig from any object with the layer-shape attributes (e.g. moe_synth.LayerConfig)."""
     return make_config(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.inter, cfg.n_shared,
-                       cfg.shared_inter if cfg.n_shared else 0, cfg.route_scale, cfg.swiglu_limit)
+                       cfg.shared_inter if cfg.n_shared else 0, cfg.route_scale, cfg.swiglu_limit,
+                       norm_eps=getattr(cfg, "norm_eps", 1e-20))
 
 
-def make_weights(router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu=None, sh_dn=None) -> MoeWeights:
+def make_weights(router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu=None, sh_dn=None,
+                 norm_gamma=None) -> MoeWeights:
     return MoeWeights(_ptr(router_w), _ptr(router_bias), _ptr(gu_q), _ptr(gu_s), _ptr(dn_q), _ptr(dn_s),
-                      _ptr(sh_gu), _ptr(sh_dn))
+                      _ptr(sh_gu), _ptr(sh_dn), _ptr(norm_gamma))
 
 
 def weights_from(inp) -> MoeWeights:
     """MoeWeights from an object with the weight tensors as attributes (e.g. moe_synth.LayerInputs)."""
-    return make_weights(inp.router_w, inp.router_bias, inp.gu_q, inp.gu_s, inp.dn_q, inp.dn_s, inp.sh_gu, inp.sh_dn)
+    return make_weights(inp.router_w, inp.router_bias, inp.gu_q, inp.gu_s, inp.dn_q, inp.dn_s, inp.sh_gu, inp.sh_dn,
+                        getattr(inp, "norm_gamma", None))
 
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)
@@ -135,6 +140,11 @@ def workspace(cfg: MoeConfig, tokens: int, device="cuda") -> torch.Tensor:
     if nbytes == 0:
         raise MoeError("moe_workspace_bytes", 1, load().moe_last_error().decode())
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_rmsnorm(cfg, gamma, x, tokens, x_norm, stream=None):
+    _check("moe_rmsnorm", load().moe_rmsnorm(ctypes.byref(cfg), _ptr(gamma), _ptr(x), tokens, _ptr(x_norm),
+                                             _stream(stream)))
 
 
 def moe_route(cfg, w, x, tokens, topk_idx, topk_w, tie_gap, ws, stream=None):

@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
-SOURCES = ["moe_ffn.cpp", "router.hip", "permute.hip", "expert_gemm.hip", "expert_gemv.hip", "decode.hip", "expert_valu.hip", "combine.hip"]
+SOURCES = ["moe_ffn.cpp", "router.hip", "permute.hip", "expert_gemm.hip", "expert_gemv.hip", "decode.hip", "expert_valu.hip", "combine.hip", "norm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: hipcc must not form packed fp32 VALU ops on its own.

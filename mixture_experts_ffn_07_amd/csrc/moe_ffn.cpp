@@ -111,6 +111,13 @@ moe_status check_routed_weights(const moe_config* c, const moe_weights* w, bool 
   return MOE_OK;
 }
 
+moe_status check_norm(const moe_config* c, const uint16_t* gamma) {
+  moe_status s;
+  if ((s = need(gamma, 16, "norm_gamma")) != MOE_OK) return s;
+  if (!std::isfinite(c->norm_eps) || !(c->norm_eps > 0.f)) return fail(MOE_ERR_INVALID_ARG, "norm_eps must be finite and > 0");
+  return MOE_OK;
+}
+
 // ---------------------------------------------------------------- workspace layout
 struct Region {
   size_t off = 0, bytes = 0;
@@ -130,7 +137,8 @@ struct WsLayout {
   bool valu_dn = false;       // decode, T <= 2: routed down + combine one wave per column on the vector ALUs
   bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
                               // down; routed down + combine
-  Region logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
+  bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
+  Region x_norm, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh;
   size_t total = 0;
 };
@@ -176,6 +184,7 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
               moe::decode_valu_supported((int)tokens, c->hidden, c->n_shared ? c->shared_inter : 0) &&
               (c->n_shared == 0 ||
                moe::gate_up_shared_down_supported((int)tokens, c->hidden, (int)L.max_tiles, c->shared_inter));
+    L.norm_in_router = L.stream4 && moe::router_norm_gemv_supported((int)tokens, c->hidden);
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
   const int64_t nchunks = moe::permute_chunks(n);
@@ -185,6 +194,7 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     r.bytes = bytes;
     off += (bytes + 255) & ~size_t(255);
   };
+  take(L.x_norm, sizeof(uint16_t) * (size_t)tokens * c->hidden);
   take(L.logits, sizeof(float) * (size_t)L.router.ksplit * tokens * E);
   take(L.scores, L.route_small ? sizeof(float) * 2 * (size_t)tokens * E : 0);
   take(L.xmx, L.route_small ? (size_t)tokens * moe::mx_row_bytes(c->hidden) : 0);
@@ -355,10 +365,14 @@ moe_status run_experts_decode(const moe_config* c, const moe_weights* w, const u
 }
 
 // Few-token layer, T <= 2, streaming form (see launch_decode_route_shared_gu).
+// With norm_gamma (and L.norm_in_router) the router launch normalises x and
+// writes the rows the later launches read.
 moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
                                  uint16_t* y, int32_t* idx, float* wts, void* ws, const WsLayout& L, hipStream_t st,
-                                 Timeline* tl) {
+                                 Timeline* tl, const uint16_t* norm_gamma) {
   const int E = c->n_experts;
+  const uint16_t* x_in = x;
+  if (norm_gamma) x = at<uint16_t>(ws, L.x_norm);
   uint16_t* y_sh = c->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;
   uint16_t* h_sh = c->n_shared ? at<uint16_t>(ws, L.h_sh) : nullptr;
   int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
@@ -393,9 +407,15 @@ moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, cons
   rp.tile_count = at<int32_t>(ws, L.tile_count);
   rp.tile_rows = at<int32_t>(ws, L.tile_rows);
   rp.max_tiles = (int)L.max_tiles;
-  hipError_t err =
-      moe::launch_router_gemv(x, w->router_w, nullptr, (int)T, E, c->hidden, f.scores, w->router_bias, st);
-  if (err == hipSuccess) err = mark(tl, "router_scores", st);
+  hipError_t err;
+  if (norm_gamma) {
+    err = moe::launch_router_norm_gemv(x_in, norm_gamma, (double)c->norm_eps, at<uint16_t>(ws, L.x_norm),
+                                       w->router_w, (int)T, E, c->hidden, f.scores, w->router_bias, st);
+    if (err == hipSuccess) err = mark(tl, "norm_router_scores", st);
+  } else {
+    err = moe::launch_router_gemv(x, w->router_w, nullptr, (int)T, E, c->hidden, f.scores, w->router_bias, st);
+    if (err == hipSuccess) err = mark(tl, "router_scores", st);
+  }
   if (err != hipSuccess) return fail_hip(err, "router launch");
   err = moe::launch_decode_route_shared_gu(f, rp, st);
   if (err == hipSuccess) err = mark(tl, "route_shared_gate_up", st);
@@ -714,6 +734,19 @@ size_t moe_workspace_bytes(const moe_config* cfg, int64_t tokens) {
   return plan_workspace(cfg, tokens).total;
 }
 
+moe_status moe_rmsnorm(const moe_config* cfg, const uint16_t* gamma, const uint16_t* x, int64_t tokens,
+                       uint16_t* x_norm, void* stream) {
+  moe_status s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_norm(cfg, gamma)) != MOE_OK) return s;
+  if ((s = need(x, 16, "x")) != MOE_OK || (s = need(x_norm, 16, "x_norm")) != MOE_OK) return s;
+  if (tokens == 0) return MOE_OK;
+  hipError_t err = moe::launch_rmsnorm_rows(x, gamma, x_norm, (int)tokens, cfg->hidden, (double)cfg->norm_eps,
+                                            static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail_hip(err, "rmsnorm launch");
+  return MOE_OK;
+}
+
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                      int32_t* topk_idx, float* topk_w, float* tie_gap, void* ws, size_t ws_bytes, void* stream) {
   moe_status s;
@@ -793,6 +826,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
   if ((s = check_routed_weights(cfg, w, true, true)) != MOE_OK) return s;
   if ((s = need(x, 16, "x")) != MOE_OK || (s = need(y, 16, "y")) != MOE_OK) return s;
+  if (w->norm_gamma && (s = check_norm(cfg, w->norm_gamma)) != MOE_OK) return s;
   if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_idx_out is not 4-byte aligned");
   if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_w_out is not 4-byte aligned");
   const WsLayout L = plan_workspace(cfg, tokens);
@@ -803,7 +837,16 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
-  if (L.stream4) return layer_forward_decode4(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
+  const uint16_t* gamma = w->norm_gamma;
+  if (gamma && L.norm_in_router) return layer_forward_decode4(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl, gamma);
+  if (gamma) {
+    uint16_t* xn = at<uint16_t>(ws, L.x_norm);
+    hipError_t err = moe::launch_rmsnorm_rows(x, gamma, xn, (int)tokens, cfg->hidden, (double)cfg->norm_eps, st);
+    if (err == hipSuccess) err = mark(tl, "rmsnorm", st);
+    if (err != hipSuccess) return fail_hip(err, "rmsnorm launch");
+    x = xn;
+  }
+  if (L.stream4) return layer_forward_decode4(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl, nullptr);
   if (L.decode) return layer_forward_decode(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
   if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
   if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;

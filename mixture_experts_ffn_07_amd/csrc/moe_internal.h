@@ -22,6 +22,15 @@ hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const
 // u = s + bias[e] at scores[T + t][e] (bias optional)
 hipError_t launch_router_gemv(const uint16_t* x, const float* router_w, float* logits, int tokens, int n_experts,
                               int hidden, float* scores, const float* bias, hipStream_t stream);
+// launch_router_gemv's scores (no logits) with the pre-FFN RMSNorm in front,
+// for 1 or 2 tokens and hidden <= 5120; the normalised rows go to x_norm [T][H]
+bool router_norm_gemv_supported(int tokens, int hidden);
+hipError_t launch_router_norm_gemv(const uint16_t* x, const uint16_t* gamma, double eps, uint16_t* x_norm,
+                                   const float* router_w, int tokens, int n_experts, int hidden, float* scores,
+                                   const float* bias, hipStream_t stream);
+// pre-FFN RMSNorm of T rows (x_norm may be x)
+hipError_t launch_rmsnorm_rows(const uint16_t* x, const uint16_t* gamma, uint16_t* x_norm, int rows, int hidden,
+                               double eps, hipStream_t stream);
 // sum of the partials, sqrtsoftplus, biased top-k, weights
 hipError_t launch_router_topk(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
                               int top_k, float route_scale, int32_t* idx, float* w, float* gap,

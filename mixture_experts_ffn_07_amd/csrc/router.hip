@@ -13,7 +13,9 @@
 // K-step give an fp32-accumulated dot product of the exact products.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "mx_device.h"
 #include "permute_device.h"
+#include "norm_device.h"
 #include "router_device.h"
 
 #include <math.h>
@@ -178,6 +180,130 @@ __global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restr
 hipError_t launch_router_gemv(const uint16_t* x, const float* router_w, float* logits, int tokens, int n_experts,
                               int hidden, float* scores, const float* bias, hipStream_t stream) {
   hipLaunchKernelGGL(router_gemv_kernel, dim3(n_experts), dim3(64), 0, stream, x, router_w, logits, tokens,
+                     n_experts, hidden, scores, bias);
+  return hipGetLastError();
+}
+
+// The router GEMV with the pre-FFN RMSNorm in front (T <= TM tokens, hidden
+// <= 256 * NX).  A block of four waves serves four experts.  Its 256 threads
+// first normalise the rows together (each a quarter of what one wave would
+// do): x and the gain are loaded before the router rows, so the waits for
+// them leave the rows' loads in flight and the normalisation runs under that
+// stream; the squares are summed per wave, the four wave sums added in a
+// fixed order, so every block derives the same scale and the same bits.  The
+// normalised rows go to LDS, where each wave reads them for its dot product
+// as router_gemv_wave does from x.  Block 0 also writes them to x_norm [T][H]
+// for the launches that follow.  Barriers are bare s_barrier after an LDS
+// wait: a workgroup fence would also wait for the router rows.
+template <int NX, int TM>
+__global__ __launch_bounds__(256) void router_norm_gemv_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ gamma, double eps,
+                                                               uint16_t* __restrict__ x_norm,
+                                                               const float* __restrict__ wr, int tokens,
+                                                               int n_experts, int hidden, float* __restrict__ scores,
+                                                               const float* __restrict__ bias) {
+  constexpr int NB = (NX + 3) / 4;  // 4-element vectors per thread in the block's share of a row
+  __shared__ __attribute__((aligned(16))) uint32_t xs[TM][128 * NX];  // bf16 pairs
+  __shared__ double part[TM][4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the row's buffer stays scalar
+  const int e = blockIdx.x * 4 + wv;
+  const int nv = hidden / 4;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)tokens * hidden * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, (uint32_t)hidden * 2);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(wr + (size_t)(e < n_experts ? e : 0) * hidden, e < n_experts ? (uint32_t)hidden * 4 : 0u);
+  uint32_t xv[TM][NB][2], gv[NB][2];
+#pragma unroll
+  for (int tt = 0; tt < TM; ++tt) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int v = 256 * i + tid;
+      const uint32_t off = v < nv && tt < tokens ? ((uint32_t)tt * hidden + 4u * v) * 2u : kOob;
+      const auto d = __builtin_amdgcn_raw_buffer_load_b64(rx, (int)off, 0, 0);
+      xv[tt][i][0] = d[0];
+      xv[tt][i][1] = d[1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int v = 256 * i + tid;
+    const auto d = __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(v < nv ? 8u * v : kOob), 0, 0);
+    gv[i][0] = d[0];
+    gv[i][1] = d[1];
+  }
+  f32x4_t w[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int v = 64 * i + lane;
+    w[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(v < nv ? 16u * v : kOob), 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+#pragma unroll
+  for (int tt = 0; tt < TM; ++tt) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc = add_squares4(xv[tt][i][0], xv[tt][i][1], acc);
+    acc = wave_sum_f64(acc);
+    if (lane == 0) part[tt][wv] = acc;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int tt = 0; tt < TM; ++tt) {
+    const double r = rms_recip(((part[tt][0] + part[tt][1]) + part[tt][2]) + part[tt][3], hidden, eps);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int v = 256 * i + tid;
+      if (v < nv) {
+        const uint32_t a = norm_pair(xv[tt][i][0], gv[i][0], r);
+        const uint32_t b = norm_pair(xv[tt][i][1], gv[i][1], r);
+        *reinterpret_cast<uint2*>(&xs[tt][2 * v]) = make_uint2(a, b);
+        if (x_norm && blockIdx.x == 0 && tt < tokens)
+          *reinterpret_cast<uint2*>(x_norm + (size_t)tt * hidden + 4 * v) = make_uint2(a, b);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (e >= n_experts) return;
+  float acc[TM];
+#pragma unroll
+  for (int tt = 0; tt < TM; ++tt) {
+    acc[tt] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int v = 64 * i + lane;
+      if (v < nv) {  // rows of x past hidden hold nothing; their weights read zero
+        const uint2 q = *reinterpret_cast<const uint2*>(&xs[tt][2 * v]);
+        acc[tt] = fmaf(__uint_as_float(q.x << 16), w[i][0], acc[tt]);
+        acc[tt] = fmaf(__uint_as_float(q.x & 0xffff0000u), w[i][1], acc[tt]);
+        acc[tt] = fmaf(__uint_as_float(q.y << 16), w[i][2], acc[tt]);
+        acc[tt] = fmaf(__uint_as_float(q.y & 0xffff0000u), w[i][3], acc[tt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TM; ++tt) {
+    const float v = wave_sum_f32(acc[tt]);
+    if (lane == 0 && tt < tokens) {
+      const float s = sqrtsoftplus(v);
+      scores[(size_t)tt * n_experts + e] = s;
+      scores[(size_t)(tokens + tt) * n_experts + e] = s + (bias ? bias[e] : 0.f);
+    }
+  }
+}
+
+bool router_norm_gemv_supported(int tokens, int hidden) {
+  return tokens >= 1 && tokens <= 2 && hidden <= 256 * 20;
+}
+
+hipError_t launch_router_norm_gemv(const uint16_t* x, const uint16_t* gamma, double eps, uint16_t* x_norm,
+                                   const float* router_w, int tokens, int n_experts, int hidden, float* scores,
+                                   const float* bias, hipStream_t stream) {
+  if (!router_norm_gemv_supported(tokens, hidden)) return hipErrorInvalidValue;
+  const bool two = tokens == 2;
+  auto kern = hidden <= 256 * 8 ? (two ? router_norm_gemv_kernel<8, 2> : router_norm_gemv_kernel<8, 1>)
+                                : (two ? router_norm_gemv_kernel<20, 2> : router_norm_gemv_kernel<20, 1>);
+  hipLaunchKernelGGL(kern, dim3((n_experts + 3) / 4), dim3(256), 0, stream, x, gamma, eps, x_norm, router_w, tokens,
                      n_experts, hidden, scores, bias);
   return hipGetLastError();
 }

@@ -33,6 +33,9 @@ class LayerConfig:
     cfg_id: int = 0
     x_std: float = 1.0
     expert_std: float = 0.02
+    #: pre-FFN RMSNorm in front of the layer (bf16 gain, eps norm_eps)
+    norm: bool = False
+    norm_eps: float = 1e-20
     extra: dict = field(default_factory=dict, compare=False)
 
     def with_(self, **kw) -> "LayerConfig":
@@ -58,6 +61,9 @@ CONFIGS = {
     "verify_t320_h5120_e384": LayerConfig("verify_t320_h5120_e384", 320, 5120, 384, 6, 2304, 1, 2304, cfg_id=7),
     # DeepSeek-V4-Pro MoE dimensions (hidden 7168, expert width 3072), one decode token
     "pro_t1_h7168_e384": LayerConfig("pro_t1_h7168_e384", 1, 7168, 384, 6, 3072, 1, 3072, cfg_id=8),
+    # the one-token decode layer with the pre-FFN RMSNorm in front (eps 1e-20)
+    "decode_t1_h5120_e384_norm": LayerConfig("decode_t1_h5120_e384_norm", 1, 5120, 384, 6, 2304, 1, 2304,
+                                             cfg_id=9, norm=True),
     # skewed routing on the drafter-style MoE, 16384 tokens
     "skew_t16384_h5120_e128": LayerConfig("skew_t16384_h5120_e128", 16384, 5120, 128, 3, 2304, 1, 2304,
                                           bias="zipf", cfg_id=5),

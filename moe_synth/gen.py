@@ -9,6 +9,9 @@ Distributions (one recipe for every workload):
 * shared expert weights: N(0, 0.02^2) rounded to bf16.
 * optional Zipf selection bias: b_e = alpha * r_e^-s with r a seeded random
   permutation of 1..E (rank 1 is the hottest expert).
+* with the pre-FFN norm on: x rows of very different sizes, the draw above
+  times 2^u per row with u uniform in [-4, 8) (a residual stream's rows are
+  not normalised), and a bf16 gain gamma ~ N(1, 0.1^2) per channel.
 
 Every tensor has its own seed, derived from (seed, config id, tensor id,
 expert, weight set) by numpy's ``SeedSequence`` hashing, so one expert can be
@@ -29,7 +32,7 @@ import torch
 
 from .configs import LayerConfig
 
-TENSOR_X, TENSOR_ROUTER, TENSOR_BIAS, TENSOR_GU, TENSOR_DN, TENSOR_SH_GU, TENSOR_SH_DN = range(7)
+TENSOR_X, TENSOR_ROUTER, TENSOR_BIAS, TENSOR_GU, TENSOR_DN, TENSOR_SH_GU, TENSOR_SH_DN, TENSOR_GAMMA = range(8)
 
 
 def derive_seed(*parts: int) -> int:
@@ -118,11 +121,13 @@ class LayerInputs:
     dn_s: torch.Tensor         # uint8 [E, H, I/32]
     sh_gu: Optional[torch.Tensor]  # int16 bf16 bits [2Is, H] or None
     sh_dn: Optional[torch.Tensor]  # int16 bf16 bits [H, Is] or None
+    norm_gamma: Optional[torch.Tensor] = None  # int16 bf16 bits [H] or None (no norm)
 
     def to(self, device) -> "LayerInputs":
         mv = lambda t: None if t is None else t.to(device)  # noqa: E731
         return LayerInputs(self.cfg, mv(self.x), mv(self.router_w), mv(self.router_bias), mv(self.gu_q),
-                           mv(self.gu_s), mv(self.dn_q), mv(self.dn_s), mv(self.sh_gu), mv(self.sh_dn))
+                           mv(self.gu_s), mv(self.dn_q), mv(self.dn_s), mv(self.sh_gu), mv(self.sh_dn),
+                           mv(self.norm_gamma))
 
     def oracle_args(self) -> dict:
         """Keyword arguments of the oracle's ``layer_forward`` (numpy on the host)."""
@@ -134,7 +139,9 @@ class LayerInputs:
                     sh_gu=None if self.sh_gu is None else npy(self.sh_gu).view(np.uint16),
                     sh_dn=None if self.sh_dn is None else npy(self.sh_dn).view(np.uint16),
                     top_k=self.cfg.top_k, route_scale=self.cfg.route_scale,
-                    swiglu_limit=self.cfg.swiglu_limit)
+                    swiglu_limit=self.cfg.swiglu_limit,
+                    norm_gamma=None if self.norm_gamma is None else npy(self.norm_gamma).view(np.uint16),
+                    norm_eps=self.cfg.norm_eps)
 
 
 def zipf_bias(cfg: LayerConfig, seed: int, weight_set: int = 0) -> torch.Tensor:
@@ -150,8 +157,12 @@ def make_router_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set
     """(x bits [T, H], W_r [E, H], bias [E] or None): the same tensors make_inputs draws."""
     dev = torch.device(device)
     xs = seed if x_seed is None else x_seed
-    x = f32_to_bf16_bits(_randn((cfg.tokens, cfg.hidden), derive_seed(xs, cfg.cfg_id, TENSOR_X, 0, 0), dev,
-                                cfg.x_std))
+    x = _randn((cfg.tokens, cfg.hidden), derive_seed(xs, cfg.cfg_id, TENSOR_X, 0, 0), dev, cfg.x_std)
+    if cfg.norm:
+        g = torch.Generator(device=dev)
+        g.manual_seed(derive_seed(xs, cfg.cfg_id, TENSOR_X, 1, 0))
+        x = x * torch.exp2(torch.randint(-4, 8, (cfg.tokens, 1), generator=g, device=dev).to(torch.float32))
+    x = f32_to_bf16_bits(x)
     router_w = _randn((cfg.n_experts, cfg.hidden), derive_seed(seed, cfg.cfg_id, TENSOR_ROUTER, 0, weight_set),
                       dev, 1.0 / math.sqrt(cfg.hidden))
     bias = zipf_bias(cfg, seed, weight_set).to(dev) if cfg.bias == "zipf" else None
@@ -186,4 +197,8 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set: int =
                                         dev, cfg.expert_std))
         sh_dn = f32_to_bf16_bits(_randn((h, i_s), derive_seed(seed, cfg.cfg_id, TENSOR_SH_DN, 0, weight_set),
                                         dev, cfg.expert_std))
-    return LayerInputs(cfg, x, router_w, bias, gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn)
+    gamma = None
+    if cfg.norm:
+        gamma = f32_to_bf16_bits(1.0 + _randn((h,), derive_seed(seed, cfg.cfg_id, TENSOR_GAMMA, 0, weight_set), dev,
+                                              0.1))
+    return LayerInputs(cfg, x, router_w, bias, gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn, gamma)

@@ -20,7 +20,7 @@ P = 0x10000  # aligned placeholder address (never dereferenced)
 def test_library_loads_and_exports_every_header_function():
     lib = moe.load()
     names = moe.header_functions()
-    assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+    assert set(names) == {"moe_workspace_bytes", "moe_rmsnorm", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
                           "moe_layer_forward", "moe_layer_forward_timed", "moe_status_str", "moe_last_error",
                           "moe_abi_version"}
     for n in names:
@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_header_function():
     dyn = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in dyn.splitlines() if " T " in line}
     assert set(names) <= exported
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -84,6 +84,7 @@ def test_bad_config_rejected_by_every_entry_point(mut, code):
     assert lib.moe_expert_ffn(r(c), r(w), P, 8, P, P, P, P, P, 1 << 40, None) == code
     assert lib.moe_combine(r(c), P, P, P, P, 8, P, None) == code
     assert lib.moe_layer_forward(r(c), r(w), P, 8, P, None, None, P, 1 << 40, None) == code
+    assert lib.moe_rmsnorm(r(c), P, P, 8, P, None) == code
     assert lib.moe_last_error()
 
 
@@ -177,3 +178,26 @@ def test_binding_raises_with_status_and_message():
         moe.moe_combine(c, None, None, None, None, 8, None)
     assert ei.value.status == INVALID
     assert "hidden" in str(ei.value)
+
+
+def test_norm_checks():
+    """moe_rmsnorm and the norm fields of moe_layer_forward are checked before anything is enqueued."""
+    lib = moe.load()
+    r, big = ctypes.byref, 1 << 40
+    c = _cfg()
+    assert lib.moe_rmsnorm(r(c), None, P, 8, P, None) == INVALID
+    assert lib.moe_rmsnorm(r(c), P + 2, P, 8, P, None) == ALIGN
+    assert lib.moe_rmsnorm(r(c), P, None, 8, P, None) == INVALID
+    assert lib.moe_rmsnorm(r(c), P, P + 8, 8, P, None) == ALIGN
+    assert lib.moe_rmsnorm(r(c), P, P, 8, None, None) == INVALID
+    assert lib.moe_rmsnorm(r(c), P, P, -1, P, None) == INVALID
+    assert lib.moe_rmsnorm(r(c), P, P, 0, P, None) == OK  # nothing to do, nothing enqueued
+    for eps in (0.0, -1e-20, float("inf"), float("nan")):
+        ce = _cfg(norm_eps=eps)
+        assert lib.moe_rmsnorm(r(ce), P, P, 8, P, None) == INVALID, eps
+        assert lib.moe_layer_forward(r(ce), r(_weights(norm_gamma=P)), P, 8, P, None, None, P, big, None) \
+            == INVALID, eps
+        # without a gain the eps is not read
+        assert lib.moe_layer_forward(r(ce), r(_weights()), P, 0, P, None, None, P, big, None) == OK, eps
+    assert lib.moe_layer_forward(r(c), r(_weights(norm_gamma=P + 2)), P, 8, P, None, None, P, big, None) == ALIGN
+    assert "norm" in lib.moe_last_error().decode()

@@ -346,3 +346,95 @@ def test_layer_many_tokens_small_dims():
     idx = gpu[1].cpu().numpy()
     assert idx.min() >= 0 and idx.max() < cfg.n_experts
     _check_layer(inp, tokens=_sample(cfg.tokens, 48, seed=2), gpu=gpu)
+
+
+# ------------------------------------------------------------------ pre-FFN RMSNorm
+
+def _norm_inputs(t, h, seed):
+    """bf16 rows of scales 2^-30..2^30 with special rows (zero, constant, one huge element over tiny ones whose
+    normalised values are bf16 subnormals), and a gain ~N(1, 0.1^2) with a few zeros and sign flips."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn((t, h), generator=g) * torch.exp2(torch.randint(-30, 31, (t, 1), generator=g).float())
+    if t > 1:
+        x[1] = 0.0
+    if t > 2:
+        x[2] = 0.375
+    if t > 3:
+        x[3] = torch.randn(h, generator=g) * 2.0 ** -116
+        x[3, 0] = 2.0 ** 20
+    gam = 1.0 + 0.1 * torch.randn(h, generator=g)
+    gam[:: 97] = 0.0
+    gam[5:: 131] *= -1.0
+    bits = lambda v: v.to(torch.bfloat16).view(torch.int16)  # noqa: E731
+    return bits(x).to(DEV), bits(gam).to(DEV)
+
+
+@pytest.mark.parametrize("t,h", [(1, 5120), (7, 5120), (3, 7168), (5, 32), (9, 8192), (4, 8224), (2, 65536),
+                                 (1000, 512), (4096, 5120)])
+def test_rmsnorm_bit_exact(t, h):
+    """moe_rmsnorm against the oracle bit for bit (single-pass rows up to 8192, two-pass beyond), in place too."""
+    x, gam = _norm_inputs(t, h, seed=t * 7 + h)
+    cfg = moe.make_config(h, 8, 2, 32)
+    out = torch.empty_like(x)
+    moe.moe_rmsnorm(cfg, gam, x, t, out)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x.cpu().numpy().view(np.uint16), gam.cpu().numpy().view(np.uint16), 1e-20)
+    got = out.cpu().numpy().view(np.uint16)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+    if t > 3:
+        sub = oracle.bf16_bits_to_f64(ref[3])
+        assert np.any((sub != 0) & (np.abs(sub) < 2.0 ** -126)), "row 3 should reach bf16 subnormals"
+    moe.moe_rmsnorm(cfg, gam, x, t, x)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(x, out)
+
+
+@pytest.mark.parametrize("tokens,variant", [(1, "tiny"), (2, "tiny"), (1, "min_dims"), (2, "ragged_k"),
+                                            (1, "no_shared"), (2, "v4pro_dims"), (5, "tiny"), (8, "tiny"),
+                                            (64, "tiny"), (300, "tiny"), (17, "ragged_k")])
+def test_layer_with_norm(tokens, variant):
+    """The layer with the pre-FFN norm: in the router launch for one or two tokens (hidden <= 5120), a norm
+    launch of its own otherwise; x itself is left as it was."""
+    base = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, norm=True)
+    cfg = {"tiny": base,
+           "min_dims": base.with_(hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2),
+           "ragged_k": base.with_(hidden=160, inter=96, shared_inter=224),
+           "no_shared": base.with_(n_shared=0, shared_inter=0),
+           "v4pro_dims": CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens, hidden=7168, inter=3072,
+                                                                 shared_inter=3072, n_experts=16, norm=True)}[variant]
+    inp = make_inputs(cfg, seed=40 + tokens, device=DEV)
+    x0 = inp.x.clone()
+    stats, _, alt = _check_layer(inp)
+    assert torch.equal(inp.x, x0)
+    print(f"norm T={tokens} {variant}:", stats, "near-tie alternatives", len(alt))
+
+
+def test_layer_with_norm_decode_t1_full():
+    """Full-size one-token layer with the norm: four launches, the norm inside the first."""
+    inp = make_inputs(CONFIGS["decode_t1_h5120_e384_norm"], seed=0, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print("decode_t1 norm:", stats, "near-tie alternatives", len(alt))
+    cfg = moe.config_from(inp.cfg)
+    y = torch.empty((1, inp.cfg.hidden), dtype=torch.int16, device=DEV)
+    names = [n for n, _ in moe.moe_layer_forward_timed(cfg, moe.weights_from(inp), inp.x, 1, y,
+                                                       moe.workspace(cfg, 1, device=DEV))]
+    assert names == ["norm_router_scores", "route_shared_gate_up", "routed_gate_up_shared_down",
+                     "routed_down_combine"]
+
+
+def test_layer_with_norm_prefill_sampled():
+    cfg = CONFIGS["prefill_t4096_h5120_e384"].with_(norm=True)
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    gpu = gpu_layer(inp)
+    stats, _, alt = _check_layer(inp, tokens=_sample(cfg.tokens, 6, seed=3), gpu=gpu)
+    print("prefill norm sampled:", stats, "near-tie alternatives", len(alt))
+
+
+def test_layer_with_norm_zero_input():
+    inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(norm=True), seed=8, device=DEV)
+    inp.x.zero_()
+    y, idx, _ = gpu_layer(inp)
+    assert torch.all(y == 0)
+    assert torch.all(idx.cpu() == torch.arange(6, dtype=torch.int32)[None, :])

@@ -536,9 +536,10 @@ def test_layer_with_norm_is_scale_invariant_and_normalises_first():
     h = inp.cfg.hidden
     gbits = torch.from_numpy(np.random.default_rng(5).normal(1, 0.1, h).astype(np.float32)) \
         .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    base = oracle.layer_forward(**a, norm_gamma=gbits, norm_eps=1e-20)
+    assert a["norm_gamma"] is None
+    base = oracle.layer_forward(**dict(a, norm_gamma=gbits, norm_eps=1e-20))
     a8 = dict(a, x_bits=oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(a["x_bits"]) * 8.0))
-    scaled = oracle.layer_forward(**a8, norm_gamma=gbits, norm_eps=1e-20)
+    scaled = oracle.layer_forward(**dict(a8, norm_gamma=gbits, norm_eps=1e-20))
     assert np.array_equal(base["y"], scaled["y"]) and np.array_equal(base["idx"], scaled["idx"])
     plain = oracle.layer_forward(**dict(a, x_bits=oracle.rmsnorm(a["x_bits"], gbits, 1e-20)))
     assert np.array_equal(base["y"], plain["y"])
