@@ -36,6 +36,8 @@ class LayerConfig:
     #: pre-FFN RMSNorm in front of the layer (bf16 gain, eps norm_eps)
     norm: bool = False
     norm_eps: float = 1e-20
+    #: routed expert weights: "mxfp4" (E2M1) or "mxfp8" (E4M3), E8M0 scale per 32
+    expert_format: str = "mxfp4"
     extra: dict = field(default_factory=dict, compare=False)
 
     def with_(self, **kw) -> "LayerConfig":
@@ -64,6 +66,11 @@ CONFIGS = {
     # the one-token decode layer with the pre-FFN RMSNorm in front (eps 1e-20)
     "decode_t1_h5120_e384_norm": LayerConfig("decode_t1_h5120_e384_norm", 1, 5120, 384, 6, 2304, 1, 2304,
                                              cfg_id=9, norm=True),
+    # MXFP8 (E4M3) routed experts: one decode token and the 4096-token prefill
+    "decode_t1_h5120_e384_fp8": LayerConfig("decode_t1_h5120_e384_fp8", 1, 5120, 384, 6, 2304, 1, 2304,
+                                            cfg_id=10, expert_format="mxfp8"),
+    "prefill_t4096_h5120_e384_fp8": LayerConfig("prefill_t4096_h5120_e384_fp8", 4096, 5120, 384, 6, 2304, 1,
+                                                2304, cfg_id=11, expert_format="mxfp8"),
     # skewed routing on the drafter-style MoE, 16384 tokens
     "skew_t16384_h5120_e128": LayerConfig("skew_t16384_h5120_e128", 16384, 5120, 128, 3, 2304, 1, 2304,
                                           bias="zipf", cfg_id=5),

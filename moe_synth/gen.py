@@ -5,7 +5,8 @@ Distributions (one recipe for every workload):
 * x: N(0, 1) per element, rounded to bf16 (round to nearest even).
 * router weight W_r [E, H]: fp32 N(0, 1/H), so that a logit is ~N(0, 1).
 * routed expert weights: fp32 N(0, 0.02^2), gate/up [2I, H] and down [H, I]
-  per expert, encoded to MXFP4 by :func:`mxfp4_encode`.
+  per expert, encoded to MXFP4 by :func:`mxfp4_encode` (or to MXFP8 by
+  :func:`mxfp8_encode` when the workload's expert format is "mxfp8").
 * shared expert weights: N(0, 0.02^2) rounded to bf16.
 * optional Zipf selection bias: b_e = alpha * r_e^-s with r a seeded random
   permutation of 1..E (rank 1 is the hottest expert).
@@ -95,6 +96,28 @@ def mxfp4_encode(w: torch.Tensor):
     return pack_nibbles(codes), code.to(torch.uint8)
 
 
+def mxfp8_encode(w: torch.Tensor):
+    """Encode fp32 rows [R, K] (K % 32 == 0) to MXFP8 with E4M3 elements (OCP rule).
+
+    Per block of 32: shared exponent floor(log2(amax)) - 8 (8 = emax of E4M3),
+    biased by 127 and clamped to [0, 254], 127 for an all-zero block;
+    elements divided by the block scale, held within +-448 and rounded to
+    nearest even by torch's float8_e4m3fn cast.  Returns (codes uint8 [R, K],
+    scales uint8 [R, K/32]).
+    """
+    rows, k = w.shape
+    assert k % 32 == 0
+    blocks = w.reshape(rows, k // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, exp = torch.frexp(amax)
+    code = (exp.to(torch.int32) - 1 - 8 + 127).clamp(0, 254)
+    code = torch.where(amax == 0, torch.full_like(code, 127), code)
+    scale = torch.ldexp(torch.ones_like(amax), (code - 127).to(torch.float32))
+    scaled = (blocks / scale.unsqueeze(-1)).clamp(-448.0, 448.0)
+    codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows, k)
+    return codes, code.to(torch.uint8)
+
+
 class ExpertTensor:
     """Per-expert read access ``t[e]`` to a device tensor [E, ...] as numpy arrays."""
 
@@ -115,9 +138,9 @@ class LayerInputs:
     x: torch.Tensor            # int16 bf16 bits [T, H]
     router_w: torch.Tensor     # float32 [E, H]
     router_bias: Optional[torch.Tensor]  # float32 [E] or None
-    gu_q: torch.Tensor         # uint8 [E, 2I, H/2]
+    gu_q: torch.Tensor         # uint8 [E, 2I, H/2] (MXFP8: [E, 2I, H])
     gu_s: torch.Tensor         # uint8 [E, 2I, H/32]
-    dn_q: torch.Tensor         # uint8 [E, H, I/2]
+    dn_q: torch.Tensor         # uint8 [E, H, I/2] (MXFP8: [E, H, I])
     dn_s: torch.Tensor         # uint8 [E, H, I/32]
     sh_gu: Optional[torch.Tensor]  # int16 bf16 bits [2Is, H] or None
     sh_dn: Optional[torch.Tensor]  # int16 bf16 bits [H, Is] or None
@@ -141,7 +164,7 @@ class LayerInputs:
                     top_k=self.cfg.top_k, route_scale=self.cfg.route_scale,
                     swiglu_limit=self.cfg.swiglu_limit,
                     norm_gamma=None if self.norm_gamma is None else npy(self.norm_gamma).view(np.uint16),
-                    norm_eps=self.cfg.norm_eps)
+                    norm_eps=self.cfg.norm_eps, expert_format=self.cfg.expert_format)
 
 
 def zipf_bias(cfg: LayerConfig, seed: int, weight_set: int = 0) -> torch.Tensor:
@@ -180,15 +203,17 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", weight_set: int =
     dev = torch.device(device)
     t, h, e, inter = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.inter
     x, router_w, bias = make_router_inputs(cfg, seed, device, weight_set, x_seed)
-    gu_q = torch.empty((e, 2 * inter, h // 2), dtype=torch.uint8, device=dev)
+    per_byte = {"mxfp4": 2, "mxfp8": 1}[cfg.expert_format]
+    encode = mxfp4_encode if cfg.expert_format == "mxfp4" else mxfp8_encode
+    gu_q = torch.empty((e, 2 * inter, h // per_byte), dtype=torch.uint8, device=dev)
     gu_s = torch.empty((e, 2 * inter, h // 32), dtype=torch.uint8, device=dev)
-    dn_q = torch.empty((e, h, inter // 2), dtype=torch.uint8, device=dev)
+    dn_q = torch.empty((e, h, inter // per_byte), dtype=torch.uint8, device=dev)
     dn_s = torch.empty((e, h, inter // 32), dtype=torch.uint8, device=dev)
     for ex in range(e):
         w = _randn((2 * inter, h), derive_seed(seed, cfg.cfg_id, TENSOR_GU, ex, weight_set), dev, cfg.expert_std)
-        gu_q[ex], gu_s[ex] = mxfp4_encode(w)
+        gu_q[ex], gu_s[ex] = encode(w)
         w = _randn((h, inter), derive_seed(seed, cfg.cfg_id, TENSOR_DN, ex, weight_set), dev, cfg.expert_std)
-        dn_q[ex], dn_s[ex] = mxfp4_encode(w)
+        dn_q[ex], dn_s[ex] = encode(w)
         del w
     sh_gu = sh_dn = None
     if cfg.n_shared:

@@ -20,6 +20,12 @@ from .moe_oracle import (  # noqa: F401
     e8m0_value,
     decode_mxfp4,
     mxfp4_packed_bytes,
+    E4M3_CODE_BITS,
+    e4m3_value,
+    e4m3_table,
+    decode_mxfp8,
+    mxfp8_bytes,
+    EXPERT_FORMATS,
     softplus,
     sqrtsoftplus,
     silu,

@@ -51,6 +51,14 @@ notes of the repository):
   norm type as not disclosed.  Reading: RMSNorm over the hidden dimension,
   x_n = x / sqrt(mean(x^2) + eps) * gamma with a bf16 gain gamma, its output
   rounded to bf16 (nearest, ties to even) before the router and the experts.
+* Optional second expert-weight codec, MXFP8: the API reference lists
+  ``float8_e4m3fn`` among ``SUPPORTED_ENCODINGS`` (and as ``DEFAULT_ENCODING``)
+  and the checkpoint's dense ``dtype`` is ``"fp8"``.  Reading: E4M3 codes of
+  the OCP "fn" kind (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+  infinities; S.1111.111 is NaN; largest value 448), one byte per element in
+  row order, with the same E8M0 scale per 32 consecutive elements of a row as
+  the MXFP4 weights (the block the "DeepSeek-V4-Pro" record gives for its
+  e4m3 values).
 """
 
 from __future__ import annotations
@@ -144,6 +152,54 @@ def decode_mxfp4(packed, scales, k: int) -> np.ndarray:
     values = e2m1_table()[codes]
     block_scale = np.repeat(e8m0_value(scales), 32, axis=-1)
     return values * block_scale
+
+
+#: Field widths of E4M3 (OCP 8-bit floating point, E4M3 "fn": no infinities,
+#: exponent and mantissa all ones is NaN): 1 sign, 4 exponent bits (bias 7),
+#: 3 mantissa bits.
+E4M3_CODE_BITS = {"sign": 7, "exponent": (6, 3), "mantissa": (2, 0), "bias": 7}
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one 8-bit E4M3 code from its fields: exponent field 0 is
+    subnormal, (-1)^s * 2^(1-7) * (m / 8); otherwise (-1)^s * 2^(e-7) * (1 + m / 8);
+    e = 15 with m = 7 is NaN."""
+    code = int(code) & 0xFF
+    s = code >> 7
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = 2.0 ** -6 * (m / 8.0) if e == 0 else 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return -mag if s else mag
+
+
+def e4m3_table() -> np.ndarray:
+    """The 256 E4M3 values indexed by code (code 0x80 is -0.0; 0x7F and 0xFF are NaN)."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_mxfp8(codes, scales, k: int) -> np.ndarray:
+    """Decode MXFP8 rows to float64.
+
+    ``codes``: uint8 [..., k], one E4M3 code per element.  ``scales``: uint8
+    [..., k/32], one E8M0 byte per 32 consecutive elements.  Element
+    i = E4M3(code_i) * 2^(scale_{i // 32} - 127).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    assert codes.shape[-1] == k and scales.shape[-1] * 32 == k
+    return e4m3_table()[codes] * np.repeat(e8m0_value(scales), 32, axis=-1)
+
+
+def mxfp8_bytes(rows: int, k: int) -> int:
+    """Bytes of an MXFP8 matrix [rows, k]: k code bytes + k/32 scale bytes a row."""
+    assert k % 32 == 0
+    return rows * (k + k // 32)
+
+
+#: expert-weight codecs: name -> (decoder, elements per code byte)
+EXPERT_FORMATS = {"mxfp4": (decode_mxfp4, 2), "mxfp8": (decode_mxfp8, 1)}
 
 
 def mxfp4_packed_bytes(rows: int, k: int) -> int:
@@ -316,10 +372,11 @@ def shared_expert(x_bits, sh_gu_bits, sh_dn_bits, limit: float):
     return expert_mlp(x, bf16_bits_to_f64(sh_gu_bits), bf16_bits_to_f64(sh_dn_bits), limit)
 
 
-def routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e: int, hidden: int, inter: int):
+def routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e: int, hidden: int, inter: int, expert_format: str = "mxfp4"):
     """Decoded float64 gate/up [2I, H] and down [H, I] matrices of routed expert e."""
-    w_gu = decode_mxfp4(np.asarray(gu_q[e]), np.asarray(gu_s[e]), hidden)
-    w_dn = decode_mxfp4(np.asarray(dn_q[e]), np.asarray(dn_s[e]), inter)
+    decode = EXPERT_FORMATS[expert_format][0]
+    w_gu = decode(np.asarray(gu_q[e]), np.asarray(gu_s[e]), hidden)
+    w_dn = decode(np.asarray(dn_q[e]), np.asarray(dn_s[e]), inter)
     return w_gu, w_dn
 
 
@@ -337,7 +394,8 @@ def combine(y_slot, slot_pos, w, y_shared, top_k: int) -> np.ndarray:
 
 def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn,
                   top_k: int, route_scale: float, swiglu_limit: float,
-                  tokens=None, selections=None, norm_gamma=None, norm_eps: float = 1e-20) -> dict:
+                  tokens=None, selections=None, norm_gamma=None, norm_eps: float = 1e-20,
+                  expert_format: str = "mxfp4") -> dict:
     """The whole layer for the rows ``tokens`` of ``x_bits`` (all rows if None).
 
     ``gu_q`` ... ``dn_s`` only need to support ``[e]`` (per-expert arrays of
@@ -346,7 +404,8 @@ def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, 
     row by one of the oracle's own ``valid_selections``.
 
     With ``norm_gamma`` (bf16 bits [H]) the rows are first RMS-normalised
-    (``rmsnorm``) and the layer runs on the result.
+    (``rmsnorm``) and the layer runs on the result.  ``expert_format`` names
+    the routed experts' codec, "mxfp4" or "mxfp8".
 
     Returns the router outputs, the permutation, ``h_slot`` [T*k, I] and
     ``y_slot`` [T*k, H] in position order, ``y_shared`` [T, H] and ``y`` [T, H].
@@ -372,7 +431,9 @@ def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, 
         lo, hi = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
         if hi == lo:
             continue
-        w_gu, w_dn = routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e, hidden, np.asarray(dn_q[e]).shape[1] * 2)
+        per_byte = EXPERT_FORMATS[expert_format][1]
+        w_gu, w_dn = routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e, hidden, np.asarray(dn_q[e]).shape[1] * per_byte,
+                                           expert_format)
         if inter is None:
             inter = w_dn.shape[1]
             h_slot = np.zeros((t_count * top_k, inter))

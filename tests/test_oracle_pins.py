@@ -545,3 +545,93 @@ def test_layer_with_norm_is_scale_invariant_and_normalises_first():
     assert np.array_equal(base["y"], plain["y"])
     raw = oracle.layer_forward(**a)
     assert not np.array_equal(base["y"], raw["y"])
+
+
+# ---------------------------------------------------------------- MXFP8 (E4M3) expert weights
+
+def test_e4m3_table_textbook_values_and_torch():
+    """E4M3 "fn": textbook codes, and every code against torch's float8_e4m3fn conversion."""
+    t = oracle.e4m3_table()
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and math.copysign(1, t[0x80]) < 0
+    assert t[0x38] == 1.0 and t[0x40] == 2.0 and t[0xC0] == -2.0 and t[0x3C] == 1.5
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0          # largest normal, no infinities
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.count_nonzero(np.isnan(t)) == 2
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(t), np.isnan(ref))
+    ok = ~np.isnan(t)
+    assert np.array_equal(t[ok], ref[ok])
+
+
+def test_decode_mxfp8_brute_force():
+    g = np.random.default_rng(21)
+    codes = g.integers(0, 256, (3, 96)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    scales = g.integers(100, 150, (3, 3)).astype(np.uint8)
+    got = oracle.decode_mxfp8(codes, scales, 96)
+    for r in range(3):
+        for i in range(96):
+            assert got[r, i] == oracle.e4m3_value(codes[r, i]) * 2.0 ** (int(scales[r, i // 32]) - 127)
+
+
+def test_mxfp8_encoder_nearest_and_block_scale():
+    """The generator's MXFP8 encoder: block exponent floor(log2 amax) - 8, each code the nearest E4M3
+    multiple of the block scale (ties to even), zero blocks scaled by 2^0."""
+    from moe_synth import mxfp8_encode
+    g = torch.Generator().manual_seed(5)
+    w = torch.randn((8, 256), generator=g) * torch.exp2(torch.randint(-12, 4, (8, 1), generator=g).float())
+    w[0, :32] = 0.0
+    codes, scales = mxfp8_encode(w)
+    c, s = codes.numpy(), scales.numpy()
+    assert s[0, 0] == 127 and np.all(c[0, :32] % 128 == 0)
+    table = oracle.e4m3_table()
+    finite = np.where(np.isnan(table), np.inf, table)
+    dec = oracle.decode_mxfp8(c, s, 256)
+    wd = w.double().numpy()
+    for r in range(8):
+        for b in range(8):
+            blk = wd[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            assert int(s[r, b]) - 127 == math.floor(math.log2(amax)) - 8
+            sc = 2.0 ** (int(s[r, b]) - 127)
+            for i in range(32):
+                v = min(max(blk[i] / sc, -448.0), 448.0)
+                best = np.min(np.abs(finite - v))
+                assert abs(dec[r, 32 * b + i] / sc - v) == best
+
+
+def test_mxfp8_and_mxfp4_layers_agree_on_shared_values():
+    """Weights whose values are exact in both codecs (E2M1 values times a power of two per block) give the
+    same layer output through the MXFP8 and the MXFP4 decoders."""
+    from moe_synth import mxfp4_encode, mxfp8_encode
+    inp = _tiny_inputs()
+    cfg = inp.cfg
+    g = torch.Generator().manual_seed(6)
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+    def exact(rows, k):
+        v = e2m1[torch.randint(0, 8, (rows, k), generator=g)] * torch.where(
+            torch.rand((rows, k), generator=g) < 0.5, -1.0, 1.0)
+        v[:, ::32] = 6.0  # every block reaches 6: the MXFP4 block exponent is exact
+        return v * torch.exp2(torch.randint(-9, -5, (rows, k // 32), generator=g).float()).repeat_interleave(32, 1)
+
+    gu = [exact(2 * cfg.inter, cfg.hidden) for _ in range(cfg.n_experts)]
+    dn = [exact(cfg.hidden, cfg.inter) for _ in range(cfg.n_experts)]
+    a = inp.oracle_args()
+    enc4 = [mxfp4_encode(m) for m in gu], [mxfp4_encode(m) for m in dn]
+    enc8 = [mxfp8_encode(m) for m in gu], [mxfp8_encode(m) for m in dn]
+    a4 = dict(a, gu_q=[q.numpy() for q, _ in enc4[0]], gu_s=[s.numpy() for _, s in enc4[0]],
+              dn_q=[q.numpy() for q, _ in enc4[1]], dn_s=[s.numpy() for _, s in enc4[1]])
+    a8 = dict(a, gu_q=[q.numpy() for q, _ in enc8[0]], gu_s=[s.numpy() for _, s in enc8[0]],
+              dn_q=[q.numpy() for q, _ in enc8[1]], dn_s=[s.numpy() for _, s in enc8[1]], expert_format="mxfp8")
+    w4 = oracle.routed_expert_weights(a4["gu_q"], a4["gu_s"], a4["dn_q"], a4["dn_s"], 3, cfg.hidden, cfg.inter)
+    w8 = oracle.routed_expert_weights(a8["gu_q"], a8["gu_s"], a8["dn_q"], a8["dn_s"], 3, cfg.hidden, cfg.inter,
+                                      "mxfp8")
+    assert np.array_equal(w4[0], gu[3].double().numpy()) and np.array_equal(w8[0], w4[0])
+    assert np.array_equal(w8[1], w4[1])
+    y4 = oracle.layer_forward(**a4)["y"]
+    y8 = oracle.layer_forward(**a8)["y"]
+    assert np.array_equal(y4, y8) and np.any(y4 != 0)
