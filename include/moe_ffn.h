@@ -40,8 +40,11 @@
  *   its 16-bit pattern (uint16_t).  MXFP4 matrices [R][K] are two arrays:
  *   codes uint8 [R][K/2], E2M1 element 2i in the low nibble of byte i and
  *   element 2i+1 in the high nibble; scales uint8 [R][K/32], an E8M0 byte
- *   (value 2^(s-127)) for each 32 consecutive elements of a row.  Expert e of
- *   a stacked tensor starts at e * (rows * row_bytes).
+ *   (value 2^(s-127)) for each 32 consecutive elements of a row.  MXFP8
+ *   matrices (expert_format 1) are the same with one E4M3 code per byte:
+ *   codes uint8 [R][K], E4M3 "fn" (bias 7, no infinities, 0x7F/0xFF NaN;
+ *   float8_e4m3fn in the MAX API's SUPPORTED_ENCODINGS).  Expert e of a
+ *   stacked tensor starts at e * (rows * row_bytes).
  *
  *   Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
  *   stream.  Work is enqueued asynchronously; results are valid once the
@@ -53,7 +56,7 @@
  *   required pointers; 16-byte alignment of tensor pointers (4-byte for the
  *   int32/fp32 per-token arrays; 256-byte for ws); H, I and I_s positive
  *   multiples of 32, at most 65536; 1 <= E <= 1024; 1 <= k <= min(E, 16);
- *   n_shared in {0, 1}; score_func == 0; route_scale finite;
+ *   n_shared in {0, 1}; score_func == 0; expert_format in {0, 1}; route_scale finite;
  *   swiglu_limit > 0 (may be +inf); 0 <= tokens <= 2^22; ws_bytes large
  *   enough.  tokens == 0 returns MOE_OK and enqueues nothing.  A failed
  *   kernel launch returns MOE_ERR_HIP.  Data are not checked: NaN/Inf
@@ -99,15 +102,17 @@ typedef struct moe_config {
   int32_t score_func;    /* 0 = sqrtsoftplus (the only one) */
   float norm_eps;        /* eps of the pre-FFN RMSNorm, 1e-20; read only when a norm gain is given,
                             then finite and > 0 */
+  int32_t expert_format; /* routed expert weights: 0 = MXFP4 (E2M1 codes, two a byte),
+                            1 = MXFP8 (E4M3 "fn" codes, one a byte); E8M0 scale per 32 either way */
 } moe_config;
 
 /* Weights: device pointers, layouts as in the header comment. */
 typedef struct moe_weights {
   const float* router_w;     /* [E][H] fp32                                      */
   const float* router_bias;  /* [E] fp32 selection bias, or NULL for none         */
-  const uint8_t* gu_q;       /* [E][2I][H/2]  MXFP4 codes; rows 0..I-1 gate,     */
+  const uint8_t* gu_q;       /* [E][2I][H/2]  MXFP4 codes ([E][2I][H] MXFP8); rows 0..I-1 gate, */
   const uint8_t* gu_s;       /* [E][2I][H/32] E8M0 scales; rows I..2I-1 up        */
-  const uint8_t* dn_q;       /* [E][H][I/2]   MXFP4 codes of the down projection */
+  const uint8_t* dn_q;       /* [E][H][I/2]   MXFP4 codes ([E][H][I] MXFP8) of the down projection */
   const uint8_t* dn_s;       /* [E][H][I/32]  E8M0 scales                         */
   const uint16_t* sh_gu;     /* [2I_s][H] bf16, gate rows then up rows; NULL iff n_shared == 0 */
   const uint16_t* sh_dn;     /* [H][I_s] bf16; NULL iff n_shared == 0             */

@@ -28,7 +28,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("score_func", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("expert_format", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -105,16 +105,19 @@ def _check(fn: str, status: int) -> None:
 
 
 def make_config(hidden, n_experts, top_k, inter, n_shared=1, shared_inter=None, route_scale=1.5,
-                swiglu_limit=10.0, score_func=0, norm_eps=1e-20) -> MoeConfig:
+                swiglu_limit=10.0, score_func=0, norm_eps=1e-20, expert_format=0) -> MoeConfig:
+    """expert_format: 0 or "mxfp4" (E2M1), 1 or "mxfp8" (E4M3)."""
+    fmt = {"mxfp4": 0, "mxfp8": 1}.get(expert_format, expert_format)
     return MoeConfig(hidden, n_experts, top_k, inter, n_shared, inter if shared_inter is None else shared_inter,
-                     route_scale, swiglu_limit, score_func, norm_eps)
+                     route_scale, swiglu_limit, score_func, norm_eps, fmt)
 
 
 def config_from(cfg) -> MoeConfig:
     """MoeConfig from any object with the layer-shape attributes (e.g. moe_synth.LayerConfig)."""
     return make_config(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.inter, cfg.n_shared,
                        cfg.shared_inter if cfg.n_shared else 0, cfg.route_scale, cfg.swiglu_limit,
-                       norm_eps=getattr(cfg, "norm_eps", 1e-20))
+                       norm_eps=getattr(cfg, "norm_eps", 1e-20),
+                       expert_format=getattr(cfg, "expert_format", "mxfp4"))
 
 
 def make_weights(router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu=None, sh_dn=None,

@@ -2,7 +2,9 @@
 //
 // One kernel template serves the routed experts (MXFP4 weights: E2M1 codes
 // with an E8M0 scale per 32 elements, Strata DEEPSEEK41 notes: "the experts
-// as MXFP4") and the shared expert (bf16 weights), both projections:
+// as MXFP4"; or MXFP8: E4M3 codes, float8_e4m3fn in the MAX API's
+// SUPPORTED_ENCODINGS, same scales) and the shared expert (bf16 weights),
+// both projections:
 //   gate/up: h = silu(min(x W_g^T, L)) * clamp(x W_u^T, -L, L)   (swiglu_limit,
 //            DeepseekV41Config), gate rows 0..I-1 and up rows I..2I-1 of the
 //            [2I][H] weight; one block computes matching gate and up columns
@@ -16,17 +18,20 @@
 // and multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
 // K layout within a 128-wide chunk: lane group g = lane/16 owns K offsets
-// [32g, 32g+32), exactly one E8M0 block, read as one 16-byte load of codes
-// (or 64 bytes of bf16); MFMA step s uses its elements 8s..8s+7 for both
-// operands, which permutes K identically on A and B.
+// [32g, 32g+32), exactly one E8M0 block, read as one 16-byte load of MXFP4
+// codes (32 bytes of MXFP8 codes, 64 bytes of bf16); MFMA step s uses its
+// elements 8s..8s+7 for both operands, which permutes K identically on A and
+// B.  MXFP8 codes are expanded with one v_cvt_scalef32_pk_bf16_fp8 per 2.
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "mx_device.h"
 
 namespace moe {
 
-template <int MT, bool SWIGLU, bool FP4>
+template <int MT, bool SWIGLU, int BF>  // BF: WeightFormat of B
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
+  constexpr bool FP4 = BF == kWMxfp4, FP8 = BF == kWMxfp8, MX = FP4 || FP8;
+  constexpr int NQ = FP8 ? 2 : 1;  // 16-byte code loads per lane and block
   constexpr int NB = SWIGLU ? 2 : 1;
   constexpr int U = 2;  // chunks loaded ahead per wave per batch
   __shared__ f32x4_t red[3][MT][NB][64];
@@ -66,8 +71,8 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int64_t brow = (int64_t)e * p.b_expert_rows + n0 + col + nb * p.b_row_second;
-    if (FP4) {
-      qrow[nb] = p.bq + brow * (K / 2);
+    if (MX) {
+      qrow[nb] = p.bq + brow * (FP4 ? K / 2 : K);
       srow[nb] = p.bs + brow * (K / 32);
     } else {
       hrow[nb] = p.bh + brow * K;
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
   const int nchunks = (K + 127) / 128;
   for (int c0 = wave; c0 < nchunks; c0 += 4 * U) {
     // ---- loads for U chunks
-    u32x4_t q[U][NB];
+    u32x4_t q[U][NB][NQ];
     uint32_t sc[U][NB];
     bf16x8_t bh[U][NB][4];
     bf16x8_t a[U][MT][4];
@@ -94,14 +99,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
       const bool kok = c < nchunks && k0 < K;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if (FP4) {
-          if (kok) {
-            q[u][nb] = *reinterpret_cast<const u32x4_t*>(qrow[nb] + k0 / 2);
-            sc[u][nb] = srow[nb][k0 / 32];
-          } else {
-            q[u][nb] = u32x4_t{0u, 0u, 0u, 0u};
-            sc[u][nb] = 127u;
-          }
+        if (MX) {
+#pragma unroll
+          for (int j = 0; j < NQ; ++j)
+            q[u][nb][j] = kok ? reinterpret_cast<const u32x4_t*>(qrow[nb] + (FP4 ? k0 / 2 : k0))[j]
+                              : u32x4_t{0u, 0u, 0u, 0u};
+          sc[u][nb] = kok ? (uint32_t)srow[nb][k0 / 32] : 127u;
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s)
@@ -124,7 +127,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
         if (FP4) {
           const float scale = e8m0_scale_operand(sc[u][nb]);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) b[s] = dequant_fp4x8(q[u][nb][s], scale);
+          for (int s = 0; s < 4; ++s) b[s] = dequant_fp4x8(q[u][nb][0][s], scale);
+        } else if (FP8) {
+          const float scale = e8m0_scale_operand(sc[u][nb]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            b[s] = dequant_fp8x8(q[u][nb][s >> 1][2 * (s & 1)], q[u][nb][s >> 1][2 * (s & 1) + 1], scale);
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s) b[s] = bh[u][nb][s];
@@ -842,7 +850,9 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   }
 }
 
-int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4, bool k_pipelined) {
+int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined) {
+  if (fmt == kWMxfp8) return 1;  // MXFP8 weights: the 16-row kernel
+  const bool fp4 = fmt == kWMxfp4;
   const int kTiledRows = 16 * (fp4 ? tiled_m<true>() : tiled_m<false>());
   // MXFP4 weights with every K a multiple of 128: the pipelined kernel at any
   // row count (it streams each expert's weights once per tile and measured
@@ -857,9 +867,10 @@ int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4, bool k_pipelined) {
 
 constexpr bool kPipe8 = true;  // the 8-wave form of the pipelined kernel
 
-template <bool SWIGLU, bool FP4>
+template <bool SWIGLU, int BF>
 static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream) {
-  if (mt == tiled_m<FP4>()) {
+  constexpr bool FP4 = BF == kWMxfp4;
+  if (BF != kWMxfp8 && mt == tiled_m<FP4>()) {
     // 128- or 64-row tiles: the LDS-tiled kernel, 4 waves x tiled_cols_per_wave columns per block
     const int cols = 4 * tiled_cols_per_wave<SWIGLU>();
     const dim3 g(grid.x, (unsigned)((p.N + cols - 1) / cols));
@@ -876,21 +887,18 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     }
     hipLaunchKernelGGL((expert_gemm_tiled_kernel<SWIGLU, FP4>), g, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, FP4>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
   }
 }
 
-hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, bool fp4, int mt, int64_t grid_tiles,
+hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt, int mt, int64_t grid_tiles,
                               hipStream_t stream) {
   dim3 grid((unsigned)grid_tiles, (unsigned)(p.N / 16));
-  if (swiglu && fp4)
-    launch_t<true, true>(p, mt, grid, stream);
-  else if (swiglu)
-    launch_t<true, false>(p, mt, grid, stream);
-  else if (fp4)
-    launch_t<false, true>(p, mt, grid, stream);
-  else
-    launch_t<false, false>(p, mt, grid, stream);
+  switch (fmt) {
+    case kWMxfp4: swiglu ? launch_t<true, kWMxfp4>(p, mt, grid, stream) : launch_t<false, kWMxfp4>(p, mt, grid, stream); break;
+    case kWMxfp8: swiglu ? launch_t<true, kWMxfp8>(p, mt, grid, stream) : launch_t<false, kWMxfp8>(p, mt, grid, stream); break;
+    default: swiglu ? launch_t<true, kWBf16>(p, mt, grid, stream) : launch_t<false, kWBf16>(p, mt, grid, stream); break;
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,19 @@ __device__ __forceinline__ bf16x8_t dequant_fp4x8(uint32_t w, float scale) {
   return r;
 }
 
+// Eight E4M3 codes (byte i = element i of lo, then of hi) to eight bf16
+// values times the block scale: one gfx950 v_cvt_scalef32_pk_bf16_fp8 per
+// two codes.  Exact whenever the scaled value is inside bf16's range (an E4M3
+// value has 4 significant bits).
+__device__ __forceinline__ bf16x8_t dequant_fp8x8(uint32_t lo, uint32_t hi, float scale) {
+  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+  bf16x8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
 // D = A(16x32) * B(32x16) + C with fp32 accumulation.  Lane l supplies
 // A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16] and holds
 // C[4*(l/16) + i][l%16], i = 0..3.

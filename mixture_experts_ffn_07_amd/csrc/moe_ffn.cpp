@@ -68,6 +68,8 @@ moe_status check_config(const moe_config* c) {
   if (c->score_func != 0) return fail(MOE_ERR_UNSUPPORTED, "score_func must be 0 (sqrtsoftplus)");
   if (!std::isfinite(c->route_scale)) return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite");
   if (!(c->swiglu_limit > 0.f)) return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be > 0");
+  if (c->expert_format != 0 && c->expert_format != 1)
+    return fail(MOE_ERR_INVALID_ARG, "expert_format must be 0 (MXFP4) or 1 (MXFP8)");
   return MOE_OK;
 }
 
@@ -125,6 +127,7 @@ struct Region {
 
 struct WsLayout {
   moe::RouterPlan router;
+  moe::WeightFormat fmt = moe::kWMxfp4;  // routed experts' codec
   bool decode = false;  // few tokens: GEMV router, fused routing, weight-streaming projections
   int bm = 16;          // rows per routed GEMM tile
   int gemm_mt = 1, shared_mt = 1;
@@ -148,11 +151,12 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   const int64_t n = tokens * c->top_k;
   const int E = c->n_experts;
   L.router = moe::router_plan(tokens, E, c->hidden);
-  L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E), true, c->hidden % 128 == 0 && c->inter % 128 == 0);
-  L.shared_mt = moe::expert_gemm_mt(tokens, 1, false, false);
+  L.fmt = c->expert_format == 1 ? moe::kWMxfp8 : moe::kWMxfp4;
+  L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E), L.fmt, c->hidden % 128 == 0 && c->inter % 128 == 0);
+  L.shared_mt = moe::expert_gemm_mt(tokens, 1, moe::kWBf16, false);
   const int k_fp4 = c->hidden > c->inter ? c->hidden : c->inter;
   const int k_bf16 = c->n_shared ? (c->hidden > c->shared_inter ? c->hidden : c->shared_inter) : 0;
-  L.decode = tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&
+  L.decode = L.fmt == moe::kWMxfp4 && tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&
              moe::gemv_lds_bytes((int)tokens, k_fp4, true) <= kDecodeMaxLds &&
              moe::gemv_lds_bytes((int)tokens, k_bf16, false) <= kDecodeMaxLds;
   if (L.decode) {
@@ -670,7 +674,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   p.C = h;
   p.ldc = I;
   p.limit = c->swiglu_limit;
-  hipError_t err = moe::launch_expert_gemm(p, true, true, L.gemm_mt, L.max_tiles, st);
+  hipError_t err = moe::launch_expert_gemm(p, true, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
   // down: A = h rows in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
@@ -686,7 +690,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   p.N = H;
   p.C = y_slot;
   p.ldc = H;
-  err = moe::launch_expert_gemm(p, false, true, L.gemm_mt, L.max_tiles, st);
+  err = moe::launch_expert_gemm(p, false, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");
   if (c->n_shared == 1) {
@@ -705,7 +709,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     q.C = hs;
     q.ldc = Is;
     q.limit = c->swiglu_limit;
-    err = moe::launch_expert_gemm(q, true, false, L.shared_mt, L.shared_tiles, st);
+    err = moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
     q.A = hs;
@@ -718,7 +722,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     q.N = H;
     q.C = y_shared;
     q.ldc = H;
-    err = moe::launch_expert_gemm(q, false, false, L.shared_mt, L.shared_tiles, st);
+    err = moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_down", st);
   if (err != hipSuccess) return fail_hip(err, "shared down launch");
   }

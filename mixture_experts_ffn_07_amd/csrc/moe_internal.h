@@ -79,7 +79,7 @@ struct GemmParams {
   int64_t lda;
   int a_rows;  // rows of A; gathered row indices are clamped into [0, a_rows)
   int K;
-  // B (weights), per expert: MXFP4 codes/scales or bf16, rows [.][K]
+  // B (weights), per expert: MXFP4 or MXFP8 codes/scales, or bf16, rows [.][K]
   const uint8_t* bq;
   const uint8_t* bs;
   const uint16_t* bh;
@@ -93,8 +93,10 @@ struct GemmParams {
 };
 // rows per tile / 16 for the grouped GEMM (MXFP4 or bf16 weights);
 // k_pipelined: every K of the problem is a multiple of 128
-int expert_gemm_mt(int64_t n_rows, int n_groups, bool fp4, bool k_pipelined);
-hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, bool fp4, int mt, int64_t grid_tiles,
+// weight codec of a grouped GEMM's B operand
+enum WeightFormat : int { kWBf16 = 0, kWMxfp4 = 1, kWMxfp8 = 2 };
+int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined);
+hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt, int mt, int64_t grid_tiles,
                               hipStream_t stream);
 
 // Few-token (decode) projections: up to two problems in one launch.

@@ -69,7 +69,7 @@ BAD_CONFIGS = [
     (dict(top_k=0), INVALID), (dict(top_k=17, n_experts=64), INVALID), (dict(top_k=7, n_experts=6), INVALID),
     (dict(n_shared=2), INVALID), (dict(shared_inter=40), INVALID), (dict(score_func=1), UNSUPPORTED),
     (dict(route_scale=float("inf")), INVALID), (dict(swiglu_limit=0.0), INVALID),
-    (dict(swiglu_limit=float("nan")), INVALID),
+    (dict(swiglu_limit=float("nan")), INVALID), (dict(expert_format=2), INVALID), (dict(expert_format=-1), INVALID),
 ]
 
 

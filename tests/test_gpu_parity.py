@@ -121,10 +121,12 @@ def test_permute_bit_exact(t, e, k, skew):
 # ------------------------------------------------------------------ experts and combine
 
 
-@pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims"])
+@pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k"])
 def test_expert_ffn(variant):
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
+           "fp8": base.with_(tokens=40, expert_format="mxfp8"),
+           "fp8_ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224, expert_format="mxfp8"),
            "decode_t3": base.with_(tokens=3),
            "ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224),
            "no_shared": base.with_(tokens=16, n_shared=0, shared_inter=0),
@@ -142,7 +144,7 @@ def test_expert_ffn(variant):
         lo, hi = perm["expert_offsets"][e], perm["expert_offsets"][e + 1]
         if hi > lo:
             wgu, wdn = oracle.routed_expert_weights(a["gu_q"], a["gu_s"], a["dn_q"], a["dn_s"], e, cfg.hidden,
-                                                    cfg.inter)
+                                                    cfg.inter, cfg.expert_format)
             rows = perm["sorted_slots"][lo:hi] // cfg.top_k
             ref_slot[lo:hi] = oracle.expert_mlp(x[rows], wgu, wdn, cfg.swiglu_limit)[1]
     assert_bar(bf16_to_f64(y_slot), ref_slot, "y_slot")
@@ -438,3 +440,55 @@ def test_layer_with_norm_zero_input():
     y, idx, _ = gpu_layer(inp)
     assert torch.all(y == 0)
     assert torch.all(idx.cpu() == torch.arange(6, dtype=torch.int32)[None, :])
+
+
+
+# ------------------------------------------------------------------ MXFP8 (E4M3) routed experts
+
+@pytest.mark.parametrize("tokens,variant", [(1, "tiny"), (2, "tiny"), (5, "tiny"), (64, "tiny"), (300, "tiny"),
+                                            (1, "min_dims"), (2, "ragged_k"), (7, "no_shared"), (3, "k16"),
+                                            (2, "v4pro_dims"), (40, "norm")])
+def test_layer_fp8(tokens, variant):
+    base = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, expert_format="mxfp8")
+    cfg = {"tiny": base,
+           "min_dims": base.with_(hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2),
+           "ragged_k": base.with_(hidden=160, inter=96, shared_inter=224),
+           "no_shared": base.with_(n_shared=0, shared_inter=0),
+           "k16": base.with_(top_k=16),
+           "norm": base.with_(norm=True),
+           "v4pro_dims": CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens, hidden=7168, inter=3072,
+                                                                 shared_inter=3072, n_experts=16,
+                                                                 expert_format="mxfp8")}[variant]
+    inp = make_inputs(cfg, seed=60 + tokens, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print(f"fp8 T={tokens} {variant}:", stats, "near-tie alternatives", len(alt))
+
+
+def test_layer_fp8_every_code():
+    """Every finite E4M3 code, under block scales from 2^-20 to 2^4, in both projections of every expert."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=16, expert_format="mxfp8", n_experts=8, top_k=4)
+    inp = make_inputs(cfg, seed=70, device=DEV)
+    g = torch.Generator().manual_seed(71)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    for q, sc in ((inp.gu_q, inp.gu_s), (inp.dn_q, inp.dn_s)):
+        n = q.numel()
+        codes = finite[torch.arange(n) % len(finite)]
+        q.copy_(codes[torch.randperm(n, generator=g)].reshape(q.shape).to(DEV))
+        # scales that keep the expert outputs in a moderate range (values up to 448 * 2^-12)
+        sc.copy_(torch.randint(107, 116, sc.shape, generator=g, dtype=torch.uint8).to(DEV))
+    stats, _, alt = _check_layer(inp)
+    print("fp8 every code:", stats, "near-tie alternatives", len(alt))
+
+
+def test_layer_fp8_decode_t1_full():
+    inp = make_inputs(CONFIGS["decode_t1_h5120_e384_fp8"], seed=0, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print("decode_t1 fp8:", stats, "near-tie alternatives", len(alt))
+
+
+def test_layer_fp8_prefill_sampled():
+    cfg = CONFIGS["prefill_t4096_h5120_e384_fp8"]
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    gpu = gpu_layer(inp)
+    stats, _, alt = _check_layer(inp, tokens=_sample(cfg.tokens, 6, seed=4), gpu=gpu)
+    print("prefill fp8 sampled:", stats, "near-tie alternatives", len(alt))
