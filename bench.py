@@ -72,13 +72,19 @@ def traffic_from_profile(kernel: str, workload: str, digest: str):
     return float(m.group(1)) if m else None
 
 
+def code_bytes(cfg) -> float:
+    """Bytes per routed-expert weight element: MXFP4 codes are half a byte, MXFP8 codes one byte."""
+    return 1.0 if cfg.expert_format == "mxfp8" else 0.5
+
+
 def algorithmic_bytes(cfg, touched: float) -> dict:
     """Bytes each kernel must move at least: weights it reads once, inputs once, outputs once."""
     t, h, e, k, i = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.inter
     i_s = cfg.shared_inter if cfg.n_shared else 0
     n = t * k
-    gu_expert = 2 * i * (h // 2 + h // 32)
-    dn_expert = h * (i // 2 + i // 32)
+    cb = code_bytes(cfg)
+    gu_expert = 2 * i * (h * cb + h // 32)
+    dn_expert = h * (i * cb + i // 32)
     return {
         "router_logits": e * h * 4 + t * h * 2 + t * e * 4,
         "router_topk": t * e * 4 + n * 8,
@@ -113,7 +119,8 @@ def layer_bytes(cfg, touched: float) -> float:
     """Algorithmic bytes of the whole layer: touched experts' and shared weights, router, x and y once."""
     t, h, e, i = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.inter
     i_s = cfg.shared_inter if cfg.n_shared else 0
-    per_expert = 2 * i * (h // 2 + h // 32) + h * (i // 2 + i // 32)
+    cb = code_bytes(cfg)
+    per_expert = 2 * i * (h * cb + h // 32) + h * (i * cb + i // 32)
     return touched * per_expert + 3 * i_s * h * 2 + e * h * 4 + 2 * t * h * 2
 
 
@@ -288,7 +295,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
-                   "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)", "router_weights": "fp32",
+                   "expert_weights": ("mxfp8 (e4m3 + e8m0 per 32)" if cfg.expert_format == "mxfp8"
+                                      else "mxfp4 (e2m1 + e8m0 per 32)"), "router_weights": "fp32",
                    "pre_ffn_rmsnorm": bool(cfg.norm),
                    "weight_sets_cycled": sets, "launch": "hipgraph (one graph per cycle over the weight sets)" if graphs is not None else "eager",
                    "parallelism": "single-gpu"},

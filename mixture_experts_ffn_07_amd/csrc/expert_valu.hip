@@ -3,9 +3,9 @@
 // At T <= 2 the routed experts are pure MXFP4 weight streaming (the layer's
 // cost is the weight bytes: Strata DEEPSEEK41 notes, opening paragraph and
 // the "Where it goes" table).  A 16-byte vector of E2M1 codes is exactly one
-// 32-element E8M0 block, so a wave reads one output column's weight rows laid
-// end to end: lane l takes vectors l, l + 64, ... with one scale byte each,
-// all issued at once.  Each vector is dequantised to bf16 pairs and
+// 32-element E8M0 block (of E4M3 codes, with MXFP8 weights, half a block), so
+// a wave reads one output column's weight rows laid end to end: lane l takes
+// vectors l, l + 64, ... with the scale byte of each, all issued at once.  Each vector is dequantised to bf16 pairs and
 // multiplied with the activations staged in LDS by v_dot2 (mx4_dot32); the
 // lanes' partial sums are added in a fixed order.
 //
@@ -51,11 +51,15 @@ struct GuItem {
   int tile, j;
 };
 
-template <int JM>
+// elements per 16-byte code vector: 32 (MXFP4) or 16 (MXFP8)
+template <bool FP8>
+constexpr int kVecElems = FP8 ? 16 : 32;
+
+template <int JM, bool FP8>
 __device__ __forceinline__ void gu_issue(ColBuf<JM>& b, const uint8_t* gu_q, const uint8_t* gu_s, const GuItem& it,
                                          int H, int I, int lane) {
-  const int VR = H / 32;
-  const uint32_t qbytes = (uint32_t)(2 * I * (H / 2)), sbytes = (uint32_t)(2 * I * VR);
+  const int VR = H / kVecElems<FP8>, row_bytes = FP8 ? H : H / 2;
+  const uint32_t qbytes = (uint32_t)(2 * I * row_bytes), sbytes = (uint32_t)(2 * I * (H / 32));
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(gu_q + (int64_t)it.rec.x * qbytes, qbytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(gu_s + (int64_t)it.rec.x * sbytes, sbytes);
 #pragma unroll
@@ -65,20 +69,20 @@ __device__ __forceinline__ void gu_issue(ColBuf<JM>& b, const uint8_t* gu_q, con
     const int bb = v - (up ? VR : 0);
     const bool ok = it.tile >= 0 && v < 2 * VR;
     const uint32_t row = (uint32_t)(it.j + (up ? I : 0));
-    const uint32_t qo = row * (uint32_t)(H / 2) + 16u * (uint32_t)bb;
-    const uint32_t so = row * (uint32_t)VR + (uint32_t)bb;
+    const uint32_t qo = row * (uint32_t)row_bytes + 16u * (uint32_t)bb;
+    const uint32_t so = row * (uint32_t)(H / 32) + (uint32_t)(FP8 ? bb >> 1 : bb);
     b.q[jj] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(ok ? qo : kOob), 0, 0));
     b.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? so : kOob), 0, 0);
   }
 }
 
 // blocks blk of nblk run the gate/up loop; lds holds x rows [T][H] bf16
-template <int JM, int TM>
+template <int JM, int TM, bool FP8>
 __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, int max_tiles, int blk, int nblk,
                                                     uint8_t* lds) {
   uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int T = p.tokens, H = p.hidden, I = p.inter, VR = H / 32;
+  const int T = p.tokens, H = p.hidden, I = p.inter, VR = H / kVecElems<FP8>;
 
   // tile records: lane t < max_tiles loads record t and its first two token
   // rows (one round trip, every wave for itself); the live ones are moved to
@@ -124,7 +128,7 @@ __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, i
   };
   ColBuf<JM> b0, b1;
   GuItem g0 = item(wg);
-  gu_issue<JM>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
+  gu_issue<JM, FP8>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
 
   stage_commit<4>(xb, x_pieces, 0, lds);
   stage_pieces<4>(rx, x_pieces, lds, x_off, 4 * kValuBlock);  // T = 2 rows beyond the first batch
@@ -148,7 +152,7 @@ __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, i
       for (int r = 0; r < TM; ++r) {
         if (r >= g.rec.z) break;  // wave-uniform
         const int src = r ? (g.rec.w >> 16) : (g.rec.w & 0xffff);
-        const float d = mx4_dot32(b.q[jj], scale, x_lds + src * H + 32 * bb, 0.f);
+        const float d = mx_dot_vec<FP8>(b.q[jj], scale, x_lds + src * H + kVecElems<FP8> * bb, 0.f);
         gs[r] += up ? 0.f : d;
         us[r] += up ? d : 0.f;
       }
@@ -163,18 +167,18 @@ __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, i
 
   for (int it = wg; it < total; it += 2 * W) {
     const GuItem g1 = item(it + W);
-    gu_issue<JM>(b1, p.gu_q, p.gu_s, g1, H, I, lane);
+    gu_issue<JM, FP8>(b1, p.gu_q, p.gu_s, g1, H, I, lane);
     compute(b0, g0);
     g0 = item(it + 2 * W);
-    gu_issue<JM>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
+    gu_issue<JM, FP8>(b0, p.gu_q, p.gu_s, g0, H, I, lane);
     if (g1.tile >= 0) compute(b1, g1);
   }
 }
 
-template <int JM, int TM>
+template <int JM, int TM, bool FP8>
 __global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpValuParams p, int max_tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  gate_up_valu_blocks<JM, TM>(p, max_tiles, (int)blockIdx.x, (int)gridDim.x, lds);
+  gate_up_valu_blocks<JM, TM, FP8>(p, max_tiles, (int)blockIdx.x, (int)gridDim.x, lds);
 }
 
 // ---------------------------------------------------------------- shared expert down
@@ -223,25 +227,25 @@ __device__ __forceinline__ void shared_down_blocks(const MidValuParams& m, int b
 // Launch 3 of the streaming few-token layer: blocks [0, gu_blocks) run the
 // routed gate/up loop, the rest the shared expert's down loop; the two are
 // independent and stream together.
-template <int JM, int TM, int KVD>
+template <int JM, int TM, int KVD, bool FP8>
 __global__ __launch_bounds__(kValuBlock) void gate_up_shared_down_kernel(GateUpValuParams p, int max_tiles,
                                                                          MidValuParams m, int gu_blocks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int b = (int)blockIdx.x;
   if (b < gu_blocks)
-    gate_up_valu_blocks<JM, TM>(p, max_tiles, b, gu_blocks, lds);
+    gate_up_valu_blocks<JM, TM, FP8>(p, max_tiles, b, gu_blocks, lds);
   else
     shared_down_blocks<KVD, TM>(m, b - gu_blocks, (int)gridDim.x - gu_blocks, lds);
 }
 
 // ---------------------------------------------------------------- down + combine
-template <int JM, int TM>
+template <int JM, int TM, bool FP8>
 __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // h of every slot [n][I] bf16
   uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.tokens, k = p.top_k, n = T * k;
-  const int H = p.hidden, I = p.inter, VR = I / 32;
+  const int H = p.hidden, I = p.inter, VR = I / kVecElems<FP8>, row_bytes = FP8 ? I : I / 2;
   // lane s < n holds slot s: expert, position of its h row, weight
   const int ls = min(lane, n - 1);
   const int my_e = p.idx[ls];
@@ -262,8 +266,8 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
     vb[jj] = v - s * VR < VR ? v - s * VR : VR - 1;
     vw[jj] = __shfl(my_w, s);
     const int64_t er = (int64_t)__shfl(my_e, s) * H;
-    qrow[jj] = p.dn_q + er * (I / 2) + 16 * vb[jj];
-    srow[jj] = p.dn_s + er * VR + vb[jj];
+    qrow[jj] = p.dn_q + er * row_bytes + 16 * vb[jj];
+    srow[jj] = p.dn_s + er * (I / 32) + (FP8 ? vb[jj] >> 1 : vb[jj]);
   }
   const int W = (int)gridDim.x * kValuWaves;
   const int wg = (int)blockIdx.x * kValuWaves + wave;
@@ -273,8 +277,8 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
     const int64_t c = min(col, H - 1);
 #pragma unroll
     for (int jj = 0; jj < JM; ++jj) {
-      b.q[jj] = *reinterpret_cast<const u32x4_t*>(qrow[jj] + c * (I / 2));
-      b.s[jj] = srow[jj][c * VR];
+      b.q[jj] = *reinterpret_cast<const u32x4_t*>(qrow[jj] + c * row_bytes);
+      b.s[jj] = srow[jj][c * (I / 32)];
     }
     b.ysh = __builtin_amdgcn_raw_buffer_load_b16(rsh, (int)(lane < T ? (uint32_t)((lane * H + c) * 2) : kOob), 0, 0);
   };
@@ -304,7 +308,8 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
     for (int jj = 0; jj < JM; ++jj) {
       __builtin_amdgcn_sched_barrier(0);  // one vector at a time (registers)
       const int s = max(vs[jj], 0);
-      const float d = mx4_dot32(b.q[jj], e8m0_scale_operand(b.s[jj]), h_lds + s * I + 32 * vb[jj], 0.f);
+      const float d = mx_dot_vec<FP8>(b.q[jj], e8m0_scale_operand(b.s[jj]), h_lds + s * I + kVecElems<FP8> * vb[jj],
+                                      0.f);
       const float wd = vs[jj] >= 0 ? vw[jj] * d : 0.f;
       const int t = s / k;
 #pragma unroll
@@ -330,71 +335,116 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
 // instantiated vector counts per lane; the smallest >= the need is used
 constexpr int kGateUpJm[] = {2, 4, 5, 7, 8};
 constexpr int kDownJm[] = {2, 4, 7, 9, 14};
+constexpr int kGateUpJm8[] = {2, 4, 10, 14};  // MXFP8: twice the vectors of a row
+constexpr int kDownJm8[] = {2, 4, 7, 14};
 // blocks per CU of the grid-stride loops (all resident at once)
 constexpr int kGateUpBlocksPerCu = 2;
 constexpr int kDownBlocksPerCu = 2;
 constexpr int kSharedDownBlocksPerCu = 1;
 
-int gate_up_jm(int hidden) {
-  const int need = (2 * (hidden / 32) + 63) / 64;
-  for (int j : kGateUpJm)
+template <size_t N>
+int first_at_least(const int (&js)[N], int need) {
+  for (int j : js)
     if (j >= need) return j;
   return 0;
 }
 
-int down_jm(int slots, int inter) {
-  const int need = (slots * (inter / 32) + 63) / 64;
-  for (int j : kDownJm)
-    if (j >= need) return j;
-  return 0;
+int gate_up_jm(int hidden, bool fp8) {
+  const int need = (2 * (hidden / (fp8 ? 16 : 32)) + 63) / 64;
+  return fp8 ? first_at_least(kGateUpJm8, need) : first_at_least(kGateUpJm, need);
+}
+
+int down_jm(int slots, int inter, bool fp8) {
+  const int need = (slots * (inter / (fp8 ? 16 : 32)) + 63) / 64;
+  return fp8 ? first_at_least(kDownJm8, need) : first_at_least(kDownJm, need);
 }
 
 using GateUpKernel = void (*)(GateUpValuParams, int);
 using GateUpSdKernel = void (*)(GateUpValuParams, int, MidValuParams, int);
-
-template <int TM, int KVD>
-GateUpSdKernel pick_gate_up_sd_t(int jm) {
-  switch (jm) {
-    case 2: return gate_up_shared_down_kernel<2, TM, KVD>;
-    case 4: return gate_up_shared_down_kernel<4, TM, KVD>;
-    case 5: return gate_up_shared_down_kernel<5, TM, KVD>;
-    case 7: return gate_up_shared_down_kernel<7, TM, KVD>;
-    case 8: return gate_up_shared_down_kernel<8, TM, KVD>;
-    default: return nullptr;
-  }
-}
-GateUpSdKernel pick_gate_up_sd(int jm, int tokens, int kvd) {
-  if (kvd == 5) return tokens == 1 ? pick_gate_up_sd_t<1, 5>(jm) : pick_gate_up_sd_t<2, 5>(jm);
-  if (kvd == 10) return tokens == 1 ? pick_gate_up_sd_t<1, 10>(jm) : pick_gate_up_sd_t<2, 10>(jm);
-  return nullptr;
-}
 using DownKernel = void (*)(DownValuParams);
 
-template <int TM>
-GateUpKernel pick_gate_up_t(int jm) {
-  switch (jm) {
-    case 2: return gate_up_valu_kernel<2, TM>;
-    case 4: return gate_up_valu_kernel<4, TM>;
-    case 5: return gate_up_valu_kernel<5, TM>;
-    case 7: return gate_up_valu_kernel<7, TM>;
-    case 8: return gate_up_valu_kernel<8, TM>;
-    default: return nullptr;
+template <int TM, int KVD, bool FP8>
+GateUpSdKernel pick_gate_up_sd_t(int jm) {
+  if constexpr (FP8) {
+    switch (jm) {
+      case 2: return gate_up_shared_down_kernel<2, TM, KVD, true>;
+      case 4: return gate_up_shared_down_kernel<4, TM, KVD, true>;
+      case 10: return gate_up_shared_down_kernel<10, TM, KVD, true>;
+      case 14: return gate_up_shared_down_kernel<14, TM, KVD, true>;
+      default: return nullptr;
+    }
+  } else {
+    switch (jm) {
+      case 2: return gate_up_shared_down_kernel<2, TM, KVD, false>;
+      case 4: return gate_up_shared_down_kernel<4, TM, KVD, false>;
+      case 5: return gate_up_shared_down_kernel<5, TM, KVD, false>;
+      case 7: return gate_up_shared_down_kernel<7, TM, KVD, false>;
+      case 8: return gate_up_shared_down_kernel<8, TM, KVD, false>;
+      default: return nullptr;
+    }
   }
 }
-GateUpKernel pick_gate_up(int jm, int tokens) { return tokens == 1 ? pick_gate_up_t<1>(jm) : pick_gate_up_t<2>(jm); }
+template <bool FP8>
+GateUpSdKernel pick_gate_up_sd_f(int jm, int tokens, int kvd) {
+  if (kvd == 5) return tokens == 1 ? pick_gate_up_sd_t<1, 5, FP8>(jm) : pick_gate_up_sd_t<2, 5, FP8>(jm);
+  if (kvd == 10) return tokens == 1 ? pick_gate_up_sd_t<1, 10, FP8>(jm) : pick_gate_up_sd_t<2, 10, FP8>(jm);
+  return nullptr;
+}
+GateUpSdKernel pick_gate_up_sd(int jm, int tokens, int kvd, bool fp8) {
+  return fp8 ? pick_gate_up_sd_f<true>(jm, tokens, kvd) : pick_gate_up_sd_f<false>(jm, tokens, kvd);
+}
 
-template <int TM>
-DownKernel pick_down_t(int jm) {
-  switch (jm) {
-    case 2: return down_combine_valu_kernel<2, TM>;
-    case 4: return down_combine_valu_kernel<4, TM>;
-    case 7: return down_combine_valu_kernel<7, TM>;
-    case 9: return down_combine_valu_kernel<9, TM>;
-    case 14: return down_combine_valu_kernel<14, TM>;
-    default: return nullptr;
+template <int TM, bool FP8>
+GateUpKernel pick_gate_up_t(int jm) {
+  if constexpr (FP8) {
+    switch (jm) {
+      case 2: return gate_up_valu_kernel<2, TM, true>;
+      case 4: return gate_up_valu_kernel<4, TM, true>;
+      case 10: return gate_up_valu_kernel<10, TM, true>;
+      case 14: return gate_up_valu_kernel<14, TM, true>;
+      default: return nullptr;
+    }
+  } else {
+    switch (jm) {
+      case 2: return gate_up_valu_kernel<2, TM, false>;
+      case 4: return gate_up_valu_kernel<4, TM, false>;
+      case 5: return gate_up_valu_kernel<5, TM, false>;
+      case 7: return gate_up_valu_kernel<7, TM, false>;
+      case 8: return gate_up_valu_kernel<8, TM, false>;
+      default: return nullptr;
+    }
   }
 }
-DownKernel pick_down(int jm, int tokens) { return tokens == 1 ? pick_down_t<1>(jm) : pick_down_t<2>(jm); }
+GateUpKernel pick_gate_up(int jm, int tokens, bool fp8) {
+  if (fp8) return tokens == 1 ? pick_gate_up_t<1, true>(jm) : pick_gate_up_t<2, true>(jm);
+  return tokens == 1 ? pick_gate_up_t<1, false>(jm) : pick_gate_up_t<2, false>(jm);
+}
+
+template <int TM, bool FP8>
+DownKernel pick_down_t(int jm) {
+  if constexpr (FP8) {
+    switch (jm) {
+      case 2: return down_combine_valu_kernel<2, TM, true>;
+      case 4: return down_combine_valu_kernel<4, TM, true>;
+      case 7: return down_combine_valu_kernel<7, TM, true>;
+      case 14: return down_combine_valu_kernel<14, TM, true>;
+      default: return nullptr;
+    }
+  } else {
+    switch (jm) {
+      case 2: return down_combine_valu_kernel<2, TM, false>;
+      case 4: return down_combine_valu_kernel<4, TM, false>;
+      case 7: return down_combine_valu_kernel<7, TM, false>;
+      case 9: return down_combine_valu_kernel<9, TM, false>;
+      case 14: return down_combine_valu_kernel<14, TM, false>;
+      default: return nullptr;
+    }
+  }
+}
+DownKernel pick_down(int jm, int tokens, bool fp8) {
+  if (fp8) return tokens == 1 ? pick_down_t<1, true>(jm) : pick_down_t<2, true>(jm);
+  return tokens == 1 ? pick_down_t<1, false>(jm) : pick_down_t<2, false>(jm);
+}
 
 int device_cus() {
   static int cached[64] = {0};
@@ -416,28 +466,28 @@ int valu_grid(int64_t columns, int blocks_per_cu) {
 
 }  // namespace
 
-bool gate_up_valu_supported(int tokens, int hidden, int max_tiles) {
+bool gate_up_valu_supported(int tokens, int hidden, int max_tiles, bool fp8) {
   return tokens >= 1 && tokens <= kValuMaxTokens && hidden % 32 == 0 && hidden <= 8192 &&
-         max_tiles <= kMaxLiveTiles && gate_up_jm(hidden) > 0;
+         max_tiles <= kMaxLiveTiles && gate_up_jm(hidden, fp8) > 0;
 }
 
-bool down_valu_supported(int tokens, int top_k, int inter) {
+bool down_valu_supported(int tokens, int top_k, int inter, bool fp8) {
   const int n = tokens * top_k;
   return tokens >= 1 && tokens <= kValuMaxTokens && inter % 32 == 0 && (int64_t)n * inter * 2 <= 64 * 1024 &&
-         down_jm(n, inter) > 0;
+         down_jm(n, inter, fp8) > 0;
 }
 
 hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream) {
   const dim3 grid(valu_grid((int64_t)max_tiles * p.inter, kGateUpBlocksPerCu));
   const size_t lds = (size_t)p.tokens * p.hidden * 2;
-  auto kern = pick_gate_up(gate_up_jm(p.hidden), p.tokens);
+  auto kern = pick_gate_up(gate_up_jm(p.hidden, p.fp8), p.tokens, p.fp8);
   if (!kern) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p, max_tiles);
   return hipGetLastError();
 }
 
-bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter) {
-  return gate_up_valu_supported(tokens, hidden, max_tiles) && shared_inter > 0 && shared_inter % 8 == 0 &&
+bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter, bool fp8) {
+  return gate_up_valu_supported(tokens, hidden, max_tiles, fp8) && shared_inter > 0 && shared_inter % 8 == 0 &&
          shared_inter <= 10 * 8 * 64;
 }
 
@@ -446,7 +496,7 @@ hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, 
   const int gu_blocks = valu_grid((int64_t)max_tiles * p.inter, kGateUpBlocksPerCu);
   const int sd_blocks = valu_grid(m.hidden, kSharedDownBlocksPerCu);
   const int kvd = m.shared_inter <= 5 * 8 * 64 ? 5 : 10;
-  auto kern = pick_gate_up_sd(gate_up_jm(p.hidden), p.tokens, kvd);
+  auto kern = pick_gate_up_sd(gate_up_jm(p.hidden, p.fp8), p.tokens, kvd, p.fp8);
   if (!kern) return hipErrorInvalidValue;
   const size_t lx = (size_t)p.tokens * p.hidden * 2, lh = (size_t)m.tokens * m.shared_inter * 2;
   hipLaunchKernelGGL(kern, dim3((unsigned)(gu_blocks + sd_blocks)), dim3(kValuBlock), lx > lh ? lx : lh, stream, p,
@@ -458,7 +508,7 @@ hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream)
   const dim3 grid(valu_grid(p.hidden, kDownBlocksPerCu));
   const int n = p.tokens * p.top_k;
   const size_t lds = (size_t)n * p.inter * 2;
-  auto kern = pick_down(down_jm(n, p.inter), p.tokens);
+  auto kern = pick_down(down_jm(n, p.inter, p.fp8), p.tokens, p.fp8);
   if (!kern) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p);
   return hipGetLastError();

@@ -127,6 +127,39 @@ __device__ __forceinline__ float mx4_dot32(const u32x4_t& q, float scale, const 
   return acc;
 }
 
+// Half an MXFP8 block: 16 E4M3 codes in a 16-byte vector (byte i = element
+// i) times 16 bf16 activations at x, added to acc; each code pair becomes two
+// bf16 values times the block scale (v_cvt_scalef32_pk_bf16_fp8, exact) for
+// one v_dot2.  Same register constraint on the activations as mx4_dot32.
+template <bool HI>
+__device__ __forceinline__ float mx8_dot_pair(uint32_t codes, float scale, uint32_t xi, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, HI),
+                                         __builtin_bit_cast(bf16x2_t, xi), acc, false);
+}
+
+__device__ __forceinline__ float mx8_dot16(const u32x4_t& q, float scale, const uint16_t* x, float acc) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4_t xx = *reinterpret_cast<const u32x4_t*>(x + 8 * h);
+    asm("" : "+v"(xx));
+    acc = mx8_dot_pair<false>(q[2 * h], scale, xx[0], acc);
+    acc = mx8_dot_pair<true>(q[2 * h], scale, xx[1], acc);
+    acc = mx8_dot_pair<false>(q[2 * h + 1], scale, xx[2], acc);
+    acc = mx8_dot_pair<true>(q[2 * h + 1], scale, xx[3], acc);
+  }
+  return acc;
+}
+
+// One 16-byte vector of codes of either codec against its activations:
+// MXFP4 32 elements, MXFP8 16.
+template <bool FP8>
+__device__ __forceinline__ float mx_dot_vec(const u32x4_t& q, float scale, const uint16_t* x, float acc) {
+  if constexpr (FP8)
+    return mx8_dot16(q, scale, x, acc);
+  else
+    return mx4_dot32(q, scale, x, acc);
+}
+
 // Copying `pieces` 16-byte pieces into LDS (dst + 16 * q) with all threads
 // of the block; piece q is read from byte offset off(q) of `rs`.  A batch
 // holds NP pieces per thread, loaded before any is stored, so it costs one

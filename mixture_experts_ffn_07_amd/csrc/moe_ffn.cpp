@@ -146,7 +146,7 @@ struct WsLayout {
   size_t total = 0;
 };
 
-WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
+WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_decode) {
   WsLayout L;
   const int64_t n = tokens * c->top_k;
   const int E = c->n_experts;
@@ -156,7 +156,8 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   L.shared_mt = moe::expert_gemm_mt(tokens, 1, moe::kWBf16, false);
   const int k_fp4 = c->hidden > c->inter ? c->hidden : c->inter;
   const int k_bf16 = c->n_shared ? (c->hidden > c->shared_inter ? c->hidden : c->shared_inter) : 0;
-  L.decode = L.fmt == moe::kWMxfp4 && tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&
+  const bool fp8 = L.fmt == moe::kWMxfp8;
+  L.decode = allow_decode && tokens >= 1 && tokens <= kDecodeMaxTokens && n <= moe::kPermuteChunk &&
              moe::gemv_lds_bytes((int)tokens, k_fp4, true) <= kDecodeMaxLds &&
              moe::gemv_lds_bytes((int)tokens, k_bf16, false) <= kDecodeMaxLds;
   if (L.decode) {
@@ -168,7 +169,7 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     L.splitk_gu = kSplitKGateUp && moe::splitk_supported((int)tokens, c->hidden, true);
     L.splitk_dn = moe::splitk_supported((int)tokens, c->inter, false);
     L.down_combine = L.down_combine && !L.splitk_dn && !L.splitk_gu;
-    L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter);
+    L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter, fp8);
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
@@ -182,12 +183,12 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
     if (bound < L.max_tiles) L.max_tiles = bound;
   }
   if (L.decode) {
-    L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden, (int)L.max_tiles);
+    L.valu_gu = L.route_small && moe::gate_up_valu_supported((int)tokens, c->hidden, (int)L.max_tiles, fp8);
     if (L.valu_gu || L.valu_dn) L.down_combine = false;  // h stays bf16
     L.stream4 = L.valu_gu && L.valu_dn &&
               moe::decode_valu_supported((int)tokens, c->hidden, c->n_shared ? c->shared_inter : 0) &&
               (c->n_shared == 0 ||
-               moe::gate_up_shared_down_supported((int)tokens, c->hidden, (int)L.max_tiles, c->shared_inter));
+               moe::gate_up_shared_down_supported((int)tokens, c->hidden, (int)L.max_tiles, c->shared_inter, fp8));
     L.norm_in_router = L.stream4 && moe::router_norm_gemv_supported((int)tokens, c->hidden);
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
@@ -220,6 +221,14 @@ WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   take(L.h_sh, sizeof(uint16_t) * tokens * is);
   take(L.y_sh, sizeof(uint16_t) * (c->n_shared ? tokens * c->hidden : 0));
   L.total = off;
+  return L;
+}
+
+WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
+  WsLayout L = plan_workspace_impl(c, tokens, true);
+  // MXFP8 weights have few-token kernels only in the one/two-token streaming
+  // form; other token counts take the general launch sequence
+  if (L.fmt == moe::kWMxfp8 && L.decode && !L.stream4) L = plan_workspace_impl(c, tokens, false);
   return L;
 }
 
@@ -436,6 +445,7 @@ moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, cons
   g.hidden = c->hidden;
   g.inter = c->inter;
   g.limit = c->swiglu_limit;
+  g.fp8 = L.fmt == moe::kWMxfp8;
   if (c->n_shared) {
     moe::MidValuParams m{};
     m.sh_dn = w->sh_dn;
@@ -465,6 +475,7 @@ moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, cons
   dv.top_k = c->top_k;
   dv.hidden = c->hidden;
   dv.inter = c->inter;
+  dv.fp8 = g.fp8;
   err = moe::launch_down_combine_valu(dv, st);
   if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
   if (err != hipSuccess) return fail_hip(err, "down/combine launch");
@@ -655,7 +666,8 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
                        hipStream_t st, Timeline* tl) {
   const int H = c->hidden, I = c->inter;
   uint16_t* h = at<uint16_t>(ws, L.h);
-  if (L.decode) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
+  // few-token expert kernels exist for MXFP4 weights; MXFP8 ones take the grouped GEMM
+  if (L.decode && L.fmt == moe::kWMxfp4) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
   moe::GemmParams p{};
   p.tiles = at<moe::GemmTile>(ws, L.tiles);
   p.tile_count = at<int32_t>(ws, L.tile_count);

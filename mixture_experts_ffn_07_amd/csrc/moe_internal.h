@@ -237,25 +237,27 @@ struct GateUpValuParams {
   const uint16_t* x;          // [T][H] bf16
   const GemmTile* tiles;      // [max_tiles]
   const int32_t* tile_rows;   // [max_tiles][kTileRows]
-  const uint8_t* gu_q;        // [E][2I][H/2]
+  const uint8_t* gu_q;        // [E][2I][H/2] (MXFP8: [E][2I][H])
   const uint8_t* gu_s;        // [E][2I][H/32]
   uint16_t* h;                // [T*k][I] bf16, row = position
   int tokens, hidden, inter;
   float limit;
+  bool fp8;                   // MXFP8 (E4M3) codes instead of MXFP4
 };
 struct DownValuParams {
   const uint16_t* h;          // [T*k][I] bf16, row = position
   const int32_t* idx;         // [T][k]
   const float* topk_w;        // [T][k]
   const int32_t* slot_pos;    // [T*k]
-  const uint8_t* dn_q;        // [E][H][I/2]
+  const uint8_t* dn_q;        // [E][H][I/2] (MXFP8: [E][H][I])
   const uint8_t* dn_s;        // [E][H][I/32]
   const uint16_t* y_shared;   // [T][H] or NULL
   uint16_t* y;                // [T][H]
   int tokens, top_k, hidden, inter;
+  bool fp8;                   // MXFP8 (E4M3) codes instead of MXFP4
 };
-bool gate_up_valu_supported(int tokens, int hidden, int max_tiles);
-bool down_valu_supported(int tokens, int top_k, int inter);
+bool gate_up_valu_supported(int tokens, int hidden, int max_tiles, bool fp8 = false);
+bool down_valu_supported(int tokens, int top_k, int inter, bool fp8 = false);
 hipError_t launch_gate_up_valu(const GateUpValuParams& p, int max_tiles, hipStream_t stream);
 hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream);
 // The streaming few-token layer (T <= 2), four launches:
@@ -264,7 +266,7 @@ hipError_t launch_down_combine_valu(const DownValuParams& p, hipStream_t stream)
 //   3. routed gate/up beside the shared down projection;
 //   4. routed down with the combine (launch_down_combine_valu).
 hipError_t launch_decode_route_shared_gu(const FrontValuParams& f, const RouteSmallParams& p, hipStream_t stream);
-bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter);
+bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter, bool fp8 = false);
 hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, const MidValuParams& m,
                                       hipStream_t stream);
 

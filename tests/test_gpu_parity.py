@@ -121,11 +121,13 @@ def test_permute_bit_exact(t, e, k, skew):
 # ------------------------------------------------------------------ experts and combine
 
 
-@pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k"])
+@pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k",
+                                     "fp8_t2"])
 def test_expert_ffn(variant):
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
            "fp8": base.with_(tokens=40, expert_format="mxfp8"),
+           "fp8_t2": base.with_(tokens=2, expert_format="mxfp8"),
            "fp8_ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224, expert_format="mxfp8"),
            "decode_t3": base.with_(tokens=3),
            "ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224),
@@ -447,8 +449,11 @@ def test_layer_with_norm_zero_input():
 
 @pytest.mark.parametrize("tokens,variant", [(1, "tiny"), (2, "tiny"), (5, "tiny"), (64, "tiny"), (300, "tiny"),
                                             (1, "min_dims"), (2, "ragged_k"), (7, "no_shared"), (3, "k16"),
-                                            (2, "v4pro_dims"), (40, "norm")])
+                                            (2, "v4pro_dims"), (40, "norm"), (1, "norm"), (1, "v4pro_dims"),
+                                            (2, "k1"), (1, "all_experts")])
 def test_layer_fp8(tokens, variant):
+    """MXFP8 experts: one and two tokens take the streaming kernels where their vector counts are built
+    (up to 14 vectors per lane), every other shape the grouped GEMM."""
     base = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, expert_format="mxfp8")
     cfg = {"tiny": base,
            "min_dims": base.with_(hidden=32, inter=32, shared_inter=32, n_experts=4, top_k=2),
@@ -456,6 +461,8 @@ def test_layer_fp8(tokens, variant):
            "no_shared": base.with_(n_shared=0, shared_inter=0),
            "k16": base.with_(top_k=16),
            "norm": base.with_(norm=True),
+           "k1": base.with_(top_k=1),
+           "all_experts": base.with_(n_experts=8, top_k=8),
            "v4pro_dims": CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens, hidden=7168, inter=3072,
                                                                  shared_inter=3072, n_experts=16,
                                                                  expert_format="mxfp8")}[variant]
@@ -484,6 +491,11 @@ def test_layer_fp8_decode_t1_full():
     inp = make_inputs(CONFIGS["decode_t1_h5120_e384_fp8"], seed=0, device=DEV)
     stats, _, alt = _check_layer(inp)
     print("decode_t1 fp8:", stats, "near-tie alternatives", len(alt))
+    cfg = moe.config_from(inp.cfg)
+    y = torch.empty((1, inp.cfg.hidden), dtype=torch.int16, device=DEV)
+    names = [n for n, _ in moe.moe_layer_forward_timed(cfg, moe.weights_from(inp), inp.x, 1, y,
+                                                       moe.workspace(cfg, 1, device=DEV))]
+    assert names == ["router_scores", "route_shared_gate_up", "routed_gate_up_shared_down", "routed_down_combine"]
 
 
 def test_layer_fp8_prefill_sampled():
