@@ -191,26 +191,29 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams p) {
 // streamed once.  Weights are read once per block from HBM and dequantised
 // in registers; the next chunk's weights and activation tile (double-
 // buffered in LDS) load while the current one is multiplied.
-// rows per tile: 128 with MXFP4 weights, 64 with bf16 weights (dense rows,
-// whose larger weight registers leave room for fewer accumulators)
-template <bool FP4>
-constexpr int tiled_m() { return FP4 ? 8 : 4; }  // 16-row MFMA tiles per block
+// rows per tile: 128 with MXFP4 weights, 96 with MXFP8 and 64 with bf16
+// weights (larger weight registers leave room for fewer accumulators at two
+// blocks per CU without spilling)
+template <int BF>
+constexpr int tiled_m() { return BF == kWBf16 ? 4 : BF == kWMxfp8 ? 6 : 8; }  // 16-row MFMA tiles per block
 // output columns per wave: 32 for gate/up (plus the 32 matching up columns), 64 for down
 template <bool SWIGLU>
 constexpr int tiled_cols_per_wave() { return SWIGLU ? 32 : 64; }
 constexpr int kTiledLdsStride = 128 + 8;  // bf16 elements per staged row (16 bytes of padding)
 
-template <bool SWIGLU, bool FP4>
+template <bool SWIGLU, int BF>
 struct TiledB {
   // 4 column tiles of 16 rows: for gate/up, tiles 0-1 are gate columns and
-  // 2-3 the matching up columns
-  u32x4_t q[4][FP4 ? 1 : 4];
+  // 2-3 the matching up columns; a lane's 32 K elements take 1 (MXFP4), 2
+  // (MXFP8) or 4 (bf16) 16-byte vectors
+  u32x4_t q[4][BF == kWMxfp4 ? 1 : BF == kWMxfp8 ? 2 : 4];
   uint32_t s[4];
 };
 
-template <bool SWIGLU, bool FP4>
-__device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, FP4>& b, const GemmParams& p, int e, int n0w, int col,
+template <bool SWIGLU, int BF>
+__device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, BF>& b, const GemmParams& p, int e, int n0w, int col,
                                              int grp, int c, int nchunks) {
+  constexpr bool FP4 = BF == kWMxfp4, FP8 = BF == kWMxfp8;
   const int K = p.K;
   const int k0 = c * 128 + grp * 32;
   const bool ok = c < nchunks && k0 < K;
@@ -227,6 +230,16 @@ __device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, FP4>& b, const GemmP
                                                   rq, (int)(ok ? r * (uint32_t)(K / 2) + (uint32_t)(k0 / 2) : kOob), 0, 0));
       b.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? r * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOob),
                                                     0, 0);
+    } else if constexpr (FP8) {
+      const uint32_t qb = (uint32_t)(p.b_expert_rows * K), sb = (uint32_t)(p.b_expert_rows * (K / 32));
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qb, qb);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sb, sb);
+      const uint32_t off = ok ? r * (uint32_t)K + (uint32_t)k0 : kOob;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        b.q[j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 16 * q, 0));
+      b.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? r * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOob),
+                                                    0, 0);
     } else {
       const uint32_t hb = (uint32_t)(p.b_expert_rows * K * 2);
       const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.bh + (int64_t)e * p.b_expert_rows * K, hb);
@@ -239,9 +252,10 @@ __device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, FP4>& b, const GemmP
   }
 }
 
-template <bool SWIGLU, bool FP4>
+template <bool SWIGLU, int BF>
 __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p) {
-  constexpr int kTiledM = tiled_m<FP4>();
+  constexpr bool FP4 = BF == kWMxfp4, FP8 = BF == kWMxfp8;
+  constexpr int kTiledM = tiled_m<BF>();
   constexpr int kTiledRows = 16 * kTiledM;
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][kTiledRows * kTiledLdsStride];
   __shared__ int32_t src_rows[kTiledRows];
@@ -305,17 +319,17 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
   // chunk keeps the matrix cores busy long enough to cover the load latency,
   // and the 4 x 32 accumulators leave no registers for a deeper pipeline)
   constexpr int PD = 1;
-  TiledB<SWIGLU, FP4> b0, b1, b2;
+  TiledB<SWIGLU, BF> b0, b1, b2;
   u32x4_t av[kAP];
   const int n_src = n_ok ? n0w : 0;
   a_issue(av, 0);
-  tiled_load_b<SWIGLU, FP4>(b0, p, e, n_src, col, grp, n_ok ? 0 : nchunks, nchunks);
-  if constexpr (PD == 2) tiled_load_b<SWIGLU, FP4>(b1, p, e, n_src, col, grp, n_ok ? 1 : nchunks, nchunks);
+  tiled_load_b<SWIGLU, BF>(b0, p, e, n_src, col, grp, n_ok ? 0 : nchunks, nchunks);
+  if constexpr (PD == 2) tiled_load_b<SWIGLU, BF>(b1, p, e, n_src, col, grp, n_ok ? 1 : nchunks, nchunks);
   a_commit(av, 0);
   __syncthreads();
   // multiply chunk c (activation tile in a_lds[buf], weights in bc): K step s
   // uses elements 8s..8s+7 of each lane group's 32
-  auto multiply = [&](const TiledB<SWIGLU, FP4>& bc, int buf) {
+  auto multiply = [&](const TiledB<SWIGLU, BF>& bc, int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t bb[4];
@@ -323,6 +337,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
       for (int j = 0; j < 4; ++j) {
         if constexpr (FP4)
           bb[j] = dequant_fp4x8(bc.q[j][0][s], e8m0_scale_operand(bc.s[j]));
+        else if constexpr (FP8)
+          bb[j] = dequant_fp8x8(bc.q[j][s >> 1][2 * (s & 1)], bc.q[j][s >> 1][2 * (s & 1) + 1],
+                                e8m0_scale_operand(bc.s[j]));
         else
           bb[j] = __builtin_bit_cast(bf16x8_t, bc.q[j][s]);
       }
@@ -340,9 +357,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
     const int buf = c & 1;
     a_issue(av, c + 1);
     if constexpr (PD == 2)
-      tiled_load_b<SWIGLU, FP4>(b2, p, e, n_src, col, grp, n_ok ? c + 2 : nchunks, nchunks);
+      tiled_load_b<SWIGLU, BF>(b2, p, e, n_src, col, grp, n_ok ? c + 2 : nchunks, nchunks);
     else
-      tiled_load_b<SWIGLU, FP4>(b1, p, e, n_src, col, grp, n_ok ? c + 1 : nchunks, nchunks);
+      tiled_load_b<SWIGLU, BF>(b1, p, e, n_src, col, grp, n_ok ? c + 1 : nchunks, nchunks);
     multiply(b0, buf);
     a_commit(av, buf ^ 1);
     b0 = b1;
@@ -851,9 +868,9 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
 }
 
 int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined) {
-  if (fmt == kWMxfp8) return 1;  // MXFP8 weights: the 16-row kernel
   const bool fp4 = fmt == kWMxfp4;
-  const int kTiledRows = 16 * (fp4 ? tiled_m<true>() : tiled_m<false>());
+  const int kTiledRows = 16 * (fmt == kWBf16 ? tiled_m<kWBf16>() : fmt == kWMxfp8 ? tiled_m<kWMxfp8>()
+                                                                                   : tiled_m<kWMxfp4>());
   // MXFP4 weights with every K a multiple of 128: the pipelined kernel at any
   // row count (it streams each expert's weights once per tile and measured
   // faster than 16-row tiles even at 1-5 rows per expert).  Otherwise rows
@@ -870,7 +887,7 @@ constexpr bool kPipe8 = true;  // the 8-wave form of the pipelined kernel
 template <bool SWIGLU, int BF>
 static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream) {
   constexpr bool FP4 = BF == kWMxfp4;
-  if (BF != kWMxfp8 && mt == tiled_m<FP4>()) {
+  if (mt == tiled_m<BF>()) {
     // 128- or 64-row tiles: the LDS-tiled kernel, 4 waves x tiled_cols_per_wave columns per block
     const int cols = 4 * tiled_cols_per_wave<SWIGLU>();
     const dim3 g(grid.x, (unsigned)((p.N + cols - 1) / cols));
@@ -885,7 +902,7 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
         return;
       }
     }
-    hipLaunchKernelGGL((expert_gemm_tiled_kernel<SWIGLU, FP4>), g, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((expert_gemm_tiled_kernel<SWIGLU, BF>), g, dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
   }

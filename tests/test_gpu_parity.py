@@ -450,7 +450,8 @@ def test_layer_with_norm_zero_input():
 @pytest.mark.parametrize("tokens,variant", [(1, "tiny"), (2, "tiny"), (5, "tiny"), (64, "tiny"), (300, "tiny"),
                                             (1, "min_dims"), (2, "ragged_k"), (7, "no_shared"), (3, "k16"),
                                             (2, "v4pro_dims"), (40, "norm"), (1, "norm"), (1, "v4pro_dims"),
-                                            (2, "k1"), (1, "all_experts")])
+                                            (2, "k1"), (1, "all_experts"), (1000, "few_experts"),
+                                            (700, "ragged_k")])
 def test_layer_fp8(tokens, variant):
     """MXFP8 experts: one and two tokens take the streaming kernels where their vector counts are built
     (up to 14 vectors per lane), every other shape the grouped GEMM."""
@@ -463,6 +464,7 @@ def test_layer_fp8(tokens, variant):
            "norm": base.with_(norm=True),
            "k1": base.with_(top_k=1),
            "all_experts": base.with_(n_experts=8, top_k=8),
+           "few_experts": base.with_(n_experts=8, top_k=2),  # ~250 rows per expert: several 96-row tiles
            "v4pro_dims": CONFIGS["decode_t1_h5120_e384"].with_(tokens=tokens, hidden=7168, inter=3072,
                                                                  shared_inter=3072, n_experts=16,
                                                                  expert_format="mxfp8")}[variant]
@@ -471,9 +473,11 @@ def test_layer_fp8(tokens, variant):
     print(f"fp8 T={tokens} {variant}:", stats, "near-tie alternatives", len(alt))
 
 
-def test_layer_fp8_every_code():
-    """Every finite E4M3 code, under block scales from 2^-20 to 2^4, in both projections of every expert."""
-    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=16, expert_format="mxfp8", n_experts=8, top_k=4)
+@pytest.mark.parametrize("tokens", [16, 512])
+def test_layer_fp8_every_code(tokens):
+    """Every finite E4M3 code, under block scales 2^-20 .. 2^-12, in both projections of every expert
+    (16 tokens: 16-row tiles; 512 tokens: 96-row tiles)."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, expert_format="mxfp8", n_experts=8, top_k=4)
     inp = make_inputs(cfg, seed=70, device=DEV)
     g = torch.Generator().manual_seed(71)
     finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
