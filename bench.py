@@ -11,7 +11,9 @@ Default workload: full-size decode, 1 token (hidden 5120, 384 MXFP4 experts
 of width 2304, top-6, one bf16 shared expert).  `roofline` describes the
 kernel that takes the most time, measured with HIP events on the stream it
 runs on; `cpu_baseline` times the CPU oracle on a few tokens of the same
-workload.
+workload.  Timed steps are plain launches on one HIP stream by default
+(`--launch graph` replays HIP graphs instead; the other form is timed after
+for reference).
 """
 
 from __future__ import annotations
@@ -41,7 +43,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_t1_h5120_e384")
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
+                    help="timed steps as plain launches on one HIP stream (measured ~2 us/step faster at one "
+                         "token) or as replays of HIP graphs (one per cycle over the weight sets); the other "
+                         "form is timed afterwards for reference")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed forwards per weight set for kernel times")
     ap.add_argument("--cpu-sample", type=int, default=16, help="decode tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--json-out", default="")
@@ -206,63 +211,62 @@ def main():
     # HIP graphs: one graph per weight set (one step) and one graph of a whole
     # cycle over the sets, replayed back to back as a model-level graph would
     # run consecutive layers; a step is still one whole layer forward
-    graphs = cycle = None
-    if not args.no_graph:
-        graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step_eager(0)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_eager(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for s in range(sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_eager(s)
+        graphs.append(g)
+    cycle = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cycle):
         for s in range(sets):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step_eager(s)
-            graphs.append(g)
-        cycle = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(cycle):
-            for s in range(sets):
-                step_eager(s)
-        torch.cuda.synchronize()
+            step_eager(s)
+    torch.cuda.synchronize()
 
-    def run(n_steps, offset=0):
+    def run(n_steps, offset=0, graph=True):
         i = 0
         while i < n_steps:
             s = (i + offset) % sets
-            if cycle is not None and s == 0 and n_steps - i >= sets:
+            if graph and s == 0 and n_steps - i >= sets:
                 cycle.replay()
                 i += sets
-            elif graphs is not None:
+            elif graph:
                 graphs[s].replay()
                 i += 1
             else:
                 step_eager(s)
                 i += 1
 
-    run(args.warmup)
+    use_graph = args.launch == "graph"
+    run(args.warmup, graph=use_graph)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record()
-    run(args.steps, offset=args.warmup)
+    run(args.steps, offset=args.warmup, graph=use_graph)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # eager timing for reference (same steps, plain launches)
+    # the other launch form for reference (same steps, from the same weight-set position)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    n_eager = min(args.steps, 100)
+    n_other = min(args.steps, 200) // sets * sets or sets
+    run(sets, graph=not use_graph)
     e0.record()
-    for i in range(n_eager):
-        step_eager(i % sets)
+    run(n_other, graph=not use_graph)
     e1.record()
     torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / n_eager
+    other_ms = e0.elapsed_time(e1) / n_other
 
     # per-kernel durations, HIP events on the library's stream around each kernel
     sums, counts = {}, {}
@@ -298,14 +302,15 @@ def main():
                    "expert_weights": ("mxfp8 (e4m3 + e8m0 per 32)" if cfg.expert_format == "mxfp8"
                                       else "mxfp4 (e2m1 + e8m0 per 32)"), "router_weights": "fp32",
                    "pre_ffn_rmsnorm": bool(cfg.norm),
-                   "weight_sets_cycled": sets, "launch": "hipgraph (one graph per cycle over the weight sets)" if graphs is not None else "eager",
+                   "weight_sets_cycled": sets, "launch": ("hipgraph (one graph per cycle over the weight sets)" if use_graph
+                                                       else "stream (plain launches on one HIP stream)"),
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
                      "kernel_ms": kernel_ms[dominant], "algorithmic_bytes": algo[dominant]},
         "layer": {"algorithmic_bytes": lb, "hbm_frac": lb / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
                   "flops": layer_flops(cfg), "experts_touched_per_step": touched_avg,
-                  "eager_ms_per_step": eager_ms, "kernel_ms": kernel_ms,
+                  ("stream_ms_per_step" if use_graph else "graph_ms_per_step"): other_ms, "kernel_ms": kernel_ms,
                   "kernel_source_digest": digest, "timed_wall_s": wall, "input_gen_s": gen_s},
         "cpu_baseline": None,
     }

@@ -395,15 +395,15 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
 }
 
 // ---------------------------------------------------------------- pipelined MXFP4 kernel
-// Same tiles as the LDS-tiled kernel (128 rows, 4 waves, 32 gate + 32 up or
-// 64 output columns per wave), with the operands brought into LDS by
-// gfx950's global-to-LDS loads (16 bytes per lane, no registers) in a
-// multi-stage pipeline: the weights kPipeB - 1 chunks ahead, the activation
-// tile one chunk ahead.  At ~64 rows per expert the routed projections read
-// each expert's weights once and are bound by that stream, so the weights
-// need several microseconds of loads in flight per CU; registers cannot hold
-// that, LDS can.  Per 128-wide K chunk and block: activation tile 128 x 256 B
-// (bf16), weight codes 256 rows x 64 B, scale words 256 x 4 B.
+// Same tiles as the LDS-tiled kernel (128 rows; 32 gate + 32 up or 64 output
+// columns per column group, four column groups per block), with the operands
+// brought into LDS by gfx950's global-to-LDS loads (16 bytes per lane, no
+// registers) in a multi-stage pipeline, activations and weights kPipe8A - 1
+// and kPipe8B - 1 chunks ahead.  At ~64 rows per expert the routed
+// projections read each expert's weights once; registers cannot hold the
+// loads in flight such a stream needs, LDS can.  Per 128-wide K chunk and
+// block: activation tile 128 x 256 B (bf16), weight codes 256 rows x 64 B,
+// scale words 256 x 4 B.
 //
 // LDS layouts are XOR-swizzled so that the 16 lanes reading one MFMA operand
 // column hit 16 different 16-byte bank groups: activation row r keeps its
@@ -412,11 +412,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
 // of consecutive LDS, so each lane fetches the global piece that belongs in
 // its slot.
 //
-// Synchronisation: per chunk each wave issues the same number of loads
-// (rows past the tile and chunks past K re-read valid addresses, results
-// unused), so an exact vmcnt wait retires the activation tile of chunk c
-// while the later weight loads stay in flight; a bare s_barrier (no fence,
-// which would drain every load) then publishes the chunk to all waves.
+// Synchronisation: per chunk each wave issues a fixed number of loads (rows
+// past the tile and chunks past K re-read valid addresses, results unused),
+// so an exact vmcnt wait retires chunk c while later chunks stay in flight; a
+// bare s_barrier (no fence, which would drain every load) then publishes the
+// chunk to all waves.
 // Global-to-LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS
 // byte address lds + 16 l (4 l).  Written in asm so that the compiler does not
 // treat the LDS it writes as possibly read by every later LDS load (it would
@@ -453,226 +453,54 @@ struct IntC {
   static constexpr int value = N;
 };
 
-constexpr int kPipeA = 2;  // activation stages
-constexpr int kPipeB = 5;  // weight stages
 constexpr int kPipeAStage = 128 * 256;  // bytes
 constexpr int kPipeBStage = 256 * 64;
 constexpr int kPipeSStage = 256 * 4;
-constexpr int kPipeLoadsA = 8;  // per wave per chunk (16-byte loads)
-constexpr int kPipeLoadsB = 4;
-constexpr int kPipeLoadsS = 1;  // 4-byte loads
-// loads a wave issues after chunk c's activation loads and before its wait at
-// chunk c: the weights of chunk c + kPipeB - kPipeA + 1, then kPipeA - 2 whole
-// chunks
-constexpr int kPipeWait = kPipeLoadsB + kPipeLoadsS + (kPipeA - 2) * (kPipeLoadsA + kPipeLoadsB + kPipeLoadsS);
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void expert_gemm_pipe_kernel(GemmParams p, int n_tiles, int col_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPipeA][kPipeAStage];
-  __shared__ __attribute__((aligned(16))) uint8_t b_lds[kPipeB][kPipeBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kPipeB][kPipeSStage];
-  __shared__ int32_t src_rows[128];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-
-  const PipeBlock pb = pipe_block(col_blocks);
-  if (pb.tile >= n_tiles) return;
-  int e = 0, m_begin, m_end;
-  if (p.tiles) {
-    if (pb.tile >= *p.tile_count) return;
-    const GemmTile tl = p.tiles[pb.tile];
-    e = tl.e;
-    m_begin = tl.m_begin;
-    m_end = min(tl.m_end, tl.m_begin + 128);
-  } else {
-    m_begin = pb.tile * 128;
-    m_end = min(m_begin + 128, p.M);
-  }
-  const int rows = m_end - m_begin;
-  const int K = p.K, nchunks = K / 128;
-  constexpr int CW = tiled_cols_per_wave<SWIGLU>();
-  const int n0 = pb.cb * 4 * CW;  // first output column of the block
-  for (int r = threadIdx.x; r < 128; r += 256) {
-    int src = p.gather ? p.gather[m_begin + min(r, rows - 1)] / p.gather_div : m_begin + min(r, rows - 1);
-    src_rows[r] = min(max(src, 0), p.a_rows - 1);
-  }
-  __syncthreads();
-
-  // this lane's global sources: activation rows of its 8 A loads, weight rows
-  // of its 4 code loads and of its scale load
-  // activation load t of this wave fills rows 4 i .. 4 i + 3, i = wave + 4 t
-  // (only while 4 i < rows: the loads after a chunk's activations, not their
-  // number, set the wait)
-  const uint8_t* a_src[kPipeLoadsA];
-#pragma unroll
-  for (int t = 0; t < kPipeLoadsA; ++t) {
-    const int row = 4 * (wave + 4 * t) + (lane >> 4);
-    const int piece = (lane & 15) ^ (row & 15);
-    a_src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src_rows[row] * p.lda) + 16 * piece;
-  }
-  auto brow_col = [&](int brow) {  // weight row (within the expert) of block weight row brow
-    int c;
-    if constexpr (SWIGLU) {
-      const int w = brow >> 6, j = (brow >> 4) & 3, n = brow & 15;
-      const int gc = min(n0 + 32 * w + 16 * (j & 1) + n, p.N - 1);
-      c = gc + (j >> 1) * p.b_row_second;
-    } else {
-      c = min(n0 + brow, p.N - 1);
-    }
-    return (int64_t)c;
-  };
-  const uint8_t* bq_e = p.bq + (int64_t)e * p.b_expert_rows * (K / 2);
-  const uint8_t* bs_e = p.bs + (int64_t)e * p.b_expert_rows * (K / 32);
-  const uint8_t* b_src[kPipeLoadsB];
-#pragma unroll
-  for (int t = 0; t < kPipeLoadsB; ++t) {
-    const int brow = 16 * (4 * wave + t) + (lane >> 2);
-    const int piece = (lane & 3) ^ ((brow >> 2) & 3);
-    b_src[t] = bq_e + brow_col(brow) * (K / 2) + 16 * piece;
-  }
-  const uint8_t* s_src = bs_e + brow_col(64 * wave + lane) * (K / 32);
-
-  auto issue_a = [&](int c) {
-    const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(a_lds[c % kPipeA] + 1024 * wave);
-#pragma unroll
-    for (int t = 0; t < kPipeLoadsA; ++t)
-      if (4 * (wave + 4 * t) < rows) load_lds16(a_src[t] + 256 * cc, dst + 4096 * t);  // wave-uniform
-  };
-  auto issue_b = [&](int c) {
-    const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(b_lds[c % kPipeB] + 1024 * (kPipeLoadsB * wave));
-#pragma unroll
-    for (int t = 0; t < kPipeLoadsB; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
-    load_lds4(s_src + 4 * cc, lds_addr(s_lds[c % kPipeB] + 256 * wave));
-  };
-
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int m_tiles = (rows + 15) / 16;  // block-uniform
-
-  // prologue: the first kPipeB - 1 weight chunks, then the first kPipeA - 1
-  // activation chunks interleaved with nothing after them (the loop's first
-  // wait is vmcnt(0))
-#pragma unroll
-  for (int c = 0; c < kPipeB - 1; ++c) issue_b(c);
-#pragma unroll
-  for (int c = 0; c < kPipeA - 1; ++c) issue_a(c);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // main loop, instantiated for MT row tiles (m_tiles rounded up to even; the
-  // extra tile's rows are copies of a valid row and are not stored).  Per
-  // chunk: weights and the first K step's activations read from LDS, then the
-  // next loads issued (their issue stalls overlap the LDS reads), then four K
-  // steps, each reading the next step's activations before its MFMAs.
-  auto run = [&](auto mt_tag) {
-    constexpr int MT = decltype(mt_tag)::value;
-    for (int c = 0; c < nchunks; ++c) {
-      if (c > 0) {
-        // chunk c's activations landed (kPipeWait later loads may be in
-        // flight); its weights were issued earlier still
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPipeWait) : "memory");
-      }
-      const uint8_t* al = a_lds[c % kPipeA];
-      const uint8_t* bl = b_lds[c % kPipeB];
-      const uint8_t* sl = s_lds[c % kPipeB];
-      u32x4_t q[4];
-      float sc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int brow = 64 * wave + 16 * j + col;
-        q[j] = *reinterpret_cast<const u32x4_t*>(bl + 64 * brow + 16 * (grp ^ ((brow >> 2) & 3)));
-        sc[j] = e8m0_scale_operand(sl[4 * brow + grp]);
-      }
-      auto read_a = [&](bf16x8_t (&a)[MT], int s4) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          a[m] = *reinterpret_cast<const bf16x8_t*>(al + 256 * (16 * m + col) + 16 * ((4 * grp + s4) ^ col));
-      };
-      bf16x8_t a_cur[MT], a_nxt[MT];
-      read_a(a_cur, 0);
-      issue_a(c + kPipeA - 1);
-      issue_b(c + kPipeB - 1);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        if (s4 < 3) read_a(a_nxt, s4 + 1);
-        bf16x8_t bb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bb[j] = dequant_fp4x8(q[j][s4], sc[j]);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[m][j] = mfma_16x16x32(a_cur[m], bb[j], acc[m][j]);
-        if (s4 < 3)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) a_cur[m] = a_nxt[m];
-      }
-    }
-  };
-  const int mt2 = (m_tiles + 1) / 2;
-  if (mt2 <= 1)
-    run(IntC<2>{});
-  else if (mt2 == 2)
-    run(IntC<4>{});
-  else if (mt2 == 3)
-    run(IntC<6>{});
-  else
-    run(IntC<8>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the past-the-end loads land before the block ends
-
-  // epilogue: lane holds rows 16m + 4*grp + i, column 16 jj + col of its columns
-  const int n0w = n0 + wave * CW;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * m + 4 * grp + i;
-      if (r < rows) {
-        if constexpr (SWIGLU) {
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int n = n0w + 16 * jj + col;
-            if (n < p.N)
-              p.C[(int64_t)(m_begin + r) * p.ldc + n] =
-                  f32_to_bf16(clamped_swiglu(acc[m][jj][i], acc[m][jj + 2][i], p.limit));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = n0w + 16 * j + col;
-            if (n < p.N) p.C[(int64_t)(m_begin + r) * p.ldc + n] = f32_to_bf16(acc[m][j][i]);
-          }
-        }
-      }
-    }
-  }
-}
-
-// 8-wave form of the pipelined kernel: two waves per column group split
+// The pipelined kernel has 8 waves: two waves per column group split
 // every K chunk (wave w: column group w & 3, K half w >> 2, i.e. steps
 // 2 (w >> 2) and 2 (w >> 2) + 1 of each lane group's 32 values), so each SIMD
 // runs two waves and one's LDS and dependency stalls overlap the other's
 // matrix work.  The halves' accumulators are added through LDS at the end.
 // Per chunk each wave issues up to 4 activation loads, then 2 weight-code
 // loads, and the waves of K half 0 one 4-byte scale load (weight rows 64 w +
-// lane); the wait after a chunk's activations is therefore vmcnt(3) for K
-// half 0 and vmcnt(2) for K half 1.  (Loads of 4 bytes or less fill 4-byte
-// LDS slots per lane.)
+// lane); the waits count these (pipe8_wait).  (Loads of 4 bytes or less fill
+// 4-byte LDS slots per lane.)
 constexpr int kPipe8LoadsA = 4;
 constexpr int kPipe8LoadsB = 2;
+constexpr int kPipe8A = 3;  // activation stages
+constexpr int kPipe8B = 3;  // weight stages
+static_assert(kPipe8A * kPipeAStage + kPipe8B * kPipeBStage >= 4 * 32768,
+              "the K-half reduction reuses 4 x 32 KB of the stage pool");
+// Each iteration c of the main loop issues the stream with the shorter lead
+// first (activations: chunk c + kPipe8A - 1, weights: chunk c + kPipe8B - 1).
+// At the top of iteration c, chunk c of both streams must have landed: the
+// wait allows as many loads in flight as were issued after the later of the
+// two (la activation and lb weight loads per iteration and wave).  Chunks
+// from the prologue are complete already (it ends with a full wait).
+constexpr bool kPipe8AFirst = kPipe8A <= kPipe8B;
+constexpr int pipe8_wait(int la, int lb) {
+  const int c = 64;  // any iteration past the prologue
+  const int ja = c - (kPipe8A - 1), jb = c - (kPipe8B - 1);
+  const int oa = kPipe8AFirst ? 0 : 1, ob = 1 - oa;
+  const bool a_later = ja > jb || (ja == jb && oa > ob);
+  const int j_last = a_later ? ja : jb, o_last = a_later ? oa : ob;
+  int n = 0;
+  for (int j = j_last; j < c; ++j)
+    for (int o = 0; o < 2; ++o)
+      if (j > j_last || o > o_last) n += o == oa ? la : lb;
+  return n;
+}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p, int n_tiles, int col_blocks) {
   // one pool: activation stages, weight-code stages, scale stages (the first
   // 128 KB also hold the K-half reduction at the end)
-  __shared__ __attribute__((aligned(16))) uint8_t pool[kPipeA * kPipeAStage + kPipeB * kPipeBStage + kPipeB * kPipeSStage];
+  __shared__ __attribute__((aligned(16))) uint8_t pool[kPipe8A * kPipeAStage + kPipe8B * kPipeBStage + kPipe8B * kPipeSStage];
   __shared__ int32_t src_rows[128];
   auto a_lds = [&](int i) { return pool + i * kPipeAStage; };
-  auto b_lds = [&](int i) { return pool + kPipeA * kPipeAStage + i * kPipeBStage; };
-  auto s_lds = [&](int i) { return pool + kPipeA * kPipeAStage + kPipeB * kPipeBStage + i * kPipeSStage; };
+  auto b_lds = [&](int i) { return pool + kPipe8A * kPipeAStage + i * kPipeBStage; };
+  auto s_lds = [&](int i) { return pool + kPipe8A * kPipeAStage + kPipe8B * kPipeBStage + i * kPipeSStage; };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int cg = wave & 3, kh = wave >> 2;
@@ -700,7 +528,12 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   }
   __syncthreads();
 
-  // activation load t fills rows 4 i .. 4 i + 3, i = wave + 8 t (while 4 i < rows)
+  // activation load t fills rows 4 i .. 4 i + 3, i = wave + 8 t, while 4 i <
+  // a_rows_run: the tile's rows rounded up to the row tiles the main loop runs
+  // (an even number of 16-row tiles), so that every wave issues MT / 2 of them
+  // (rows past the tile re-read its last row); the waits count on that
+  const int mt_run = min(2 * ((rows + 31) / 32), 8);
+  const int a_rows_run = 16 * mt_run;
   const uint8_t* a_src[kPipe8LoadsA];
 #pragma unroll
   for (int t = 0; t < kPipe8LoadsA; ++t) {
@@ -732,17 +565,17 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
 
   auto issue_a = [&](int c) {
     const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(a_lds(c % kPipeA) + 1024 * wave);
+    const uint32_t dst = lds_addr(a_lds(c % kPipe8A) + 1024 * wave);
 #pragma unroll
     for (int t = 0; t < kPipe8LoadsA; ++t)
-      if (4 * (wave + 8 * t) < rows) load_lds16(a_src[t] + 256 * cc, dst + 8192 * t);  // wave-uniform
+      if (4 * (wave + 8 * t) < a_rows_run) load_lds16(a_src[t] + 256 * cc, dst + 8192 * t);  // wave-uniform
   };
   auto issue_b = [&](int c) {
     const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(b_lds(c % kPipeB) + 2048 * wave);
+    const uint32_t dst = lds_addr(b_lds(c % kPipe8B) + 2048 * wave);
 #pragma unroll
     for (int t = 0; t < kPipe8LoadsB; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
-    if (kh == 0) load_lds4(s_src + 4 * cc, lds_addr(s_lds(c % kPipeB) + 256 * wave));  // wave-uniform
+    if (kh == 0) load_lds4(s_src + 4 * cc, lds_addr(s_lds(c % kPipe8B) + 256 * wave));  // wave-uniform
   };
 
   f32x4_t acc[8][4];
@@ -753,24 +586,28 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   const int m_tiles = (rows + 15) / 16;
 
 #pragma unroll
-  for (int c = 0; c < kPipeB - 1; ++c) issue_b(c);
+  for (int c = 0; c < kPipe8B - 1; ++c) issue_b(c);
 #pragma unroll
-  for (int c = 0; c < kPipeA - 1; ++c) issue_a(c);
+  for (int c = 0; c < kPipe8A - 1; ++c) issue_a(c);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   auto run = [&](auto mt_tag) {
     constexpr int MT = decltype(mt_tag)::value;
     for (int c = 0; c < nchunks; ++c) {
+      // MT / 2 activation loads per wave, the weight codes, and for K half 0
+      // the scale word
+      constexpr int kWait0 = pipe8_wait(MT / 2, kPipe8LoadsB + 1);
+      constexpr int kWait1 = pipe8_wait(MT / 2, kPipe8LoadsB);
       if (c > 0) {
         if (kh == 0)
-          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kPipe8LoadsB + 1) : "memory");
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait0) : "memory");
         else
-          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kPipe8LoadsB) : "memory");
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait1) : "memory");
         asm volatile("s_barrier" ::: "memory");
       }
-      const uint8_t* al = a_lds(c % kPipeA);
-      const uint8_t* bl = b_lds(c % kPipeB);
-      const uint8_t* sl = s_lds(c % kPipeB);
+      const uint8_t* al = a_lds(c % kPipe8A);
+      const uint8_t* bl = b_lds(c % kPipe8B);
+      const uint8_t* sl = s_lds(c % kPipe8B);
       uint32_t q[4][2];
       float sc[4];
 #pragma unroll
@@ -788,8 +625,13 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
       };
       bf16x8_t a0[MT], a1[MT];
       read_a(a0, 2 * kh);
-      issue_a(c + kPipeA - 1);
-      issue_b(c + kPipeB - 1);
+      if constexpr (kPipe8AFirst) {
+        issue_a(c + kPipe8A - 1);
+        issue_b(c + kPipe8B - 1);
+      } else {
+        issue_b(c + kPipe8B - 1);
+        issue_a(c + kPipe8A - 1);
+      }
       read_a(a1, 2 * kh + 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -803,12 +645,11 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
       }
     }
   };
-  const int mt2 = (m_tiles + 1) / 2;
-  if (mt2 <= 1)
+  if (mt_run <= 2)
     run(IntC<2>{});
-  else if (mt2 == 2)
+  else if (mt_run == 4)
     run(IntC<4>{});
-  else if (mt2 == 3)
+  else if (mt_run == 6)
     run(IntC<6>{});
   else
     run(IntC<8>{});
@@ -882,8 +723,6 @@ int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipeli
   return (avg > 16 && tiles >= 16) ? kTiledRows / 16 : 1;
 }
 
-constexpr bool kPipe8 = true;  // the 8-wave form of the pipelined kernel
-
 template <bool SWIGLU, int BF>
 static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream) {
   constexpr bool FP4 = BF == kWMxfp4;
@@ -895,10 +734,7 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
       if (p.K % 128 == 0) {  // MXFP4 weights: the pipelined kernel
         const int n_tiles = (int)grid.x, col_blocks = (int)g.y;
         const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
-        if (kPipe8)
-          hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
-        else
-          hipLaunchKernelGGL((expert_gemm_pipe_kernel<SWIGLU>), g1, dim3(256), 0, stream, p, n_tiles, col_blocks);
+        hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
         return;
       }
     }
