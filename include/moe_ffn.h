@@ -155,8 +155,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t t
 
 /* Expert FFNs.  For each position p in expert e's run (flat slot
  * f = sorted_slots[p], token t = f / k): y_slot[p] = o_e(x[t]) as bf16
- * [T*k][H], computed with the MXFP4 gated MLP of expert e (clamped SwiGLU,
- * "experts are gated MLPs": 'DeepSeek-V4.1-Flash' architecture sheet).
+ * [T*k][H], computed with the MXFP4 (or, by expert_format, MXFP8) gated
+ * MLP of expert e (clamped SwiGLU, "experts are gated MLPs":
+ * 'DeepSeek-V4.1-Flash' architecture sheet).
  * If n_shared == 1, also y_shared[t] = o_shared(x[t]) as bf16 [T][H]
  * (BF16 weights, same clamp); y_shared must be NULL iff n_shared == 0.
  * expert_offsets and sorted_slots as produced by moe_permute. */

@@ -91,7 +91,7 @@ struct GemmParams {
   int64_t ldc;
   float limit;
 };
-// rows per tile / 16 for the grouped GEMM (MXFP4 or bf16 weights);
+// rows per tile / 16 for the grouped GEMM (MXFP4, MXFP8 or bf16 weights);
 // k_pipelined: every K of the problem is a multiple of 128
 // weight codec of a grouped GEMM's B operand
 enum WeightFormat : int { kWBf16 = 0, kWMxfp4 = 1, kWMxfp8 = 2 };
