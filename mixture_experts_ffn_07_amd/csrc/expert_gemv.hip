@@ -612,22 +612,19 @@ hipError_t launch_splitk(const GemvProblem& p, int rows_cap, float limit, hipStr
 
 }  // namespace
 
-// Split-K few-token projection: usable when the rows of a tile, the block's
-// scales and the wave partials fit in 64 KB and K needs at most 8 waves.
-bool splitk_supported(int rows_cap, int K, bool swiglu) {
-  const int nb = swiglu ? 2 : 1, cpw = swiglu ? kSplitKChunksGateUp : kSplitKChunksDown;
+// Split-K few-token down projection (the gate/up projection measured faster
+// on the 64-column kernel): usable when the rows of a tile, the block's scales
+// and the wave partials fit in 64 KB and K needs at most 8 waves.
+bool splitk_supported(int rows_cap, int K) {
+  const int nb = 1, cpw = kSplitKChunksDown;
   const int waves = ((K + 127) / 128 + cpw - 1) / cpw;
   const size_t shm = gemv_lds_bytes(rows_cap, K, true) + (size_t)nb * 16 * (K / 32) + 16 + (size_t)(waves - 1) * nb * 1024;
   return rows_cap <= kTileRows && waves <= 8 && shm <= 64 * 1024;
 }
 
-hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, float limit, bool swiglu,
-                                     hipStream_t stream) {
+hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, hipStream_t stream) {
   if (p.grid_tiles == 0 || p.N == 0) return hipSuccess;
-  if (swiglu)
-    return p.amx ? launch_splitk<2, kSplitKChunksGateUp, true>(p, rows_cap, limit, stream)
-                 : launch_splitk<2, kSplitKChunksGateUp, false>(p, rows_cap, limit, stream);
-  return launch_splitk<1, kSplitKChunksDown, false>(p, rows_cap, limit, stream);
+  return launch_splitk<1, kSplitKChunksDown, false>(p, rows_cap, 0.f, stream);
 }
 
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream) {

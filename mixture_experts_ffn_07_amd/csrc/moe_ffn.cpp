@@ -48,8 +48,6 @@ constexpr int64_t kMaxTokens = int64_t(1) << 22;
 constexpr int64_t kDecodeMaxTokens = 8;
 constexpr size_t kDecodeMaxLds = 64 * 1024;
 constexpr int kMaxDim = 65536;
-// few tokens: routed gate/up by the split-K kernel (else the 64-column kernel)
-constexpr bool kSplitKGateUp = false;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -134,7 +132,6 @@ struct WsLayout {
   int64_t max_tiles = 0, shared_tiles = 0;
   bool route_small = false;   // decode with T * k <= 64: scores from the router GEMV, one-block routing
   bool down_combine = false;  // decode: routed down projection with the combine folded in
-  bool splitk_gu = false;     // decode: routed gate/up by the split-K MXFP4 kernel
   bool splitk_dn = false;     // decode: routed down by the split-K MXFP4 kernel
   bool valu_gu = false;       // decode, T <= 2: routed gate/up one wave per column on the vector ALUs
   bool valu_dn = false;       // decode, T <= 2: routed down + combine one wave per column on the vector ALUs
@@ -166,9 +163,8 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
                      moe::down_combine_lds_bytes((int)tokens, c->top_k, c->inter) <= kDecodeMaxLds;
     // the split-K down projection plus a separate combine measured faster than
     // the fused down+combine kernel (11.8 + 4.1 us against 19.8 us at T = 1)
-    L.splitk_gu = kSplitKGateUp && moe::splitk_supported((int)tokens, c->hidden, true);
-    L.splitk_dn = moe::splitk_supported((int)tokens, c->inter, false);
-    L.down_combine = L.down_combine && !L.splitk_dn && !L.splitk_gu;
+    L.splitk_dn = moe::splitk_supported((int)tokens, c->inter);
+    L.down_combine = L.down_combine && !L.splitk_dn;
     L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter, fp8);
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
@@ -598,8 +594,6 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     g.inter = c->inter;
     g.limit = c->swiglu_limit;
     err = moe::launch_gate_up_valu(g, (int)L.max_tiles, st);
-  } else if (L.splitk_gu) {
-    err = moe::launch_expert_gemv_splitk(gu.p[0], gu.rows_cap, gu.limit, true, st);
   } else {
     if (L.down_combine) gu.p[0].cmx = at<uint8_t>(ws, L.hmx);  // h in MXFP8 form for the down step
     err = moe::launch_expert_gemv(gu, true, true, st);
@@ -650,7 +644,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   }
   moe::GemvParams dn = routed_gemv(c, w, x, nullptr, T, sorted, ws, L, false, y_slot);
   if (L.route_small) dn.p[0].tile_rows = nullptr;  // down rows are the tile's own positions
-  err = L.splitk_dn ? moe::launch_expert_gemv_splitk(dn.p[0], dn.rows_cap, dn.limit, false, st)
+  err = L.splitk_dn ? moe::launch_expert_gemv_splitk(dn.p[0], dn.rows_cap, st)
                     : moe::launch_expert_gemv(dn, false, true, st);
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");

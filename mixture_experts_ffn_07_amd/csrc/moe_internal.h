@@ -137,14 +137,12 @@ size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4);
 // 64-column blocks).  Otherwise up to two dense bf16 problems (bh).
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream);
 
-// MXFP4 few-token projection, split-K form: one block per (tile, 16 output
-// columns), its waves splitting K into ranges of kSplitKChunks* 128-wide
-// chunks.  Problem as for launch_expert_gemv with fp4 (no MXFP8 output).
-constexpr int kSplitKChunksGateUp = 10;
+// MXFP4 few-token down projection, split-K form: one block per (tile, 16
+// output columns), its waves splitting K into ranges of kSplitKChunksDown
+// 128-wide chunks.  Problem as for launch_expert_gemv with fp4.
 constexpr int kSplitKChunksDown = 5;
-bool splitk_supported(int rows_cap, int K, bool swiglu);
-hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, float limit, bool swiglu,
-                                     hipStream_t stream);
+bool splitk_supported(int rows_cap, int K);
+hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, hipStream_t stream);
 
 // One-block routing of T tokens with T * top_k <= 64 from the scores of
 // launch_router_gemv: top-k and weights, the stable permutation and the
