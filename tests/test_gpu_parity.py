@@ -375,7 +375,7 @@ def _norm_inputs(t, h, seed):
 
 
 @pytest.mark.parametrize("t,h", [(1, 5120), (7, 5120), (3, 7168), (5, 32), (9, 8192), (4, 8224), (2, 65536),
-                                 (1000, 512), (4096, 5120)])
+                                 (1000, 512), (4096, 5120), (20000, 256)])
 def test_rmsnorm_bit_exact(t, h):
     """moe_rmsnorm against the oracle bit for bit (single-pass rows up to 8192, two-pass beyond), in place too."""
     x, gam = _norm_inputs(t, h, seed=t * 7 + h)
@@ -508,3 +508,13 @@ def test_layer_fp8_prefill_sampled():
     gpu = gpu_layer(inp)
     stats, _, alt = _check_layer(inp, tokens=_sample(cfg.tokens, 6, seed=4), gpu=gpu)
     print("prefill fp8 sampled:", stats, "near-tie alternatives", len(alt))
+
+
+@pytest.mark.parametrize("e,k,tokens", [(1, 1, 3), (2, 2, 1), (128, 3, 40), (1000, 6, 2), (1000, 6, 24)])
+def test_layer_fp8_expert_counts(e, k, tokens):
+    """MXFP8 experts across expert counts and top-k (streaming kernels at one or two tokens, grouped GEMM
+    otherwise)."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, n_experts=e, top_k=k, expert_format="mxfp8")
+    inp = make_inputs(cfg, seed=80 + e, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print(f"fp8 E={e} k={k} T={tokens}:", stats, "near-tie alternatives", len(alt))
