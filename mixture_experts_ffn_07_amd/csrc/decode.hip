@@ -25,6 +25,27 @@
 namespace moe {
 
 // ---------------------------------------------------------------- routing
+// x -> two-term MXFP8 rows (mx_device.h): one thread per block of 32 values,
+// items i = first + k * stride (k = 0, 1, ...), loads first.
+__device__ __forceinline__ void convert_x_mx(const uint16_t* x, uint8_t* xmx, int tokens, int hidden, int first,
+                                             int stride) {
+  const int nblk = hidden / 32, row_stride = mx_row_bytes(hidden);
+  const int total = tokens * nblk;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)tokens * hidden * 2);
+  for (int i = first; i < total; i += stride) {
+    const int r = i / nblk, b = i - r * nblk;
+    u32x4_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = __builtin_bit_cast(u32x4_t,
+                                __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((r * hidden + 32 * b) * 2), 16 * q, 0));
+    float xv[32];
+    unpack_bf16x32(v, xv);
+    uint8_t* row = xmx + (int64_t)r * row_stride;
+    mx_convert_block(xv, row + 32 * b, row + hidden + 32 * b, row + 2 * hidden + b);
+  }
+}
+
 template <int MPL>
 __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   __shared__ int32_t idx_sh[64];
@@ -34,32 +55,31 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
   // streaming waves: highest issue priority for this block's waves
   __builtin_amdgcn_s_setprio(3);
 
-  // x -> MXFP8 rows: one thread per block of 32 values, loads first
-  if (p.xmx) {
-    const int nblk = p.hidden / 32, stride = mx_row_bytes(p.hidden);
-    const int total = p.tokens * nblk;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)p.tokens * p.hidden * 2);
-    // items are dealt from the last thread down, so the first waves, which
-    // also run the top-k below, get the least conversion work
-    for (int i = 255 - (int)threadIdx.x; i < total; i += 256) {
-      const int r = i / nblk, b = i - r * nblk;
-      u32x4_t v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((r * p.hidden + 32 * b) * 2), 16 * q, 0));
-      float xv[32];
-      unpack_bf16x32(v, xv);
-      uint8_t* row = p.xmx + (int64_t)r * stride;
-      mx_convert_block(xv, row + 32 * b, row + p.hidden + 32 * b, row + 2 * p.hidden + b);
+  // x -> MXFP8 rows (when launch 1 has not made them); items are dealt from
+  // the last thread down, so the first waves, which also run the top-k
+  // below, get the least conversion work
+  if (p.xmx) convert_x_mx(p.x, p.xmx, p.tokens, p.hidden, 255 - (int)threadIdx.x, 256);
+
+  // top-k of each token from its scores (s at scores[t], s + bias at scores[T + t]);
+  // past four tokens a wave takes tokens t and t + 4 together
+  if (p.tokens <= 4) {
+    for (int t = wave; t < p.tokens; t += 4)
+      topk_token<MPL, true>(p.scores + (size_t)t * p.n_experts, 1, 0, nullptr, p.n_experts, p.top_k, p.route_scale,
+                            p.idx + (size_t)t * p.top_k, p.w + (size_t)t * p.top_k, nullptr, idx_sh + t * p.top_k,
+                            p.scores + (size_t)(p.tokens + t) * p.n_experts);
+  } else {
+    for (int t0 = wave; t0 < p.tokens; t0 += 8) {
+      const bool two = t0 + 4 < p.tokens;
+      const int t1 = two ? t0 + 4 : t0;
+      const float* const s_row[2] = {p.scores + (size_t)t0 * p.n_experts, p.scores + (size_t)t1 * p.n_experts};
+      const float* const u_row[2] = {p.scores + (size_t)(p.tokens + t0) * p.n_experts,
+                                     p.scores + (size_t)(p.tokens + t1) * p.n_experts};
+      int32_t* const idx_row[2] = {p.idx + (size_t)t0 * p.top_k, p.idx + (size_t)t1 * p.top_k};
+      float* const w_row[2] = {p.w + (size_t)t0 * p.top_k, p.w + (size_t)t1 * p.top_k};
+      int32_t* const idx_l[2] = {idx_sh + t0 * p.top_k, idx_sh + t1 * p.top_k};
+      topk_token_pair<MPL>(s_row, u_row, two, p.n_experts, p.top_k, p.route_scale, idx_row, w_row, idx_l);
     }
   }
-
-  // top-k of each token from its scores (s at scores[t], s + bias at scores[T + t])
-  for (int t = wave; t < p.tokens; t += 4)
-    topk_token<MPL, true>(p.scores + (size_t)t * p.n_experts, 1, 0, nullptr, p.n_experts, p.top_k, p.route_scale,
-                          p.idx + (size_t)t * p.top_k, p.w + (size_t)t * p.top_k, nullptr, idx_sh + t * p.top_k,
-                          p.scores + (size_t)(p.tokens + t) * p.n_experts);
   __syncthreads();
   if (wave != 0) return;
 
@@ -103,7 +123,9 @@ __device__ __forceinline__ void route_small_block(const RouteSmallParams& p) {
 }
 
 // Launch 1 of the few-token layer: the shared expert's gate/up blocks
-// (longest first), then the router GEMV, one expert per wave.
+// (longest first), then the router GEMV, one expert per wave, then (with
+// f.xmx) the blocks that put x in two-term MXFP8 form for the routed gate/up,
+// off the routing block's critical path in launch 2.
 __global__ __launch_bounds__(256) void decode_front_kernel(FrontParams f) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int shared_blocks = f.shared.grid_tiles * f.shared.col_tiles;
@@ -111,8 +133,15 @@ __global__ __launch_bounds__(256) void decode_front_kernel(FrontParams f) {
     gemv_bf16_block<true>(f.shared, blockIdx.x, f.rows_cap, f.limit, lds);
     return;
   }
-  const int e = ((int)blockIdx.x - shared_blocks) * 4 + (int)(threadIdx.x >> 6);
-  router_gemv_wave(f.x, f.router_w, nullptr, f.tokens, f.n_experts, f.hidden, f.scores, f.bias, e);
+  const int router_blocks = (f.n_experts + 3) / 4;
+  const int rb = (int)blockIdx.x - shared_blocks;
+  if (rb < router_blocks) {
+    router_gemv_wave(f.x, f.router_w, nullptr, f.tokens, f.n_experts, f.hidden, f.scores, f.bias,
+                     rb * 4 + (int)(threadIdx.x >> 6));
+    return;
+  }
+  const int cb = rb - router_blocks, conv_blocks = (int)gridDim.x - shared_blocks - router_blocks;
+  convert_x_mx(f.x, f.xmx, f.tokens, f.hidden, cb * 256 + (int)threadIdx.x, conv_blocks * 256);
 }
 
 // Launch 2: the routing block (block 0), then the shared expert's down
@@ -273,7 +302,8 @@ hipError_t launch_decode_route_shared_gu(const FrontValuParams& f, const RouteSm
 
 hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream) {
   const int shared_blocks = f.shared.grid_tiles * f.shared.col_tiles;
-  const dim3 grid((unsigned)(shared_blocks + (f.n_experts + 3) / 4));
+  const int conv_blocks = f.xmx ? (f.tokens * (f.hidden / 32) + 255) / 256 : 0;
+  const dim3 grid((unsigned)(shared_blocks + (f.n_experts + 3) / 4 + conv_blocks));
   const size_t shm = shared_blocks ? gemv_bf16_lds_bytes(f.rows_cap, f.shared.K) : 0;
   hipLaunchKernelGGL(decode_front_kernel, grid, dim3(256), shm, stream, f);
   return hipGetLastError();

@@ -528,6 +528,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
       if (c->n_shared) f.shared = shared_gemv(c, w, x, T, ws, L, true, y_sh).p[0];
       f.rows_cap = (int)T;
       f.limit = c->swiglu_limit;
+      f.xmx = L.valu_gu ? nullptr : at<uint8_t>(ws, L.xmx);  // converted beside the router, not in the routing block
       err = moe::launch_decode_front(f, st);
     }
     if (err == hipSuccess) err = mark(tl, "router_shared_gate_up", st);
@@ -535,7 +536,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     xmx = at<uint8_t>(ws, L.xmx);
     moe::RouteSmallParams rp{};
     rp.x = x;
-    rp.xmx = L.valu_gu ? nullptr : xmx;  // the vector-ALU gate/up reads bf16 x
+    rp.xmx = L.valu_gu || !valu ? nullptr : xmx;  // the vector-ALU gate/up reads bf16 x; launch 1 converted it
     rp.scores = scores;
     rp.tokens = (int)T;
     rp.n_experts = E;

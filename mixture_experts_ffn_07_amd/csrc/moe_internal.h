@@ -177,6 +177,7 @@ struct FrontParams {
   GemvProblem shared;
   int rows_cap;
   float limit;
+  uint8_t* xmx;  // non-NULL: also write x in two-term MXFP8 form (mx_device.h), [T][mx_row_bytes(H)]
 };
 hipError_t launch_decode_front(const FrontParams& f, hipStream_t stream);
 // T <= 2 forms of the two launches: every weight row streamed by one wave

@@ -152,6 +152,111 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
   if (gap_out && lane == 0) *gap_out = gap;
 }
 
+// topk_token<MPL, true> for two tokens at once (scores s at s_row[i], selection
+// scores u at u_row[i], i = 0, 1): the same per-token selection, with the two
+// tokens' loads issued together and their reduction chains interleaved, so
+// the pair takes about the latency of one.  Outputs as topk_token (no tie
+// gap); the second token is skipped when `two` is false (wave-uniform).
+template <int kMaxPerLane>
+__device__ __forceinline__ void topk_token_pair(const float* const (&s_row)[2], const float* const (&u_row)[2],
+                                                bool two, int n_experts, int top_k, float route_scale,
+                                                int32_t* const (&idx_row)[2], float* const (&w_row)[2],
+                                                int32_t* const (&idx_lds)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int nt = two ? 2 : 1;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j)
+    if (lane + 64 * j < n_experts) valid |= 1u << j;
+  float su[2][kMaxPerLane], ss[2][kMaxPerLane];
+  int se[2][kMaxPerLane];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = tt < nt ? tt : 0;  // a missing second token repeats the first (results dropped)
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = min(lane + 64 * j, n_experts - 1);
+      const bool v = (valid >> j) & 1u;
+      const float uu = u_row[t][e];
+      ss[tt][j] = s_row[t][e];
+      su[tt][j] = v && uu == uu ? uu : -INFINITY;
+      se[tt][j] = v ? lane + 64 * j : 0x7fffffff;
+    }
+  }
+  // each lane's list sorted by (u desc, index asc): odd-even transposition
+#pragma unroll
+  for (int pass = 0; pass < kMaxPerLane; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < kMaxPerLane; i += 2) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bool sw = (su[tt][i + 1] > su[tt][i]) | ((su[tt][i + 1] == su[tt][i]) & (se[tt][i + 1] < se[tt][i]));
+        const float tu = su[tt][i], ts = ss[tt][i];
+        const int te = se[tt][i];
+        su[tt][i] = sw ? su[tt][i + 1] : su[tt][i];
+        se[tt][i] = sw ? se[tt][i + 1] : se[tt][i];
+        ss[tt][i] = sw ? ss[tt][i + 1] : ss[tt][i];
+        su[tt][i + 1] = sw ? tu : su[tt][i + 1];
+        se[tt][i + 1] = sw ? te : se[tt][i + 1];
+        ss[tt][i + 1] = sw ? ts : ss[tt][i + 1];
+      }
+    }
+  }
+  float hu[2], hs[2], my_s[2];
+  int he[2], ptr[2], my_e[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    hu[tt] = su[tt][0];
+    hs[tt] = ss[tt][0];
+    he[tt] = se[tt][0];
+    ptr[tt] = 0;
+    my_s[tt] = 0.f;
+    my_e[tt] = 0;
+  }
+  for (int r = 0; r < top_k; ++r) {
+    float M[2];
+    int ew[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) M[tt] = wave_max_f32(hu[tt]);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) ew[tt] = wave_min_i32(hu[tt] == M[tt] ? he[tt] : 0x7fffffff);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int owner = ew[tt] & 63;  // expert e lives in lane e % 64
+      const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hs[tt]), owner));
+      if (lane == owner) {
+        ++ptr[tt];
+        float nu = -INFINITY, ns = 0.f;
+        int ne = 0x7fffffff;
+#pragma unroll
+        for (int j = 1; j < kMaxPerLane; ++j) {
+          nu = (j == ptr[tt]) ? su[tt][j] : nu;
+          ne = (j == ptr[tt]) ? se[tt][j] : ne;
+          ns = (j == ptr[tt]) ? ss[tt][j] : ns;
+        }
+        hu[tt] = nu;
+        he[tt] = ne;
+        hs[tt] = ns;
+      }
+      if (lane == r) {
+        my_s[tt] = sw;
+        my_e[tt] = ew[tt];
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (tt >= nt) break;  // wave-uniform
+    float total = 0.f;
+    for (int r = 0; r < top_k; ++r) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s[tt]), r));
+    if (lane < top_k) {
+      idx_row[tt][lane] = my_e[tt];
+      idx_lds[tt][lane] = my_e[tt];
+      w_row[tt][lane] = total > 0.f ? route_scale * my_s[tt] / total : route_scale / (float)top_k;
+    }
+  }
+}
+
 // Few tokens: logits as a weight-streaming GEMV on the vector ALUs.  One
 // wave per expert reads its fp32 router row once (1 KB per load
 // instruction across the wave, all loads of a 5120-wide row in flight) and

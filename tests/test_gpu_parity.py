@@ -518,3 +518,21 @@ def test_layer_fp8_expert_counts(e, k, tokens):
     inp = make_inputs(cfg, seed=80 + e, device=DEV)
     stats, _, alt = _check_layer(inp)
     print(f"fp8 E={e} k={k} T={tokens}:", stats, "near-tie alternatives", len(alt))
+
+
+@pytest.mark.parametrize("tokens", [1, 3, 5, 6, 8])
+def test_layer_few_tokens_duplicate_router_rows(tokens):
+    """The one-block routing of the few-token paths (tokens 5..8 take two tokens per wave): equal
+    router rows give equal scores, taken lowest index first; the layer matches the oracle."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens)
+    inp = make_inputs(cfg, seed=90 + tokens, device=DEV)
+    inp.router_w[20] = inp.router_w[3]
+    inp.router_w[31] = inp.router_w[3]
+    y, idx, w = gpu_layer(inp)
+    for row in idx.cpu().numpy().tolist():
+        have = [e for e in (3, 20, 31) if e in row]
+        if have:
+            pos = [row.index(e) for e in have]
+            assert have == [3, 20, 31][:len(have)] and pos == list(range(pos[0], pos[0] + len(pos)))
+    stats, _, alt = _check_layer(inp, gpu=(y, idx, w))
+    print(f"T={tokens} duplicate router rows:", stats, "near-tie alternatives", len(alt))
