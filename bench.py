@@ -164,7 +164,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this layer is measured on one MI355X and has no multi-GPU "
-              "path here (see the sharding notes in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+              "path here. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
