@@ -395,11 +395,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
 }
 
 // ---------------------------------------------------------------- pipelined MXFP4 kernel
-// Same tiles as the LDS-tiled kernel (128 rows; 32 gate + 32 up or 64 output
-// columns per column group, four column groups per block), with the operands
-// brought into LDS by gfx950's global-to-LDS loads (16 bytes per lane, no
-// registers) in a multi-stage pipeline, activations and weights kPipe8A - 1
-// and kPipe8B - 1 chunks ahead.  At ~64 rows per expert the routed
+// Tiles of 128 rows, as in the LDS-tiled kernel, or 32 (32 gate + 32 up or 64
+// output columns per column group, four column groups per block), with the
+// operands brought into LDS by gfx950's global-to-LDS loads (16 bytes per
+// lane, no registers) in a multi-stage pipeline, activations and weights
+// SA - 1 and SB - 1 chunks ahead.  At ~64 rows per expert the routed
 // projections read each expert's weights once; registers cannot hold the
 // loads in flight such a stream needs, LDS can.  Per 128-wide K chunk and
 // block: activation tile 128 x 256 B (bf16), weight codes 256 rows x 64 B,
@@ -466,23 +466,42 @@ constexpr int kPipeSStage = 256 * 4;
 // loads, and the waves of K half 0 one 4-byte scale load (weight rows 64 w +
 // lane); the waits count these (pipe8_wait).  (Loads of 4 bytes or less fill
 // 4-byte LDS slots per lane.)
-constexpr int kPipe8LoadsA = 4;
+//
+// Tiles of AR = 128 rows serve many rows per expert.  At a few rows per
+// expert the kernel streams weights with little matrix work per byte: 32-row
+// tiles shrink the activation stages to 8 KB, and with two stages of each
+// operand two blocks fit on a CU.
+constexpr int kPipe8LoadsA = 4;  // activation loads per wave and chunk at 128-row tiles
 constexpr int kPipe8LoadsB = 2;
-constexpr int kPipe8A = 3;  // activation stages
-constexpr int kPipe8B = 3;  // weight stages
-static_assert(kPipe8A * kPipeAStage + kPipe8B * kPipeBStage >= 4 * 32768,
-              "the K-half reduction reuses 4 x 32 KB of the stage pool");
+template <int AR>
+struct Pipe8Cfg {
+  static constexpr int kA = 3;  // activation stages
+  static constexpr int kB = 3;  // weight stages
+};
+template <>
+struct Pipe8Cfg<32> {
+  static constexpr int kA = 2;
+  static constexpr int kB = 3;
+};
+template <int AR>
+constexpr int pipe8_pool_bytes() {
+  return Pipe8Cfg<AR>::kA * AR * 256 + Pipe8Cfg<AR>::kB * (kPipeBStage + kPipeSStage);
+}
+static_assert(pipe8_pool_bytes<128>() >= 4 * 128 * 256 && pipe8_pool_bytes<32>() >= 4 * 32 * 256,
+              "the K-half reduction reuses 4 x AR x 256 B of the stage pool");
 // Each iteration c of the main loop issues the stream with the shorter lead
-// first (activations: chunk c + kPipe8A - 1, weights: chunk c + kPipe8B - 1).
-// At the top of iteration c, chunk c of both streams must have landed: the
-// wait allows as many loads in flight as were issued after the later of the
-// two (la activation and lb weight loads per iteration and wave).  Chunks
-// from the prologue are complete already (it ends with a full wait).
-constexpr bool kPipe8AFirst = kPipe8A <= kPipe8B;
+// first (activations: chunk c + SA - 1, weights: chunk c + SB - 1, with SA
+// and SB stages).  At the top of iteration c, chunk c of both streams must
+// have landed: the wait allows as many loads in flight as were issued after
+// the later of the two (la activation and lb weight loads per iteration and
+// wave).  Chunks from the prologue are complete already (it ends with a full
+// wait).
+template <int SA, int SB>
 constexpr int pipe8_wait(int la, int lb) {
+  constexpr bool kAFirst = SA <= SB;
   const int c = 64;  // any iteration past the prologue
-  const int ja = c - (kPipe8A - 1), jb = c - (kPipe8B - 1);
-  const int oa = kPipe8AFirst ? 0 : 1, ob = 1 - oa;
+  const int ja = c - (SA - 1), jb = c - (SB - 1);
+  const int oa = kAFirst ? 0 : 1, ob = 1 - oa;
   const bool a_later = ja > jb || (ja == jb && oa > ob);
   const int j_last = a_later ? ja : jb, o_last = a_later ? oa : ob;
   int n = 0;
@@ -492,15 +511,20 @@ constexpr int pipe8_wait(int la, int lb) {
   return n;
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p, int n_tiles, int col_blocks) {
+template <bool SWIGLU, int AR>
+__global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kernel(GemmParams p, int n_tiles, int col_blocks) {
+  constexpr int kSA = Pipe8Cfg<AR>::kA, kSB = Pipe8Cfg<AR>::kB;
+  constexpr bool kAFirst = kSA <= kSB;
+  constexpr int kAStage = AR * 256;
+  constexpr int kLoadsA = AR / 32;  // activation loads per wave and chunk at full tiles
+  constexpr int MTMAX = AR / 16;
   // one pool: activation stages, weight-code stages, scale stages (the first
-  // 128 KB also hold the K-half reduction at the end)
-  __shared__ __attribute__((aligned(16))) uint8_t pool[kPipe8A * kPipeAStage + kPipe8B * kPipeBStage + kPipe8B * kPipeSStage];
-  __shared__ int32_t src_rows[128];
-  auto a_lds = [&](int i) { return pool + i * kPipeAStage; };
-  auto b_lds = [&](int i) { return pool + kPipe8A * kPipeAStage + i * kPipeBStage; };
-  auto s_lds = [&](int i) { return pool + kPipe8A * kPipeAStage + kPipe8B * kPipeBStage + i * kPipeSStage; };
+  // AR KB also hold the K-half reduction at the end)
+  __shared__ __attribute__((aligned(16))) uint8_t pool[pipe8_pool_bytes<AR>()];
+  __shared__ int32_t src_rows[AR];
+  auto a_lds = [&](int i) { return pool + i * kAStage; };
+  auto b_lds = [&](int i) { return pool + kSA * kAStage + i * kPipeBStage; };
+  auto s_lds = [&](int i) { return pool + kSA * kAStage + kSB * kPipeBStage + i * kPipeSStage; };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int cg = wave & 3, kh = wave >> 2;
@@ -513,16 +537,16 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
     const GemmTile tl = p.tiles[pb.tile];
     e = tl.e;
     m_begin = tl.m_begin;
-    m_end = min(tl.m_end, tl.m_begin + 128);
+    m_end = min(tl.m_end, tl.m_begin + AR);
   } else {
-    m_begin = pb.tile * 128;
-    m_end = min(m_begin + 128, p.M);
+    m_begin = pb.tile * AR;
+    m_end = min(m_begin + AR, p.M);
   }
   const int rows = m_end - m_begin;
   const int K = p.K, nchunks = K / 128;
   constexpr int CW = tiled_cols_per_wave<SWIGLU>();
   const int n0 = pb.cb * 4 * CW;
-  for (int r = threadIdx.x; r < 128; r += 512) {
+  for (int r = threadIdx.x; r < AR; r += 512) {
     int src = p.gather ? p.gather[m_begin + min(r, rows - 1)] / p.gather_div : m_begin + min(r, rows - 1);
     src_rows[r] = min(max(src, 0), p.a_rows - 1);
   }
@@ -532,11 +556,11 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   // a_rows_run: the tile's rows rounded up to the row tiles the main loop runs
   // (an even number of 16-row tiles), so that every wave issues MT / 2 of them
   // (rows past the tile re-read its last row); the waits count on that
-  const int mt_run = min(2 * ((rows + 31) / 32), 8);
+  const int mt_run = min(2 * ((rows + 31) / 32), MTMAX);
   const int a_rows_run = 16 * mt_run;
-  const uint8_t* a_src[kPipe8LoadsA];
+  const uint8_t* a_src[kLoadsA];
 #pragma unroll
-  for (int t = 0; t < kPipe8LoadsA; ++t) {
+  for (int t = 0; t < kLoadsA; ++t) {
     const int row = 4 * (wave + 8 * t) + (lane >> 4);
     const int piece = (lane & 15) ^ (row & 15);
     a_src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src_rows[row] * p.lda) + 16 * piece;
@@ -565,30 +589,30 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
 
   auto issue_a = [&](int c) {
     const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(a_lds(c % kPipe8A) + 1024 * wave);
+    const uint32_t dst = lds_addr(a_lds(c % kSA) + 1024 * wave);
 #pragma unroll
-    for (int t = 0; t < kPipe8LoadsA; ++t)
+    for (int t = 0; t < kLoadsA; ++t)
       if (4 * (wave + 8 * t) < a_rows_run) load_lds16(a_src[t] + 256 * cc, dst + 8192 * t);  // wave-uniform
   };
   auto issue_b = [&](int c) {
     const int cc = min(c, nchunks - 1);
-    const uint32_t dst = lds_addr(b_lds(c % kPipe8B) + 2048 * wave);
+    const uint32_t dst = lds_addr(b_lds(c % kSB) + 2048 * wave);
 #pragma unroll
     for (int t = 0; t < kPipe8LoadsB; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
-    if (kh == 0) load_lds4(s_src + 4 * cc, lds_addr(s_lds(c % kPipe8B) + 256 * wave));  // wave-uniform
+    if (kh == 0) load_lds4(s_src + 4 * cc, lds_addr(s_lds(c % kSB) + 256 * wave));  // wave-uniform
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[MTMAX][4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < MTMAX; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int m_tiles = (rows + 15) / 16;
 
 #pragma unroll
-  for (int c = 0; c < kPipe8B - 1; ++c) issue_b(c);
+  for (int c = 0; c < kSB - 1; ++c) issue_b(c);
 #pragma unroll
-  for (int c = 0; c < kPipe8A - 1; ++c) issue_a(c);
+  for (int c = 0; c < kSA - 1; ++c) issue_a(c);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   auto run = [&](auto mt_tag) {
@@ -596,8 +620,9 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
     for (int c = 0; c < nchunks; ++c) {
       // MT / 2 activation loads per wave, the weight codes, and for K half 0
       // the scale word
-      constexpr int kWait0 = pipe8_wait(MT / 2, kPipe8LoadsB + 1);
-      constexpr int kWait1 = pipe8_wait(MT / 2, kPipe8LoadsB);
+      constexpr int kWait0 = pipe8_wait<kSA, kSB>(MT / 2, kPipe8LoadsB + 1);
+      constexpr int kWait1 = pipe8_wait<kSA, kSB>(MT / 2, kPipe8LoadsB);
+      static_assert(kWait0 < 64 && kWait1 < 64, "vmcnt holds at most 63");
       if (c > 0) {
         if (kh == 0)
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait0) : "memory");
@@ -605,9 +630,9 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait1) : "memory");
         asm volatile("s_barrier" ::: "memory");
       }
-      const uint8_t* al = a_lds(c % kPipe8A);
-      const uint8_t* bl = b_lds(c % kPipe8B);
-      const uint8_t* sl = s_lds(c % kPipe8B);
+      const uint8_t* al = a_lds(c % kSA);
+      const uint8_t* bl = b_lds(c % kSB);
+      const uint8_t* sl = s_lds(c % kSB);
       uint32_t q[4][2];
       float sc[4];
 #pragma unroll
@@ -625,12 +650,12 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
       };
       bf16x8_t a0[MT], a1[MT];
       read_a(a0, 2 * kh);
-      if constexpr (kPipe8AFirst) {
-        issue_a(c + kPipe8A - 1);
-        issue_b(c + kPipe8B - 1);
+      if constexpr (kAFirst) {
+        issue_a(c + kSA - 1);
+        issue_b(c + kSB - 1);
       } else {
-        issue_b(c + kPipe8B - 1);
-        issue_a(c + kPipe8A - 1);
+        issue_b(c + kSB - 1);
+        issue_a(c + kSA - 1);
       }
       read_a(a1, 2 * kh + 1);
 #pragma unroll
@@ -645,24 +670,28 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
       }
     }
   };
-  if (mt_run <= 2)
+  if constexpr (MTMAX == 2) {
     run(IntC<2>{});
-  else if (mt_run == 4)
-    run(IntC<4>{});
-  else if (mt_run == 6)
-    run(IntC<6>{});
-  else
-    run(IntC<8>{});
+  } else {
+    if (mt_run <= 2)
+      run(IntC<2>{});
+    else if (mt_run == 4)
+      run(IntC<4>{});
+    else if (mt_run == 6)
+      run(IntC<6>{});
+    else
+      run(IntC<8>{});
+  }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // every load landed, LDS free
 
   // the K-half-1 waves hand their sums to the K-half-0 waves through LDS
   // (lane-major: element (m, j, i) of lane l at ((m * 4 + j) * 4 + i) * 256 + 4 l
-  // within the column group's 32 KB)
-  float* red = reinterpret_cast<float*>(pool) + cg * 8192;  // 4 x 32 KB of the pool
-  const int mtr = min(m_tiles, 8);
+  // within the column group's AR x 256 B)
+  float* red = reinterpret_cast<float*>(pool) + cg * (AR * 64);  // 4 x AR x 256 B of the pool
+  const int mtr = min(m_tiles, MTMAX);
   if (kh == 1) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < MTMAX; ++m) {
       if (m >= mtr) break;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -673,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
   __syncthreads();
   if (kh == 1) return;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < MTMAX; ++m) {
     if (m >= mtr) break;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -683,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pipe8_kernel(GemmParams p,
 
   const int n0w = n0 + cg * CW;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < MTMAX; ++m) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * m + 4 * grp + i;
@@ -909,6 +938,11 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_wide_kernel(GemmParams p, 
   }
 }
 
+// MXFP4 weights with K a multiple of 128 at up to this many rows per expert
+// on average: 32-row tiles for the pipelined kernel
+constexpr int kPipeSmallMt = 2;
+constexpr int64_t kPipeSmallAvgRows = 16;
+
 int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined) {
   const bool fp4 = fmt == kWMxfp4;
   const int kTiledRows = 16 * (fmt == kWBf16 ? tiled_m<kWBf16>() : fmt == kWMxfp8 ? tiled_m<kWMxfp8>()
@@ -918,8 +952,8 @@ int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipeli
   // faster than 16-row tiles even at 1-5 rows per expert).  Otherwise rows
   // per group on average decides: 128-row tiles go to the LDS-tiled kernel,
   // which needs enough of them to fill the chip.
-  if (fp4 && k_pipelined) return kTiledRows / 16;
   const int64_t avg = n_groups > 0 ? (n_rows + n_groups - 1) / n_groups : n_rows;
+  if (fp4 && k_pipelined) return avg <= kPipeSmallAvgRows ? kPipeSmallMt : kTiledRows / 16;
   const int64_t tiles = (n_rows + kTiledRows - 1) / kTiledRows;
   return (avg > 16 && tiles >= 16) ? kTiledRows / 16 : 1;
 }
@@ -948,12 +982,24 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
         } else {
           const int col_blocks = (int)g.y;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
-          hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
+          hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
         }
         return;
       }
     }
     hipLaunchKernelGGL((expert_gemm_tiled_kernel<SWIGLU, BF>), g, dim3(256), 0, stream, p);
+  } else if (FP4 && mt == kPipeSmallMt && p.K % 128 == 0) {
+    // 32-row tiles: the down projection runs the 32-row pipelined kernel, two
+    // blocks per CU (one block's start and end overlap the other's stream;
+    // 382 -> 345 us at 64 tokens); the gate/up projection measured slower so
+    // (770 -> 850 us) and keeps the 128-row kernel, one block per CU
+    const int n_tiles = (int)grid.x;
+    const int col_blocks = (p.N + 4 * tiled_cols_per_wave<SWIGLU>() - 1) / (4 * tiled_cols_per_wave<SWIGLU>());
+    const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
+    if constexpr (SWIGLU)
+      hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
+    else
+      hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
   } else {
     hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
   }

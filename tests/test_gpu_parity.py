@@ -273,6 +273,25 @@ def test_layer_many_rows_per_expert(variant):
     print(f"{variant}:", stats, "near-tie alternatives", len(alt))
 
 
+@pytest.mark.parametrize("variant", ["hot_expert", "one_chunk", "two_rows_per_expert"])
+def test_layer_small_tiles(variant):
+    """32-row tiles of the pipelined grouped GEMM (K a multiple of 128, at most 16 rows per expert on average):
+    a hot expert that spans many tiles, K of one 128-wide chunk, and a full-size-like spread of 1-5 rows."""
+    base = CONFIGS["tiny_t8_h512_e32"]
+    cfg = {"hot_expert": base.with_(tokens=400, n_experts=256, top_k=4, bias="zipf", zipf_alpha=1.0),
+           "one_chunk": base.with_(tokens=50, n_experts=64, hidden=128, inter=128, shared_inter=128),
+           "two_rows_per_expert": base.with_(tokens=64, n_experts=192, hidden=1024, inter=384,
+                                             shared_inter=256)}[variant]
+    inp = make_inputs(cfg, seed=31, device=DEV)
+    gpu = gpu_layer(inp)
+    load = np.bincount(gpu[1].cpu().numpy().reshape(-1), minlength=cfg.n_experts)
+    assert load.sum() / max(1, np.count_nonzero(load)) <= 16
+    if variant == "hot_expert":
+        assert load.max() > 64, load.max()  # three or more tiles for one expert
+    stats, _, alt = _check_layer(inp, gpu=gpu)
+    print(f"{variant}: max load {load.max()}", stats, "near-tie alternatives", len(alt))
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7, 8, 16])
 def test_layer_top_k_range(k):
     inp = make_inputs(CONFIGS["tiny_t8_h512_e32"].with_(tokens=12, top_k=k), seed=3, device=DEV)
