@@ -938,6 +938,145 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_wide_kernel(GemmParams p, 
   }
 }
 
+// ---------------------------------------------------------------- dense bf16 pipelined kernel
+// The shared expert at many tokens: a dense bf16 GEMM, rows [0, M) of A
+// against one bf16 weight matrix.  Tiles of 128 rows x 256 weight rows (32
+// gate + 32 up or 64 output columns per column group, four column groups),
+// eight waves: column group w & 3, row half w >> 2 (64 rows, 4 x 4 MFMA
+// tiles per wave).  Both operands reach LDS through the global-to-LDS loads
+// in chunks of 32 K (64 bytes per row), DS stages ahead; every row of both
+// stages keeps its 16-byte piece q in slot q ^ ((r >> 2) & 3), so the 16
+// lanes reading one MFMA operand column hit 16 different bank groups.  Per
+// chunk each wave issues one activation load (16 rows) and two weight loads
+// (32 rows), whatever the tile's size (rows past M and columns past N re-read
+// the last valid ones, results unused), so the waits are constants.
+template <int DS>
+constexpr int dense_pool_bytes() {
+  return DS * (128 + 256) * 64;
+}
+template <bool SWIGLU, int DS>
+__global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel(GemmParams p, int n_tiles,
+                                                                                  int col_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS>()];
+  auto a_lds = [&](int i) { return pool + i * (128 * 64); };
+  auto b_lds = [&](int i) { return pool + DS * (128 * 64) + i * (256 * 64); };
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int cg = wave & 3, mh = wave >> 2;
+
+  const PipeBlock pb = pipe_block(col_blocks);
+  if (pb.tile >= n_tiles) return;
+  const int m_begin = pb.tile * 128;
+  const int rows = min(128, p.M - m_begin);
+  const int K = p.K, nchunks = K / 32;
+  constexpr int CW = tiled_cols_per_wave<SWIGLU>();
+  const int n0 = pb.cb * 4 * CW;
+
+  // load sources: 16 rows x 64 bytes per instruction, lane l fills slot
+  // l & 3 of row l >> 2 of its group
+  const int lrow = lane >> 2;
+  const uint8_t* a_src;
+  {
+    const int r = 16 * wave + lrow;
+    const int q = (lane & 3) ^ ((r >> 2) & 3);
+    const int src = min(m_begin + r, p.M - 1);
+    a_src = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src * p.lda) + 16 * q;
+  }
+  auto brow_col = [&](int brow) {
+    int c;
+    if constexpr (SWIGLU) {
+      const int w = brow >> 6, j = (brow >> 4) & 3, n = brow & 15;
+      const int gc = min(n0 + 32 * w + 16 * (j & 1) + n, p.N - 1);
+      c = gc + (j >> 1) * p.b_row_second;
+    } else {
+      c = min(n0 + brow, p.N - 1);
+    }
+    return (int64_t)c;
+  };
+  const uint8_t* b_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int brow = 16 * (2 * wave + t) + lrow;
+    const int q = (lane & 3) ^ ((brow >> 2) & 3);
+    b_src[t] = reinterpret_cast<const uint8_t*>(p.bh + brow_col(brow) * K) + 16 * q;
+  }
+  auto issue = [&](int c) {
+    const int cc = min(c, nchunks - 1);
+    load_lds16(a_src + 64 * cc, lds_addr(a_lds(c % DS) + 1024 * wave));
+    const uint32_t dst = lds_addr(b_lds(c % DS) + 2048 * wave);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int c = 0; c < DS - 1; ++c) issue(c);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // at the top of iteration c, chunk c was issued DS - 1 iterations earlier;
+  // the loads of the DS - 2 iterations since then may stay in flight
+  constexpr int kWait = (DS - 2) * 3;
+  for (int c = 0; c < nchunks; ++c) {
+    if (c > 0) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait) : "memory");
+      asm volatile("s_barrier" ::: "memory");
+    }
+    const uint8_t* al = a_lds(c % DS);
+    const uint8_t* bl = b_lds(c % DS);
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int br = 64 * cg + 16 * j + col;
+      b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ar = 64 * mh + 16 * m + col;
+      a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
+    }
+    issue(c + DS - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the block ends
+
+  const int n0w = n0 + cg * CW;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 64 * mh + 16 * m + 4 * grp + i;
+      if (r < rows) {
+        if constexpr (SWIGLU) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int n = n0w + 16 * jj + col;
+            if (n < p.N)
+              p.C[(int64_t)(m_begin + r) * p.ldc + n] =
+                  f32_to_bf16(clamped_swiglu(acc[m][jj][i], acc[m][jj + 2][i], p.limit));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0w + 16 * j + col;
+            if (n < p.N) p.C[(int64_t)(m_begin + r) * p.ldc + n] = f32_to_bf16(acc[m][j][i]);
+          }
+        }
+      }
+    }
+  }
+}
+// three stages, two blocks per CU (measured against four stages, one block
+// per CU: 274 -> 252 us for the gate/up projection at 4096 tokens)
+constexpr int kDenseStages = 3;
+
 // MXFP4 weights with K a multiple of 128 at up to this many rows per expert
 // on average: 32-row tiles for the pipelined kernel
 constexpr int kPipeSmallMt = 2;
@@ -984,6 +1123,16 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
           hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
         }
+        return;
+      }
+    }
+    if constexpr (BF == kWBf16) {
+      if (!p.tiles && !p.gather) {  // one dense bf16 matrix (the shared expert): the pipelined dense kernel
+        const int n_tiles = (p.M + 127) / 128;
+        const int col_blocks = (int)g.y;
+        const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
+        hipLaunchKernelGGL((expert_gemm_dense_kernel<SWIGLU, kDenseStages>), g1, dim3(512), 0, stream, p, n_tiles,
+                           col_blocks);
         return;
       }
     }

@@ -259,14 +259,19 @@ def test_layer_one_two_tokens(tokens, variant):
     print(f"T={tokens} {variant}:", stats, "near-tie alternatives", len(alt))
 
 
-@pytest.mark.parametrize("variant", ["two_tiles_per_expert", "three_chunks", "ragged_k_fallback", "down_one_chunk"])
+@pytest.mark.parametrize("variant", ["two_tiles_per_expert", "three_chunks", "ragged_k_fallback", "down_one_chunk",
+                                     "dense_shared_ragged", "dense_shared_one_chunk"])
 def test_layer_many_rows_per_expert(variant):
-    """Tiles of up to 128 rows (the pipelined grouped GEMM when K is a multiple of 128), sampled rows."""
+    """Tiles of up to 128 rows (the pipelined grouped GEMM when K is a multiple of 128), sampled rows; from 1024
+    tokens the shared expert takes the dense pipelined kernel (ragged last row tile and column block)."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"two_tiles_per_expert": base.with_(tokens=1024),             # ~192 rows per expert
            "three_chunks": base.with_(tokens=600, n_experts=8, hidden=384, inter=128, shared_inter=256),
            "ragged_k_fallback": base.with_(tokens=700, n_experts=16, hidden=160, inter=96, shared_inter=224),
-           "down_one_chunk": base.with_(tokens=500, n_experts=8, top_k=3, inter=128, shared_inter=128)}[variant]
+           "down_one_chunk": base.with_(tokens=500, n_experts=8, top_k=3, inter=128, shared_inter=128),
+           "dense_shared_ragged": base.with_(tokens=1100, n_experts=8, hidden=384, inter=128, shared_inter=96),
+           "dense_shared_one_chunk": base.with_(tokens=1031, n_experts=8, hidden=32, inter=32,
+                                                shared_inter=32)}[variant]
     inp = make_inputs(cfg, seed=21, device=DEV)
     gpu = gpu_layer(inp)
     stats, _, alt = _check_layer(inp, tokens=_sample(cfg.tokens, 40, seed=5), gpu=gpu)
