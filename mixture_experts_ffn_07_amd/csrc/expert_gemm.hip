@@ -950,13 +950,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_wide_kernel(GemmParams p, 
 // chunk each wave issues one activation load (16 rows) and two weight loads
 // (32 rows), whatever the tile's size (rows past M and columns past N re-read
 // the last valid ones, results unused), so the waits are constants.
+// F32: fp32 outputs in slices (blockIdx.y = z * k_slices + k-part): slice z
+// multiplies the weight matrix bh + z * b_slice_stride over the k-part's range
+// of K chunks and writes Cf + slice * c_slice_stride (the router's three-term
+// split logits, summed later).
 template <int DS>
 constexpr int dense_pool_bytes() {
   return DS * (128 + 256) * 64;
 }
-template <bool SWIGLU, int DS>
+template <bool SWIGLU, int DS, bool F32 = false>
 __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel(GemmParams p, int n_tiles,
                                                                                   int col_blocks) {
+  static_assert(!(F32 && SWIGLU), "fp32 slices are plain products");
   __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS>()];
   auto a_lds = [&](int i) { return pool + i * (128 * 64); };
   auto b_lds = [&](int i) { return pool + DS * (128 * 64) + i * (256 * 64); };
@@ -968,7 +973,17 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
   if (pb.tile >= n_tiles) return;
   const int m_begin = pb.tile * 128;
   const int rows = min(128, p.M - m_begin);
-  const int K = p.K, nchunks = K / 32;
+  const int K = p.K;
+  int c_lo = 0, nchunks = K / 32;
+  const uint16_t* bh = p.bh;
+  if constexpr (F32) {
+    // the host sizes k_slices so that every k-part holds at least one chunk
+    const int z = (int)blockIdx.y / p.k_slices, kp = (int)blockIdx.y % p.k_slices;
+    const int per = (nchunks + p.k_slices - 1) / p.k_slices;
+    c_lo = kp * per;
+    nchunks = min(nchunks - c_lo, per);
+    bh += z * p.b_slice_stride;
+  }
   constexpr int CW = tiled_cols_per_wave<SWIGLU>();
   const int n0 = pb.cb * 4 * CW;
 
@@ -980,7 +995,7 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
     const int r = 16 * wave + lrow;
     const int q = (lane & 3) ^ ((r >> 2) & 3);
     const int src = min(m_begin + r, p.M - 1);
-    a_src = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src * p.lda) + 16 * q;
+    a_src = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src * p.lda) + 64 * c_lo + 16 * q;
   }
   auto brow_col = [&](int brow) {
     int c;
@@ -998,7 +1013,7 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
   for (int t = 0; t < 2; ++t) {
     const int brow = 16 * (2 * wave + t) + lrow;
     const int q = (lane & 3) ^ ((brow >> 2) & 3);
-    b_src[t] = reinterpret_cast<const uint8_t*>(p.bh + brow_col(brow) * K) + 16 * q;
+    b_src[t] = reinterpret_cast<const uint8_t*>(bh + brow_col(brow) * K) + 64 * c_lo + 16 * q;
   }
   auto issue = [&](int c) {
     const int cc = min(c, nchunks - 1);
@@ -1061,6 +1076,13 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
             if (n < p.N)
               p.C[(int64_t)(m_begin + r) * p.ldc + n] =
                   f32_to_bf16(clamped_swiglu(acc[m][jj][i], acc[m][jj + 2][i], p.limit));
+          }
+        } else if constexpr (F32) {
+          float* cf = p.Cf + (int64_t)blockIdx.y * p.c_slice_stride + (int64_t)(m_begin + r) * p.ldc;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0w + 16 * j + col;
+            if (n < p.N) cf[n] = acc[m][j][i];
           }
         } else {
 #pragma unroll
@@ -1152,6 +1174,15 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
   } else {
     hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
   }
+}
+
+hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream) {
+  const int n_tiles = (p.M + 127) / 128;
+  const int col_blocks = (p.N + 255) / 256;
+  const dim3 g((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks), (unsigned)slices);
+  hipLaunchKernelGGL((expert_gemm_dense_kernel<false, kDenseStages, true>), g, dim3(512), 0, stream, p, n_tiles,
+                     col_blocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt, int mt, int64_t grid_tiles,

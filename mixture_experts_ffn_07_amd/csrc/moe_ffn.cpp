@@ -138,7 +138,7 @@ struct WsLayout {
   bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
                               // down; routed down + combine
   bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
-  Region x_norm, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
+  Region x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh;
   size_t total = 0;
 };
@@ -167,6 +167,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     L.down_combine = L.down_combine && !L.splitk_dn;
     L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter, fp8);
     L.router.ksplit = 1;  // full logits from the GEMV router
+    L.router.dense_kslices = 0;
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
     L.bm = 16 * L.gemm_mt;
@@ -196,6 +197,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     off += (bytes + 255) & ~size_t(255);
   };
   take(L.x_norm, sizeof(uint16_t) * (size_t)tokens * c->hidden);
+  take(L.w3, moe::router_w3_bytes(L.router, E, c->hidden));
   take(L.logits, sizeof(float) * (size_t)L.router.ksplit * tokens * E);
   take(L.scores, L.route_small ? sizeof(float) * 2 * (size_t)tokens * E : 0);
   take(L.xmx, L.route_small ? (size_t)tokens * moe::mx_row_bytes(c->hidden) : 0);
@@ -247,7 +249,8 @@ moe_status run_route(const moe_config* c, const moe_weights* w, const uint16_t* 
   hipError_t err = L.decode
                        ? moe::launch_router_gemv(x, w->router_w, part, (int)T, c->n_experts, c->hidden, nullptr,
                                                  nullptr, st)
-                       : moe::launch_router_logits(L.router, x, w->router_w, part, (int)T, c->n_experts, c->hidden, st);
+                       : moe::launch_router_logits(L.router, x, w->router_w, part, (int)T, c->n_experts, c->hidden,
+                                                   at<uint16_t>(ws, L.w3), st);
   if (err == hipSuccess) err = mark(tl, "router_logits", st);
   if (err != hipSuccess) return fail_hip(err, "router logits launch");
   err = moe::launch_router_topk(part, L.router.ksplit, w->router_bias, (int)T, c->n_experts, c->top_k,

@@ -9,14 +9,20 @@ namespace moe {
 // ---------------------------------------------------------------- router
 struct RouterPlan {
   int mt;                // 16-token row tiles per block (1 or 4)
-  int ksplit;            // number of K ranges, each a whole number of 128-wide chunks
+  int ksplit;            // number of partial logit matrices the top-k adds
   int chunks_per_split;  // 128-wide K chunks per range
+  // > 0: W_r is split into three bf16 matrices (hi, mid, lo) in the
+  // workspace and the dense pipelined GEMM runs each over this many K ranges
+  // (ksplit = 3 * dense_kslices); 0: router_logits_kernel
+  int dense_kslices;
 };
 RouterPlan router_plan(int64_t tokens, int n_experts, int hidden);
+// workspace bytes for the split weights (0 unless plan.dense_kslices > 0)
+size_t router_w3_bytes(const RouterPlan& plan, int n_experts, int hidden);
 
-// partial logits [ksplit][T][E] fp32
+// partial logits [ksplit][T][E] fp32; w3: router_w3_bytes of workspace
 hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const float* router_w, float* part,
-                                int tokens, int n_experts, int hidden, hipStream_t stream);
+                                int tokens, int n_experts, int hidden, uint16_t* w3, hipStream_t stream);
 // few tokens: full fp32 logits [T][E] by a weight-streaming GEMV (logits optional);
 // with `scores` non-null also s = sqrtsoftplus(l) at scores[t][e] and
 // u = s + bias[e] at scores[T + t][e] (bias optional)
@@ -90,6 +96,12 @@ struct GemmParams {
   uint16_t* C;
   int64_t ldc;
   float limit;
+  // fp32 slices of the dense kernel (launch_dense_f32): slice s = z * k_slices
+  // + k-part, weights bh + z * b_slice_stride, output Cf + s * c_slice_stride
+  float* Cf;
+  int k_slices;
+  int64_t b_slice_stride;
+  int64_t c_slice_stride;
 };
 // rows per tile / 16 for the grouped GEMM (MXFP4, MXFP8 or bf16 weights);
 // k_pipelined: every K of the problem is a multiple of 128
@@ -98,6 +110,8 @@ enum WeightFormat : int { kWBf16 = 0, kWMxfp4 = 1, kWMxfp8 = 2 };
 int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined);
 hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt, int mt, int64_t grid_tiles,
                               hipStream_t stream);
+// dense bf16 rows [0, M) of A against `slices` weight slices, fp32 outputs (see GemmParams)
+hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream);
 
 // Few-token (decode) projections: up to two problems in one launch.
 struct GemvProblem {

@@ -141,8 +141,48 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
                 tile_count);
 }
 
+// W_r [E][H] fp32 -> three bf16 matrices [3][E][H] with hi + mid + lo == w
+// exactly (the same split as router_logits_kernel's registers).
+__global__ __launch_bounds__(256) void router_split3_kernel(const float* __restrict__ wr, uint16_t* __restrict__ w3,
+                                                            int64_t n) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float v = wr[i];
+    const uint16_t h = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h);
+    const uint16_t m = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(m);
+    w3[i] = h;
+    w3[n + i] = m;
+    w3[2 * n + i] = f32_to_bf16(r2);
+  }
+}
+
+// From this many tokens the split weights go through the dense pipelined
+// GEMM with 128-token tiles (4096 tokens: logits 180 -> 81 us, the top-k over
+// twelve partials 19 -> 37 us; 16384 tokens: 269 + 18 -> 140 + 23 us).
+constexpr int64_t kDenseRouterMinTokens = 1024;
+
+size_t router_w3_bytes(const RouterPlan& plan, int n_experts, int hidden) {
+  return plan.dense_kslices > 0 ? sizeof(uint16_t) * 3 * (size_t)n_experts * hidden : 0;
+}
+
 RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
   RouterPlan p;
+  p.dense_kslices = 0;
+  if (tokens >= kDenseRouterMinTokens) {
+    // three weight slices x K ranges: aim for ~768 blocks of 128 tokens x 256 experts
+    const int64_t per_slice = (tokens + 127) / 128 * ((n_experts + 255) / 256);
+    const int nch = hidden / 32;
+    int64_t ks = (768 + 3 * per_slice - 1) / (3 * per_slice);
+    ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+    if (ks > nch) ks = nch;
+    const int per = (int)((nch + ks - 1) / ks);
+    p.dense_kslices = (nch + per - 1) / per;  // every K range non-empty
+    p.ksplit = 3 * p.dense_kslices;
+    p.mt = 4;
+    p.chunks_per_split = 0;
+    return p;
+  }
   // 64-token tiles from 256 tokens; below that 16-token tiles give more
   // blocks (64 tokens: 32 -> 24 us)
   p.mt = tokens >= 256 ? 4 : 1;
@@ -159,7 +199,27 @@ RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
 }
 
 hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const float* router_w, float* part,
-                                int tokens, int n_experts, int hidden, hipStream_t stream) {
+                                int tokens, int n_experts, int hidden, uint16_t* w3, hipStream_t stream) {
+  if (plan.dense_kslices > 0) {
+    const int64_t n = (int64_t)n_experts * hidden;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(router_split3_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream,
+                       router_w, w3, n);
+    GemmParams q{};
+    q.M = tokens;
+    q.A = x;
+    q.lda = hidden;
+    q.a_rows = tokens;
+    q.K = hidden;
+    q.bh = w3;
+    q.N = n_experts;
+    q.ldc = n_experts;
+    q.Cf = part;
+    q.k_slices = plan.dense_kslices;
+    q.b_slice_stride = n;
+    q.c_slice_stride = (int64_t)tokens * n_experts;
+    return launch_dense_f32(q, 3 * plan.dense_kslices, stream);
+  }
   dim3 grid((tokens + 16 * plan.mt - 1) / (16 * plan.mt), (n_experts + 63) / 64, plan.ksplit);
   if (plan.mt == 4)
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, stream, x, router_w, part, tokens, n_experts,

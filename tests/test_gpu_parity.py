@@ -63,8 +63,11 @@ def test_route_full_size(name):
     print(f"{name}: near-tie alternatives {len(alt)}, oracle gaps < 1e-6: {(ref['gap'] < TIE_TOL).sum()}")
 
 
-def test_route_exact_ties_resolve_to_lowest_index():
-    cfg = CONFIGS["decode_t64_h5120_e384"]
+@pytest.mark.parametrize("tokens", [64, 1030])
+def test_route_exact_ties_resolve_to_lowest_index(tokens):
+    """All router rows equal: every logit ties exactly (the MFMA router below 1024 tokens, the split-weight dense
+    GEMM from 1024)."""
+    cfg = CONFIGS["decode_t64_h5120_e384"].with_(tokens=tokens)
     x, wr, _ = make_router_inputs(cfg, seed=1, device=DEV)
     wr[:] = wr[7]  # every expert has the same router row: all logits tie exactly
     idx, w, gap = gpu_route(cfg, x, wr, None)
@@ -76,8 +79,9 @@ def test_route_exact_ties_resolve_to_lowest_index():
     assert torch.all(idx.cpu() == torch.arange(cfg.top_k, dtype=torch.int32)[None, :])
 
 
-def test_route_duplicate_rows_tie():
-    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=256)
+@pytest.mark.parametrize("tokens", [256, 1500])
+def test_route_duplicate_rows_tie(tokens):
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens)
     x, wr, _ = make_router_inputs(cfg, seed=3, device=DEV)
     wr[20] = wr[3]
     wr[31] = wr[3]
