@@ -1185,6 +1185,57 @@ hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream)
   return hipGetLastError();
 }
 
+// Sum of fp32 K slices in slice order, then clamp-SwiGLU of (gate column n,
+// up column n + n_out) or the plain sum, rounded to bf16.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, int slices,
+                                                        int64_t slice_stride, int rows, int n_out, int ld_part,
+                                                        float limit, uint16_t* __restrict__ C, int64_t ldc) {
+  const int64_t total = (int64_t)rows * n_out;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int r = (int)(i / n_out), n = (int)(i % n_out);
+    const float* src = part + (int64_t)r * ld_part + n;
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < slices; ++s) {
+      g += src[s * slice_stride];
+      if constexpr (SWIGLU) u += src[s * slice_stride + n_out];
+    }
+    C[(int64_t)r * ldc + n] = f32_to_bf16(SWIGLU ? clamped_swiglu(g, u, limit) : g);
+  }
+}
+
+int dense_k_slices(int M, int n_rows, int K) {
+  const int64_t blocks = (int64_t)((M + 127) / 128) * ((n_rows + 255) / 256);
+  const int nch = K / 32;
+  int64_t ks = (640 + blocks - 1) / blocks;
+  ks = ks < 1 ? 1 : ks > 16 ? 16 : ks;
+  if (ks > nch) ks = nch;
+  const int per = (int)((nch + ks - 1) / ks);
+  return (nch + per - 1) / per;  // every K range non-empty
+}
+
+hipError_t launch_dense_sliced(const GemmParams& p, bool swiglu, int k_slices, float* part, hipStream_t stream) {
+  GemmParams q = p;
+  q.N = swiglu ? 2 * p.N : p.N;  // weight rows: gate rows, then up rows (b_row_second == N)
+  q.ldc = q.N;
+  q.Cf = part;
+  q.k_slices = k_slices;
+  q.b_slice_stride = 0;
+  q.c_slice_stride = (int64_t)p.M * q.N;
+  hipError_t err = launch_dense_f32(q, k_slices, stream);
+  if (err != hipSuccess) return err;
+  const int64_t total = (int64_t)p.M * p.N;
+  const int64_t blocks = (total + 255) / 256;
+  const dim3 g((unsigned)(blocks < 4096 ? blocks : 4096));
+  if (swiglu)
+    hipLaunchKernelGGL(slice_sum_kernel<true>, g, dim3(256), 0, stream, part, k_slices, q.c_slice_stride, p.M, p.N,
+                       q.N, p.limit, p.C, p.ldc);
+  else
+    hipLaunchKernelGGL(slice_sum_kernel<false>, g, dim3(256), 0, stream, part, k_slices, q.c_slice_stride, p.M, p.N,
+                       q.N, p.limit, p.C, p.ldc);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt, int mt, int64_t grid_tiles,
                               hipStream_t stream) {
   dim3 grid((unsigned)grid_tiles, (unsigned)(p.N / 16));

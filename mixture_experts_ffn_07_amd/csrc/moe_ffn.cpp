@@ -129,6 +129,8 @@ struct WsLayout {
   bool decode = false;  // few tokens: GEMV router, fused routing, weight-streaming projections
   int bm = 16;          // rows per routed GEMM tile
   int gemm_mt = 1, shared_mt = 1;
+  // shared expert at 128..1023 tokens: the dense kernel over K slices (0: off)
+  int shared_ks_gu = 0, shared_ks_dn = 0;
   int64_t max_tiles = 0, shared_tiles = 0;
   bool route_small = false;   // decode with T * k <= 64: scores from the router GEMV, one-block routing
   bool down_combine = false;  // decode: routed down projection with the combine folded in
@@ -139,7 +141,7 @@ struct WsLayout {
                               // down; routed down + combine
   bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
   Region x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
-      y_slot, h_sh, y_sh;
+      y_slot, h_sh, y_sh, sh_part;
   size_t total = 0;
 };
 
@@ -189,6 +191,13 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     L.norm_in_router = L.stream4 && moe::router_norm_gemv_supported((int)tokens, c->hidden);
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
+  if (c->n_shared == 1 && !L.decode && tokens >= 128 && tokens < 1024) {
+    // 16-row tiles would re-read the shared weights once per tile (320
+    // tokens: 184 + 114 -> 101 + 75 us); below 128 tokens the slices are too
+    // short and their partial sums cost more (64 tokens: 57 + 31 -> 89 + 62 us)
+    L.shared_ks_gu = moe::dense_k_slices((int)tokens, 2 * c->shared_inter, c->hidden);
+    L.shared_ks_dn = moe::dense_k_slices((int)tokens, c->hidden, c->shared_inter);
+  }
   const int64_t nchunks = moe::permute_chunks(n);
   size_t off = 0;
   auto take = [&](Region& r, size_t bytes) {
@@ -217,6 +226,10 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
   take(L.y_slot, sizeof(uint16_t) * n * c->hidden);
   const int64_t is = c->n_shared ? c->shared_inter : 0;
   take(L.h_sh, sizeof(uint16_t) * tokens * is);
+  {
+    const size_t gu = (size_t)L.shared_ks_gu * tokens * 2 * is, dn = (size_t)L.shared_ks_dn * tokens * c->hidden;
+    take(L.sh_part, sizeof(float) * (gu > dn ? gu : dn));
+  }
   take(L.y_sh, sizeof(uint16_t) * (c->n_shared ? tokens * c->hidden : 0));
   L.total = off;
   return L;
@@ -719,7 +732,9 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     q.C = hs;
     q.ldc = Is;
     q.limit = c->swiglu_limit;
-    err = moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
+    float* sh_part = at<float>(ws, L.sh_part);
+    err = L.shared_ks_gu ? moe::launch_dense_sliced(q, true, L.shared_ks_gu, sh_part, st)
+                         : moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
     q.A = hs;
@@ -732,7 +747,8 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     q.N = H;
     q.C = y_shared;
     q.ldc = H;
-    err = moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
+    err = L.shared_ks_dn ? moe::launch_dense_sliced(q, false, L.shared_ks_dn, sh_part, st)
+                         : moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_down", st);
   if (err != hipSuccess) return fail_hip(err, "shared down launch");
   }

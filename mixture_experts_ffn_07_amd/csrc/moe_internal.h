@@ -112,6 +112,11 @@ hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt
                               hipStream_t stream);
 // dense bf16 rows [0, M) of A against `slices` weight slices, fp32 outputs (see GemmParams)
 hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream);
+// One dense bf16 matrix (no tiles, no gather) split over K: k_slices fp32
+// partial products into `part` ([k_slices][M][N or 2N] floats), then their sum
+// (and clamp-SwiGLU with the up rows at b_row_second == N) to C in bf16.
+int dense_k_slices(int M, int n_rows, int K);
+hipError_t launch_dense_sliced(const GemmParams& p, bool swiglu, int k_slices, float* part, hipStream_t stream);
 
 // Few-token (decode) projections: up to two problems in one launch.
 struct GemvProblem {

@@ -264,10 +264,12 @@ def test_layer_one_two_tokens(tokens, variant):
 
 
 @pytest.mark.parametrize("variant", ["two_tiles_per_expert", "three_chunks", "ragged_k_fallback", "down_one_chunk",
-                                     "dense_shared_ragged", "dense_shared_one_chunk"])
+                                     "dense_shared_ragged", "dense_shared_one_chunk", "sliced_shared_t128",
+                                     "sliced_shared_t1023"])
 def test_layer_many_rows_per_expert(variant):
     """Tiles of up to 128 rows (the pipelined grouped GEMM when K is a multiple of 128), sampled rows; from 1024
-    tokens the shared expert takes the dense pipelined kernel (ragged last row tile and column block)."""
+    tokens the shared expert takes the dense pipelined kernel (ragged last row tile and column block), from 128 to
+    1023 tokens the same kernel over K slices plus their sum (one-chunk slices, fewer weight rows than a block)."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"two_tiles_per_expert": base.with_(tokens=1024),             # ~192 rows per expert
            "three_chunks": base.with_(tokens=600, n_experts=8, hidden=384, inter=128, shared_inter=256),
@@ -275,7 +277,10 @@ def test_layer_many_rows_per_expert(variant):
            "down_one_chunk": base.with_(tokens=500, n_experts=8, top_k=3, inter=128, shared_inter=128),
            "dense_shared_ragged": base.with_(tokens=1100, n_experts=8, hidden=384, inter=128, shared_inter=96),
            "dense_shared_one_chunk": base.with_(tokens=1031, n_experts=8, hidden=32, inter=32,
-                                                shared_inter=32)}[variant]
+                                                shared_inter=32),
+           "sliced_shared_t128": base.with_(tokens=128, n_experts=8, hidden=352, inter=128, shared_inter=96),
+           "sliced_shared_t1023": base.with_(tokens=1023, n_experts=16, hidden=256, inter=128,
+                                             shared_inter=160)}[variant]
     inp = make_inputs(cfg, seed=21, device=DEV)
     gpu = gpu_layer(inp)
     stats, _, alt = _check_layer(inp, tokens=_sample(cfg.tokens, 40, seed=5), gpu=gpu)
