@@ -1172,6 +1172,12 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     else
       hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
   } else {
+    if constexpr (BF == kWBf16) {
+      if (mt == 2) {  // 32-row tiles (the shared expert at 17..127 tokens)
+        hipLaunchKernelGGL((expert_gemm_kernel<2, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
+        return;
+      }
+    }
     hipLaunchKernelGGL((expert_gemm_kernel<1, SWIGLU, BF>), grid, dim3(256), 0, stream, p);
   }
 }

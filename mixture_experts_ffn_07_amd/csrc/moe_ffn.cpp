@@ -153,6 +153,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
   L.fmt = c->expert_format == 1 ? moe::kWMxfp8 : moe::kWMxfp4;
   L.gemm_mt = moe::expert_gemm_mt(n, (int)(n < E ? n : E), L.fmt, c->hidden % 128 == 0 && c->inter % 128 == 0);
   L.shared_mt = moe::expert_gemm_mt(tokens, 1, moe::kWBf16, false);
+  if (L.shared_mt == 1 && tokens > 16) L.shared_mt = 2;  // 32-row tiles: the weights read half as often
   const int k_fp4 = c->hidden > c->inter ? c->hidden : c->inter;
   const int k_bf16 = c->n_shared ? (c->hidden > c->shared_inter ? c->hidden : c->shared_inter) : 0;
   const bool fp8 = L.fmt == moe::kWMxfp8;
