@@ -116,9 +116,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           float* __restrict__ w_out, float* __restrict__ gap_out) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= tokens) return;
-  topk_token<MPL>(part + (size_t)t * n_experts, ksplit, (int64_t)tokens * n_experts, bias, n_experts, top_k,
-                  route_scale, idx_out + (size_t)t * top_k, w_out + (size_t)t * top_k,
-                  gap_out ? gap_out + t : nullptr, nullptr);
+  constexpr int G = MPL <= 4 ? 8 : MPL <= 8 ? 4 : 2;
+  topk_token<MPL, false, G>(part + (size_t)t * n_experts, ksplit, (int64_t)tokens * n_experts, bias, n_experts,
+                            top_k, route_scale, idx_out + (size_t)t * top_k, w_out + (size_t)t * top_k,
+                            gap_out ? gap_out + t : nullptr, nullptr);
 }
 
 // Few tokens (T*k <= 1024): top-k of every token, then the permutation and

@@ -31,7 +31,8 @@ __device__ __forceinline__ bool ranks_above(float u, int e, float bu, int be) {
 // (and idx_lds when non-null); lane 0 writes *gap_out when non-null.
 // With FROM_SCORES, `part` holds the scores s and `sel` the selection scores
 // u of this token (computed by the router kernel) and ksplit/bias are unused.
-template <int kMaxPerLane, bool FROM_SCORES = false>  // ceil(n_experts / 64) rounded up; at most 16
+// G: partials whose loads issue together (1 where registers are short).
+template <int kMaxPerLane, bool FROM_SCORES = false, int G = 1>  // ceil(n_experts / 64) rounded up; at most 16
 __device__ __forceinline__ void topk_token(const float* __restrict__ part, int ksplit, int64_t part_stride,
                                            const float* __restrict__ bias, int n_experts, int top_k,
                                            float route_scale, int32_t* __restrict__ idx_row,
@@ -54,14 +55,24 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
       u[j] = ((valid >> j) & 1u) && uu == uu ? uu : -INFINITY;
     }
   } else {
-  // Partial sums, z in order.  The loads of one z are unconditional (expert
-  // index clamped into range; unused slots are dropped below), so they all
-  // issue before the first wait.
+  // Partial sums, z in order.  The loads of G partials at a time (expert
+  // index clamped into range; unused slots are dropped below) all issue
+  // before the first wait: the partials were just written, often through
+  // another XCD's L2, and one round trip per partial would dominate.
   const int nj = (n_experts + 63) / 64;
-  for (int zz = 0; zz < ksplit; ++zz) {
+  for (int z0 = 0; z0 < ksplit; z0 += G) {
+    float v[G][kMaxPerLane];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j)
-      if (j < nj) s[j] += part[zz * part_stride + min(lane + 64 * j, n_experts - 1)];
+    for (int dz = 0; dz < G; ++dz)
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j)
+        v[dz][j] = (z0 + dz < ksplit && j < nj) ? part[(z0 + dz) * part_stride + min(lane + 64 * j, n_experts - 1)]
+                                                : 0.f;
+#pragma unroll
+    for (int dz = 0; dz < G; ++dz)
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j)
+        if (z0 + dz < ksplit) s[j] += v[dz][j];
   }
   // u holds the bias until the scores are known
 #pragma unroll
