@@ -1,8 +1,8 @@
 // Grouped expert GEMMs of the MoE FFN layer on gfx950 matrix cores.
 //
 // One kernel template serves the routed experts (MXFP4 weights: E2M1 codes
-// with an E8M0 scale per 32 elements, Strata DEEPSEEK41 notes: "the experts
-// as MXFP4"; or MXFP8: E4M3 codes, float8_e4m3fn in the MAX API's
+// with an E8M0 scale per 32 elements, the routed experts' format in the Strata
+// DEEPSEEK41 notes; or MXFP8: E4M3 codes, float8_e4m3fn in the MAX API's
 // SUPPORTED_ENCODINGS, same scales) and the shared expert (bf16 weights),
 // both projections:
 //   gate/up: h = silu(min(x W_g^T, L)) * clamp(x W_u^T, -L, L)   (swiglu_limit,

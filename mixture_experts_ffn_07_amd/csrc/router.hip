@@ -190,9 +190,11 @@ RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
   const int64_t etiles = (n_experts + 63) / 64;
   const int64_t ttiles = tokens > 0 ? (tokens + 16 * p.mt - 1) / (16 * p.mt) : 1;
   const int nchunks = (hidden + 127) / 128;
-  int64_t want = (512 + etiles * ttiles - 1) / (etiles * ttiles);  // aim for ~512 blocks
+  // aim for ~2048 blocks, at most 16 K ranges (the top-k adds the partials;
+  // 64 tokens: 512 blocks and 8 ranges 24 + 11 us, this 19 + 13 us)
+  int64_t want = (2048 + etiles * ttiles - 1) / (etiles * ttiles);
   if (want < 1) want = 1;
-  if (want > 8) want = 8;  // the top-k adds the partials; keep that short
+  if (want > 16) want = 16;
   if (want > nchunks) want = nchunks;
   p.chunks_per_split = (int)((nchunks + want - 1) / want);
   p.ksplit = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
