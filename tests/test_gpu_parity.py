@@ -126,10 +126,12 @@ def test_permute_bit_exact(t, e, k, skew):
 
 
 @pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k",
-                                     "fp8_t2"])
+                                     "fp8_t2", "t200_sliced_shared", "t1100_dense_shared"])
 def test_expert_ffn(variant):
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
+           "t200_sliced_shared": base.with_(tokens=200, shared_inter=160),
+           "t1100_dense_shared": base.with_(tokens=1100, hidden=384, shared_inter=224),
            "fp8": base.with_(tokens=40, expert_format="mxfp8"),
            "fp8_t2": base.with_(tokens=2, expert_format="mxfp8"),
            "fp8_ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224, expert_format="mxfp8"),
