@@ -430,6 +430,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// 12 bytes per lane; lane l's bytes land at lds + 16 l (the fourth dword of
+// each 16-byte slot is left alone; checked on gfx950).
+__device__ __forceinline__ void load_lds12(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void load_lds4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
@@ -511,24 +516,28 @@ constexpr int pipe8_wait(int la, int lb) {
   return n;
 }
 
-// S16 (K a multiple of 512): the scale bytes of four chunks come as one
-// 16-byte load per weight row instead of one 4-byte load per row and chunk.
-// Each such load touches 64 scattered rows, and their number per chunk
-// counts (timing copies: one extra 4-byte load of that kind per wave and
-// chunk cost 17%).  Wave 0 issues one 16-byte load (64 rows) per iteration:
-// in iteration c, part c & 3 of scale group (c >> 2) + 2, four chunks per
-// group, into a ring of three 4 KB groups; groups 0 and 1 come in the
-// prologue.  A group's last part lands five iterations before its first
-// chunk is read.
-template <bool SWIGLU, int AR, bool S16 = false>
+// SG = 4 (K a multiple of 512) or 3 (K a multiple of 384): the scale bytes of
+// SG chunks come as one 16- or 12-byte load per weight row instead of one
+// 4-byte load per row and chunk.  Each such load touches 64 scattered rows,
+// and their number per chunk counts (timing copies: one extra 4-byte load of
+// that kind per wave and chunk cost 17%).  A scale group (SG chunks of 256
+// rows, 16 bytes per row in LDS) is four parts of 64 rows; a ring holds three
+// groups, and groups 0 and 1 come in the prologue.  SG = 4: wave 0 issues
+// part c & 3 of group (c >> 2) + 2 in iteration c.  SG = 3: waves 0 and 1
+// issue parts 2 (c % 3) + wave (mod 4) of group c / 3 + 2, so the third
+// iteration repeats parts 0 and 1.  A group's parts land four or more
+// iterations before its first chunk is read.  SG = 0: a 4-byte load per row
+// and chunk by the K-half-0 waves.
+template <bool SWIGLU, int AR, int SG = 0>
 __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kernel(GemmParams p, int n_tiles, int col_blocks) {
   constexpr int kSA = Pipe8Cfg<AR>::kA, kSB = Pipe8Cfg<AR>::kB;
   constexpr bool kAFirst = kSA <= kSB;
   constexpr int kAStage = AR * 256;
   constexpr int kLoadsA = AR / 32;  // activation loads per wave and chunk at full tiles
   constexpr int MTMAX = AR / 16;
-  constexpr int kS16Group = 256 * 16;
-  constexpr int kPool = kSA * kAStage + kSB * kPipeBStage + (S16 ? 3 * kS16Group : kSB * kPipeSStage);
+  static_assert(SG == 0 || SG == 3 || SG == 4, "scale groups of 3 or 4 chunks");
+  constexpr int kSGroup = 256 * 16;
+  constexpr int kPool = kSA * kAStage + kSB * kPipeBStage + (SG ? 3 * kSGroup : kSB * kPipeSStage);
   static_assert(kPool >= 4 * AR * 256, "the K-half reduction reuses 4 x AR x 256 B of the stage pool");
   // one pool: activation stages, weight-code stages, scale stages (the first
   // AR KB also hold the K-half reduction at the end)
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
   auto a_lds = [&](int i) { return pool + i * kAStage; };
   auto b_lds = [&](int i) { return pool + kSA * kAStage + i * kPipeBStage; };
   auto s_lds = [&](int i) { return pool + kSA * kAStage + kSB * kPipeBStage + i * kPipeSStage; };
-  auto s16_lds = [&](int g) { return pool + kSA * kAStage + kSB * kPipeBStage + (g % 3) * kS16Group; };
+  auto sg_lds = [&](int g) { return pool + kSA * kAStage + kSB * kPipeBStage + (g % 3) * kSGroup; };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int cg = wave & 3, kh = wave >> 2;
@@ -599,13 +608,15 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
     b_src[t] = bq_e + brow_col(brow) * (K / 2) + 16 * piece;
   }
   const uint8_t* s_src = bs_e + brow_col(64 * (wave & 3) + lane) * (K / 32);
-  // S16: row 64 i + lane of part i (i = 0..3)
-  const uint8_t* s16_src[4];
-  if constexpr (S16) {
+  // scale groups: row 64 i + lane of part i (i = 0..3)
+  const uint8_t* sg_src[4];
+  if constexpr (SG != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s16_src[i] = bs_e + brow_col(64 * i + lane) * (K / 32);
+    for (int i = 0; i < 4; ++i) sg_src[i] = bs_e + brow_col(64 * i + lane) * (K / 32);
   }
-  const int n_groups = nchunks / 4;
+  const int n_groups = SG ? nchunks / SG : 1;
+  // the waves that issue scale loads in the main loop (wave-uniform)
+  const bool s_issuer = SG == 4 ? wave == 0 : SG == 3 ? wave < 2 : kh == 0;
 
   auto issue_a = [&](int c) {
     const int cc = min(c, nchunks - 1);
@@ -619,16 +630,29 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
     const uint32_t dst = lds_addr(b_lds(c % kSB) + 2048 * wave);
 #pragma unroll
     for (int t = 0; t < kPipe8LoadsB; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
-    if constexpr (!S16)
+    if constexpr (SG == 0)
       if (kh == 0) load_lds4(s_src + 4 * cc, lds_addr(s_lds(c % kSB) + 256 * wave));  // wave-uniform
   };
-  // S16: part i of scale group g (groups past the end re-read the last one
-  // into a ring slot no longer read)
-  auto issue_s16 = [&](int g, int i) {
+  // part i of scale group g (groups past the end re-read the last one into a
+  // ring slot no longer read)
+  auto issue_sg = [&](int g, int i) {
     const int gg = min(g, n_groups - 1);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      if (ii == i) load_lds16(s16_src[ii] + 16 * gg, lds_addr(s16_lds(g) + 1024 * ii));
+    for (int ii = 0; ii < 4; ++ii) {
+      if (ii == i) {
+        if constexpr (SG == 4)
+          load_lds16(sg_src[ii] + 16 * gg, lds_addr(sg_lds(g) + 1024 * ii));
+        else
+          load_lds12(sg_src[ii] + 12 * gg, lds_addr(sg_lds(g) + 1024 * ii));
+      }
+    }
+  };
+  auto issue_sg_iter = [&](int c) {
+    if constexpr (SG == 4) {
+      if (s_issuer) issue_sg((c >> 2) + 2, c & 3);
+    } else if constexpr (SG == 3) {
+      if (s_issuer) issue_sg(c / 3 + 2, (2 * (c % 3) + wave) & 3);
+    }
   };
 
   f32x4_t acc[MTMAX][4];
@@ -642,12 +666,12 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
   for (int c = 0; c < kSB - 1; ++c) issue_b(c);
 #pragma unroll
   for (int c = 0; c < kSA - 1; ++c) issue_a(c);
-  if constexpr (S16) {
+  if constexpr (SG != 0) {
     if (wave == 0) {  // wave-uniform
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) issue_s16(g, i);
+        for (int i = 0; i < 4; ++i) issue_sg(g, i);
     }
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -656,13 +680,13 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
     constexpr int MT = decltype(mt_tag)::value;
     for (int c = 0; c < nchunks; ++c) {
       // MT / 2 activation loads per wave, the weight codes, and the scale
-      // load of the waves that issue one (K half 0, or wave 0 with S16);
-      // S16 data for chunk c was issued before its weight codes
+      // load of the waves that issue one; a scale group for chunk c was
+      // issued before chunk c's weight codes
       constexpr int kWait0 = pipe8_wait<kSA, kSB>(MT / 2, kPipe8LoadsB + 1);
       constexpr int kWait1 = pipe8_wait<kSA, kSB>(MT / 2, kPipe8LoadsB);
       static_assert(kWait0 < 64 && kWait1 < 64, "vmcnt holds at most 63");
       if (c > 0) {
-        if (S16 ? wave == 0 : kh == 0)
+        if (s_issuer)
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait0) : "memory");
         else
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait1) : "memory");
@@ -670,8 +694,8 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
       }
       const uint8_t* al = a_lds(c % kSA);
       const uint8_t* bl = b_lds(c % kSB);
-      const uint8_t* sl = S16 ? s16_lds(c >> 2) + 4 * (c & 3) : s_lds(c % kSB);
-      constexpr int kSRow = S16 ? 16 : 4;  // scale bytes per row in LDS
+      const uint8_t* sl = SG ? sg_lds(c / (SG ? SG : 1)) + 4 * (c % (SG ? SG : 1)) : s_lds(c % kSB);
+      constexpr int kSRow = SG ? 16 : 4;  // scale bytes per row in LDS
       uint32_t q[4][2];
       float sc[4];
 #pragma unroll
@@ -692,12 +716,10 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
       if constexpr (kAFirst) {
         issue_a(c + kSA - 1);
         issue_b(c + kSB - 1);
-        if constexpr (S16)
-          if (wave == 0) issue_s16((c >> 2) + 2, c & 3);  // wave-uniform
+        issue_sg_iter(c);
       } else {
         issue_b(c + kSB - 1);
-        if constexpr (S16)
-          if (wave == 0) issue_s16((c >> 2) + 2, c & 3);  // wave-uniform
+        issue_sg_iter(c);
         issue_a(c + kSA - 1);
       }
       read_a(a1, 2 * kh + 1);
@@ -1187,7 +1209,7 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
           const int col_blocks = (int)g.y;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
           if (p.K % 512 == 0)
-            hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU, 128, true>), g1, dim3(512), 0, stream, p, n_tiles,
+            hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU, 128, 4>), g1, dim3(512), 0, stream, p, n_tiles,
                                col_blocks);
           else
             hipLaunchKernelGGL((expert_gemm_pipe8_kernel<SWIGLU, 128>), g1, dim3(512), 0, stream, p, n_tiles,
@@ -1217,12 +1239,15 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
     if constexpr (SWIGLU) {
       if (p.K % 512 == 0)
-        hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128, true>), g1, dim3(512), 0, stream, p, n_tiles,
+        hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128, 4>), g1, dim3(512), 0, stream, p, n_tiles,
                            col_blocks);
       else
         hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
-    } else
+    } else if (p.K % 384 == 0) {
+      hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32, 3>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
+    } else {
       hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
+    }
   } else {
     if constexpr (BF == kWBf16) {
       if (mt == 2) {  // 32-row tiles (the shared expert at 17..127 tokens)
