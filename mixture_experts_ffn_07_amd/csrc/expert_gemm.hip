@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
 // projections read each expert's weights once; registers cannot hold the
 // loads in flight such a stream needs, LDS can.  Per 128-wide K chunk and
 // block: activation tile 128 x 256 B (bf16), weight codes 256 rows x 64 B,
-// scale words 256 x 4 B.
+// scale words 256 x 4 B (or a share of a scale group).
 //
 // LDS layouts are XOR-swizzled so that the 16 lanes reading one MFMA operand
 // column hit 16 different 16-byte bank groups: activation row r keeps its
@@ -468,9 +468,10 @@ constexpr int kPipeSStage = 256 * 4;
 // runs two waves and one's LDS and dependency stalls overlap the other's
 // matrix work.  The halves' accumulators are added through LDS at the end.
 // Per chunk each wave issues up to 4 activation loads, then 2 weight-code
-// loads, and the waves of K half 0 one 4-byte scale load (weight rows 64 w +
-// lane); the waits count these (pipe8_wait).  (Loads of 4 bytes or less fill
-// 4-byte LDS slots per lane.)
+// loads, and the waves that carry scales one scale load: a 4-byte word per
+// weight row (K-half-0 waves, rows 64 w + lane), or with scale groups (below)
+// a 16- or 12-byte load covering several chunks; the waits count these
+// (pipe8_wait).  (Loads of 4 bytes or less fill 4-byte LDS slots per lane.)
 //
 // Tiles of AR = 128 rows serve many rows per expert.  At a few rows per
 // expert the kernel streams weights with little matrix work per byte: 32-row
@@ -1230,16 +1231,17 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     }
     hipLaunchKernelGGL((expert_gemm_tiled_kernel<SWIGLU, BF>), g, dim3(256), 0, stream, p);
   } else if (FP4 && mt == kPipeSmallMt && p.K % 128 == 0) {
-    // 32-row tiles: the down projection runs the 32-row pipelined kernel, two
-    // blocks per CU (one block's start and end overlap the other's stream;
-    // 382 -> 345 us at 64 tokens); the gate/up projection measured slower so
-    // (770 -> 850 us) and keeps the 128-row kernel, one block per CU
+    // 32-row tiles: the 32-row pipelined kernel, two blocks per CU (one
+    // block's start and end overlap the other's stream; down 382 -> 345 us at
+    // 64 tokens).  Gate/up takes it with scale groups (673 -> 663 us); with
+    // 4-byte scale words it measured slower (770 -> 850 us) and keeps the
+    // 128-row kernel, one block per CU
     const int n_tiles = (int)grid.x;
     const int col_blocks = (p.N + 4 * tiled_cols_per_wave<SWIGLU>() - 1) / (4 * tiled_cols_per_wave<SWIGLU>());
     const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
     if constexpr (SWIGLU) {
       if (p.K % 512 == 0)
-        hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128, 4>), g1, dim3(512), 0, stream, p, n_tiles,
+        hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 32, 4>), g1, dim3(512), 0, stream, p, n_tiles,
                            col_blocks);
       else
         hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
