@@ -210,9 +210,10 @@ struct TiledB {
   uint32_t s[4];
 };
 
+// with_scale false: the scale bytes come from the kernel's scale groups
 template <bool SWIGLU, int BF>
 __device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, BF>& b, const GemmParams& p, int e, int n0w, int col,
-                                             int grp, int c, int nchunks) {
+                                             int grp, int c, int nchunks, bool with_scale = true) {
   constexpr bool FP4 = BF == kWMxfp4, FP8 = BF == kWMxfp8;
   const int K = p.K;
   const int k0 = c * 128 + grp * 32;
@@ -238,8 +239,9 @@ __device__ __forceinline__ void tiled_load_b(TiledB<SWIGLU, BF>& b, const GemmPa
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         b.q[j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 16 * q, 0));
-      b.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? r * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOob),
-                                                    0, 0);
+      b.s[j] = with_scale ? __builtin_amdgcn_raw_buffer_load_b8(
+                                rs, (int)(ok ? r * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOob), 0, 0)
+                          : 0u;
     } else {
       const uint32_t hb = (uint32_t)(p.b_expert_rows * K * 2);
       const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.bh + (int64_t)e * p.b_expert_rows * K, hb);
@@ -322,8 +324,29 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
   TiledB<SWIGLU, BF> b0, b1, b2;
   u32x4_t av[kAP];
   const int n_src = n_ok ? n0w : 0;
+  // MXFP8, K a multiple of 512 (384): scale groups of sgs = 4 (3) chunks.  A
+  // per-chunk byte load per lane and column tile touches 16 scattered rows
+  // per instruction; instead lane group g < sgs loads the scale word of
+  // chunk sgs G + g of its row once per group, and each chunk takes its byte
+  // from that lane (ds_bpermute).
+  const int sgs = FP8 ? (K % 512 == 0 ? 4 : K % 384 == 0 ? 3 : 0) : 0;  // block-uniform
+  const bool groups = sgs != 0;
+  uint32_t sw_cur[4] = {0u, 0u, 0u, 0u}, sw_next[4] = {0u, 0u, 0u, 0u};
+  auto load_sw = [&](uint32_t (&sw)[4], int g) {
+    const uint32_t sb = (uint32_t)(p.b_expert_rows * (K / 32));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sb, sb);
+    const int ci = sgs * g + grp;
+    const bool ok = n_ok && grp < sgs && ci < nchunks;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ncol = SWIGLU ? n_src + 16 * (j & 1) + col + (j >> 1) * p.b_row_second : n_src + 16 * j + col;
+      sw[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, (int)(ok ? (uint32_t)ncol * (uint32_t)(K / 32) + 4u * (uint32_t)ci : kOob), 0, 0);
+    }
+  };
   a_issue(av, 0);
-  tiled_load_b<SWIGLU, BF>(b0, p, e, n_src, col, grp, n_ok ? 0 : nchunks, nchunks);
+  tiled_load_b<SWIGLU, BF>(b0, p, e, n_src, col, grp, n_ok ? 0 : nchunks, nchunks, !groups);
+  if (groups) load_sw(sw_next, 0);
   if constexpr (PD == 2) tiled_load_b<SWIGLU, BF>(b1, p, e, n_src, col, grp, n_ok ? 1 : nchunks, nchunks);
   a_commit(av, 0);
   __syncthreads();
@@ -355,11 +378,25 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
   };
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
+    int sub = 0;
+    if (groups) {
+      sub = c % sgs;
+      if (sub == 0) {  // block-uniform
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sw_cur[j] = sw_next[j];
+        load_sw(sw_next, c / sgs + 1);
+      }
+    }
     a_issue(av, c + 1);
     if constexpr (PD == 2)
-      tiled_load_b<SWIGLU, BF>(b2, p, e, n_src, col, grp, n_ok ? c + 2 : nchunks, nchunks);
+      tiled_load_b<SWIGLU, BF>(b2, p, e, n_src, col, grp, n_ok ? c + 2 : nchunks, nchunks, !groups);
     else
-      tiled_load_b<SWIGLU, BF>(b1, p, e, n_src, col, grp, n_ok ? c + 1 : nchunks, nchunks);
+      tiled_load_b<SWIGLU, BF>(b1, p, e, n_src, col, grp, n_ok ? c + 1 : nchunks, nchunks, !groups);
+    if (groups) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b0.s[j] = ((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (col + 16 * sub), (int)sw_cur[j]) >> (8 * grp)) & 0xffu;
+    }
     multiply(b0, buf);
     a_commit(av, buf ^ 1);
     b0 = b1;
