@@ -58,7 +58,15 @@
  *   multiples of 32, at most 65536; 1 <= E <= 1024; 1 <= k <= min(E, 16);
  *   n_shared in {0, 1}; score_func == 0; expert_format in {0, 1}; route_scale finite;
  *   swiglu_limit > 0 (may be +inf); 0 <= tokens <= 2^22; ws_bytes large
- *   enough.  tokens == 0 returns MOE_OK and enqueues nothing.  A failed
+ *   enough.  Some kernels address a matrix through a 32-bit buffer
+ *   descriptor, so every one of these must stay below 2^31 - 16 bytes:
+ *   x [T][H] and h [T*k][I] bf16 (the routed inner activations, T*k*I*2
+ *   bytes), the shared expert's [T][I_s] bf16 activations, one routed
+ *   expert's gate/up or down codes, the shared gate/up and down matrices and
+ *   the router matrix; a call that would pass this limit returns
+ *   MOE_ERR_UNSUPPORTED (at H 5120, I 2304, k 6: at most 77,672 tokens a
+ *   call; split larger batches).  tokens == 0 returns MOE_OK and enqueues
+ *   nothing.  A failed
  *   kernel launch returns MOE_ERR_HIP.  Data are not checked: NaN/Inf
  *   inputs, E8M0 byte 0xFF, expert ids outside [0, E) or an offset table
  *   that is not a permutation give unspecified values, but every access
@@ -117,11 +125,12 @@ typedef struct moe_weights {
   const uint16_t* sh_gu;     /* [2I_s][H] bf16, gate rows then up rows; NULL iff n_shared == 0 */
   const uint16_t* sh_dn;     /* [H][I_s] bf16; NULL iff n_shared == 0             */
   const uint16_t* norm_gamma; /* [H] bf16 gain of the pre-FFN RMSNorm, or NULL: no norm.
-                                 Read by moe_layer_forward(_timed) only. */
+                                 Read by moe_layer_forward only. */
 } moe_weights;
 
 /* Bytes of workspace every entry point below needs for `tokens` tokens
- * (the maximum over them).  Returns 0 for an invalid config. */
+ * (the maximum over them).  Returns 0 for an invalid config, or for a token
+ * count past the buffer limit stated under Errors. */
 size_t moe_workspace_bytes(const moe_config* cfg, int64_t tokens);
 
 /* Pre-FFN RMSNorm of T rows: x_norm[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)
@@ -180,18 +189,6 @@ moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int3
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);
-
-/* Kernel-level timing of moe_layer_forward, for profiling tools: enqueues
- * the same kernels with the same launch configuration on `stream`, with a
- * HIP event recorded before the first kernel and after each one, then
- * WAITS for the stream to reach the last event (unlike every other entry
- * point).  kernel_ms[i] receives the time between the events around kernel
- * i, kernel_names[i] a static string naming it; at most max_kernels entries
- * are written and *n_kernels receives the number of kernels launched.
- * Routing outputs are not returned.  Creates and destroys its own events. */
-moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
-                                   uint16_t* y, void* ws, size_t ws_bytes, void* stream, float* kernel_ms,
-                                   const char** kernel_names, int32_t max_kernels, int32_t* n_kernels);
 
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);

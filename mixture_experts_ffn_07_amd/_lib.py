@@ -1,4 +1,5 @@
-"""ctypes binding of libmoe_ffn.so (the C ABI in include/moe_ffn.h).
+"""ctypes binding of libmoe_ffn.so (the C ABI in include/moe_ffn.h, and the
+timing call of include/moe_ffn_profile.h).
 
 Argument marshalling only: torch tensors in, device pointers and sizes out.
 Every step of the layer runs in the HIP library; if the library is missing
@@ -17,7 +18,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # MOE_FFN_LIB selects another build of the same library (same ABI)
 LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_PKG, "libmoe_ffn.so")
-HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_ffn.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_PKG), "include")
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_ALIGNMENT",
@@ -81,10 +82,13 @@ def load() -> ctypes.CDLL:
 
 
 def header_functions() -> list:
-    """Names of the functions declared in include/moe_ffn.h."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text, flags=re.M)
+    """Names of the functions declared in the headers under include/."""
+    names = []
+    for path in sorted(os.path.join(INCLUDE_DIR, h) for h in os.listdir(INCLUDE_DIR) if h.endswith(".h")):
+        with open(path) as f:
+            text = f.read()
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text, flags=re.M)
+    return names
 
 
 # ------------------------------------------------------------------ marshalling helpers

@@ -459,21 +459,22 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_tiled_kernel(GemmParams p)
 // treat the LDS it writes as possibly read by every later LDS load (it would
 // then wait for all loads in flight before each one); the kernel waits for
 // these loads itself.  The loads write no registers; M0 carries the LDS
-// address (one wait state after an SALU write of M0 before the load).  No
-// other code in these kernels uses M0.
+// address.  It is an input operand of the asm ("{m0}"), so the compiler
+// writes M0 itself and knows the asm reads it; the asm opens with one wait
+// state, which gfx950 needs between an SALU write of M0 and the load.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 // 12 bytes per lane; lane l's bytes land at lds + 16 l (the fourth dword of
 // each 16-byte slot is left alone; checked on gfx950).
 __device__ __forceinline__ void load_lds12(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void load_lds4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
 // XCD-aware block order for the pipelined kernels: a 1-D grid of

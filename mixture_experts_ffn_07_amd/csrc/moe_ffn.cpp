@@ -1,6 +1,8 @@
 // C ABI of the MoE FFN layer: argument checks, workspace layout and the launch
-// sequence of each entry point (declared in include/moe_ffn.h).
+// sequence of each entry point (declared in include/moe_ffn.h, and the timing
+// call in include/moe_ffn_profile.h).
 #include "../../include/moe_ffn.h"
+#include "../../include/moe_ffn_profile.h"
 
 #include <hip/hip_runtime.h>
 
@@ -73,6 +75,38 @@ moe_status check_config(const moe_config* c) {
 
 moe_status check_tokens(int64_t tokens) {
   if (tokens < 0 || tokens > kMaxTokens) return fail(MOE_ERR_INVALID_ARG, "tokens must be in [0, 2^22]");
+  return MOE_OK;
+}
+
+// Matrices some kernels address through a 32-bit buffer descriptor, whose
+// out-of-range offset is kOob: each must stay below kOob bytes.  Called with
+// a checked config.
+moe_status check_buffer_extents(const moe_config* c, int64_t T) {
+  const int64_t H = c->hidden, I = c->inter, k = c->top_k, E = c->n_experts;
+  const int64_t Is = c->n_shared ? c->shared_inter : 0;
+  const int64_t code = c->expert_format == 1 ? 2 : 1;  // code bytes per two elements
+  struct Extent {
+    const char* what;
+    int64_t bytes;
+  };
+  const Extent ext[] = {
+      {"x [tokens][hidden] bf16", T * H * 2},
+      {"the routed activations [tokens*top_k][inter] bf16", T * k * I * 2},
+      {"the shared activations [tokens][shared_inter] bf16", T * Is * 2},
+      {"one routed expert's gate/up codes", 2 * I * H * code / 2},
+      {"one routed expert's down codes", H * I * code / 2},
+      {"the shared gate/up matrix", 2 * Is * H * 2},
+      {"the shared down matrix", H * Is * 2},
+      {"the router matrix", E * H * 4},
+  };
+  for (const Extent& e : ext) {
+    if (e.bytes >= (int64_t)moe::kOob) {
+      static thread_local char buf[200];
+      std::snprintf(buf, sizeof(buf), "%s would take %lld bytes, at or above the 2^31 - 16 a buffer may have; "
+                    "split the tokens into smaller calls", e.what, (long long)e.bytes);
+      return fail(MOE_ERR_UNSUPPORTED, buf);
+    }
+  }
   return MOE_OK;
 }
 
@@ -761,7 +795,8 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_config* cfg, int64_t tokens) {
-  if (check_config(cfg) != MOE_OK || check_tokens(tokens) != MOE_OK) return 0;
+  if (check_config(cfg) != MOE_OK || check_tokens(tokens) != MOE_OK || check_buffer_extents(cfg, tokens) != MOE_OK)
+    return 0;
   return plan_workspace(cfg, tokens).total;
 }
 
@@ -781,7 +816,9 @@ moe_status moe_rmsnorm(const moe_config* cfg, const uint16_t* gamma, const uint1
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                      int32_t* topk_idx, float* topk_w, float* tie_gap, void* ws, size_t ws_bytes, void* stream) {
   moe_status s;
-  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK ||
+      (s = check_buffer_extents(cfg, tokens)) != MOE_OK)
+    return s;
   if ((s = check_routed_weights(cfg, w, true, false)) != MOE_OK) return s;
   if ((s = need(x, 16, "x")) != MOE_OK || (s = need(topk_idx, 4, "topk_idx")) != MOE_OK ||
       (s = need(topk_w, 4, "topk_w")) != MOE_OK)
@@ -811,7 +848,9 @@ moe_status moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const uin
                           const int32_t* expert_offsets, const int32_t* sorted_slots, uint16_t* y_slot,
                           uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream) {
   moe_status s;
-  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK ||
+      (s = check_buffer_extents(cfg, tokens)) != MOE_OK)
+    return s;
   if ((s = check_routed_weights(cfg, w, false, true)) != MOE_OK) return s;
   if ((s = need(x, 16, "x")) != MOE_OK || (s = need(expert_offsets, 4, "expert_offsets")) != MOE_OK ||
       (s = need(sorted_slots, 4, "sorted_slots")) != MOE_OK || (s = need(y_slot, 16, "y_slot")) != MOE_OK)
@@ -854,7 +893,9 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
                               uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                               hipStream_t st, Timeline* tl) {
   moe_status s;
-  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK) return s;
+  if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK ||
+      (s = check_buffer_extents(cfg, tokens)) != MOE_OK)
+    return s;
   if ((s = check_routed_weights(cfg, w, true, true)) != MOE_OK) return s;
   if ((s = need(x, 16, "x")) != MOE_OK || (s = need(y, 16, "y")) != MOE_OK) return s;
   if (w->norm_gamma && (s = check_norm(cfg, w->norm_gamma)) != MOE_OK) return s;

@@ -11,7 +11,6 @@ exactly), directly from the definitions, with no tiling, fusion or reordering.
 """
 
 from .moe_oracle import (  # noqa: F401
-    E2M1_CODE_BITS,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
     rmsnorm,
@@ -20,11 +19,9 @@ from .moe_oracle import (  # noqa: F401
     e8m0_value,
     decode_mxfp4,
     mxfp4_packed_bytes,
-    E4M3_CODE_BITS,
     e4m3_value,
     e4m3_table,
     decode_mxfp8,
-    mxfp8_bytes,
     EXPERT_FORMATS,
     softplus,
     sqrtsoftplus,

@@ -71,9 +71,6 @@ import numpy as np
 # Number formats
 # ---------------------------------------------------------------------------
 
-#: Field widths of E2M1 (OCP Microscaling Formats v1.0, FP4 element type):
-#: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; no Inf, no NaN.
-E2M1_CODE_BITS = {"sign": 3, "exponent": (2, 1), "mantissa": 0, "bias": 1}
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -154,10 +151,6 @@ def decode_mxfp4(packed, scales, k: int) -> np.ndarray:
     return values * block_scale
 
 
-#: Field widths of E4M3 (OCP 8-bit floating point, E4M3 "fn": no infinities,
-#: exponent and mantissa all ones is NaN): 1 sign, 4 exponent bits (bias 7),
-#: 3 mantissa bits.
-E4M3_CODE_BITS = {"sign": 7, "exponent": (6, 3), "mantissa": (2, 0), "bias": 7}
 
 
 def e4m3_value(code: int) -> float:
@@ -190,12 +183,6 @@ def decode_mxfp8(codes, scales, k: int) -> np.ndarray:
     scales = np.asarray(scales, dtype=np.uint8)
     assert codes.shape[-1] == k and scales.shape[-1] * 32 == k
     return e4m3_table()[codes] * np.repeat(e8m0_value(scales), 32, axis=-1)
-
-
-def mxfp8_bytes(rows: int, k: int) -> int:
-    """Bytes of an MXFP8 matrix [rows, k]: k code bytes + k/32 scale bytes a row."""
-    assert k % 32 == 0
-    return rows * (k + k // 32)
 
 
 #: expert-weight codecs: name -> (decoder, elements per code byte)

@@ -31,6 +31,25 @@ def test_library_loads_and_exports_every_header_function():
     assert lib.moe_abi_version() == 2
 
 
+@pytest.mark.parametrize("tokens,code", [(77672, OK), (77673, UNSUPPORTED), (1 << 22, UNSUPPORTED)])
+def test_buffer_extent_limit(tokens, code):
+    """Matrices read through 32-bit buffer descriptors must stay below 2^31 - 16 bytes: at the full layer shape
+    the routed activations [T*k][I] bf16 reach that at 77,673 tokens."""
+    lib = moe.load()
+    c, w, r, big = moe.make_config(5120, 384, 6, 2304), _weights(), ctypes.byref, 1 << 44
+    assert (moe.moe_workspace_bytes(c, tokens) > 0) == (code == OK)
+    if code != OK:
+        assert lib.moe_layer_forward(r(c), r(w), P, tokens, P, None, None, P, big, None) == code
+        assert "split the tokens" in lib.moe_last_error().decode()
+        assert lib.moe_route(r(c), r(w), P, tokens, P, P, None, P, big, None) == code
+        assert lib.moe_expert_ffn(r(c), r(w), P, tokens, P, P, P, P, P, big, None) == code
+    # one MXFP8 expert's gate/up codes at H = I = 65536 would take 8 GiB
+    c8 = moe.make_config(65536, 8, 2, 65536, n_shared=0, expert_format=1)
+    assert moe.moe_workspace_bytes(c8, 1) == 0
+    assert lib.moe_layer_forward(r(c8), r(_weights(sh_gu=None, sh_dn=None)), P, 1, P, None, None, P, big, None) \
+        == UNSUPPORTED
+
+
 def test_status_strings():
     lib = moe.load()
     for code in range(6):
