@@ -190,6 +190,25 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_layer_forward, with the same arguments minus the workspace.
+ * Its scratch memory is a device array of MOE_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * inside the library, one per GPU, which each GPU the library runs on holds
+ * until the process ends; the call allocates nothing.  Shapes whose
+ * moe_workspace_bytes exceeds that return MOE_ERR_UNSUPPORTED before
+ * anything is enqueued (at the full layer shape, up to about 120 tokens a
+ * call fit).  Every call on a GPU shares that GPU's array, which keeps the
+ * last call's contents (no kernel reads scratch it has not written in the
+ * same call): calls that overlap on one GPU -- on different streams, or
+ * from several threads -- race and give unspecified results; order them on
+ * one stream.  `stream` must belong to the calling thread's current device
+ * (else MOE_ERR_INVALID_ARG); the first call on a device looks up that
+ * device's copy of the array (a failure returns MOE_ERR_HIP). */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                                     uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);
 

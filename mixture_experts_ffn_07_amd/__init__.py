@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_expert_ffn,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_layer_forward_timed,
     moe_permute,
     moe_rmsnorm,

@@ -66,6 +66,7 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, vp, vp, vp, sz, vp]),
         "moe_combine": (ctypes.c_int, [cfgp, vp, vp, vp, vp, i64, vp, vp]),
         "moe_layer_forward": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "moe_layer_forward_noalloc": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, vp, vp]),
         "moe_layer_forward_timed": (ctypes.c_int, [cfgp, wp, vp, i64, vp, vp, sz, vp,
                                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p),
                                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
@@ -182,6 +183,12 @@ def moe_layer_forward(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, stream
     _check("moe_layer_forward", load().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), tokens,
                                                          _ptr(y), _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws),
                                                          ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_layer_forward_noalloc(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, stream=None):
+    _check("moe_layer_forward_noalloc",
+           load().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), tokens, _ptr(y),
+                                            _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)))
 
 
 def moe_layer_forward_timed(cfg, w, x, tokens, y, ws, stream=None, max_kernels: int = 32):

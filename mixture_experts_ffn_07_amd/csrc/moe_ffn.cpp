@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "mx_device.h"
@@ -28,6 +29,33 @@ moe_status fail_hip(hipError_t err, const char* where) {
   std::snprintf(buf, sizeof(buf), "%s: %s", where, hipGetErrorString(err));
   g_last_error = buf;
   return MOE_ERR_HIP;
+}
+
+// Scratch memory of moe_layer_forward_noalloc: a device array in this code
+// object, so every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: the kernels get the device address from
+// hipGetSymbolAddress, taken once per device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, which must be the current
+// device; looked up on the first call for that device.
+moe_status scratch_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index beyond the 64 the library tracks");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return fail_hip(err, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
 }
 
 // Optional per-kernel timing: an event recorded after every launch.
@@ -889,9 +917,9 @@ moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int3
 
 namespace {
 
-moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
-                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                              hipStream_t st, Timeline* tl) {
+// Checks of moe_layer_forward's arguments other than the workspace.
+moe_status check_layer_args(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                            const uint16_t* y, const int32_t* topk_idx_out, const float* topk_w_out) {
   moe_status s;
   if ((s = check_config(cfg)) != MOE_OK || (s = check_tokens(tokens)) != MOE_OK ||
       (s = check_buffer_extents(cfg, tokens)) != MOE_OK)
@@ -901,6 +929,14 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   if (w->norm_gamma && (s = check_norm(cfg, w->norm_gamma)) != MOE_OK) return s;
   if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_idx_out is not 4-byte aligned");
   if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_ERR_ALIGNMENT, "topk_w_out is not 4-byte aligned");
+  return MOE_OK;
+}
+
+moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                              hipStream_t st, Timeline* tl) {
+  moe_status s;
+  if ((s = check_layer_args(cfg, w, x, tokens, y, topk_idx_out, topk_w_out)) != MOE_OK) return s;
   const WsLayout L = plan_workspace(cfg, tokens);
   if ((s = check_ws(ws, ws_bytes, L)) != MOE_OK) return s;
   if (tokens == 0) return MOE_OK;
@@ -940,6 +976,33 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              void* stream) {
   return layer_forward_impl(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes,
                             static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
+                                     uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  moe_status s;
+  if ((s = check_layer_args(cfg, w, x, tokens, y, topk_idx_out, topk_w_out)) != MOE_OK) return s;
+  const size_t need = plan_workspace(cfg, tokens).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) {
+    static thread_local char buf[200];
+    std::snprintf(buf, sizeof(buf), "this shape needs %zu bytes of scratch, more than the %u the no-allocation entry "
+                  "point holds; call moe_layer_forward with a workspace", need, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+    return fail(MOE_ERR_UNSUPPORTED, buf);
+  }
+  if (tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail_hip(err, "hipGetDevice");
+  if (st) {
+    hipDevice_t sdev = -1;
+    if ((err = hipStreamGetDevice(st, &sdev)) != hipSuccess) return fail_hip(err, "hipStreamGetDevice");
+    if ((int)sdev != dev) return fail(MOE_ERR_INVALID_ARG, "stream belongs to a device other than the current one");
+  }
+  void* ws = nullptr;
+  if ((s = scratch_ptr(dev, &ws)) != MOE_OK) return s;
+  return layer_forward_impl(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
+                            st, nullptr);
 }
 
 moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,

@@ -21,8 +21,8 @@ def test_library_loads_and_exports_every_header_function():
     lib = moe.load()
     names = moe.header_functions()
     assert set(names) == {"moe_workspace_bytes", "moe_rmsnorm", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-                          "moe_layer_forward", "moe_layer_forward_timed", "moe_status_str", "moe_last_error",
-                          "moe_abi_version"}
+                          "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_timed",
+                          "moe_status_str", "moe_last_error", "moe_abi_version"}
     for n in names:
         assert hasattr(lib, n)
     dyn = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -220,3 +220,20 @@ def test_norm_checks():
         assert lib.moe_layer_forward(r(ce), r(_weights()), P, 0, P, None, None, P, big, None) == OK, eps
     assert lib.moe_layer_forward(r(c), r(_weights(norm_gamma=P + 2)), P, 8, P, None, None, P, big, None) == ALIGN
     assert "norm" in lib.moe_last_error().decode()
+
+
+def test_noalloc_argument_checks():
+    """moe_layer_forward_noalloc checks its arguments (and its scratch limit) before it touches the HIP runtime."""
+    lib = moe.load()
+    c, w, r = _cfg(), _weights(), ctypes.byref
+    assert lib.moe_layer_forward_noalloc(r(c), r(w), P, 0, P, None, None, None) == OK
+    assert lib.moe_layer_forward_noalloc(r(_cfg(hidden=48)), r(w), P, 8, P, None, None, None) == INVALID
+    assert lib.moe_layer_forward_noalloc(r(c), r(w), None, 8, P, None, None, None) == INVALID
+    assert lib.moe_layer_forward_noalloc(r(c), r(w), P + 2, 8, P, None, None, None) == ALIGN
+    assert lib.moe_layer_forward_noalloc(r(c), r(_weights(gu_q=None)), P, 8, P, None, None, None) == INVALID
+    assert lib.moe_layer_forward_noalloc(r(c), r(w), P, -1, P, None, None, None) == INVALID
+    # the full-size layer at 128 tokens needs more than the 16 MiB of scratch the library holds
+    big = moe.make_config(5120, 384, 6, 2304)
+    assert moe.moe_workspace_bytes(big, 128) > (16 << 20) >= moe.moe_workspace_bytes(big, 64)
+    assert lib.moe_layer_forward_noalloc(r(big), r(w), P, 128, P, None, None, None) == UNSUPPORTED
+    assert "scratch" in lib.moe_last_error().decode()

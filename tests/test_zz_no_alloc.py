@@ -1,0 +1,58 @@
+"""moe_layer_forward_noalloc (scratch in a library-held device array) against moe_layer_forward (caller's
+workspace) through the C ABI: the same kernels on the same inputs, so the outputs must be identical bit for bit.
+Two calls in a row, the second with fewer tokens, so the second runs on scratch the first left behind."""
+
+import pytest
+import torch
+
+import mixture_experts_ffn_07_amd as moe
+from moe_synth import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _both(inp, tokens):
+    cfg = moe.config_from(inp.cfg)
+    w = moe.weights_from(inp)
+    h, k = inp.cfg.hidden, inp.cfg.top_k
+    x = inp.x[:tokens].contiguous()
+    out = []
+    for noalloc in (False, True):
+        y = torch.full((tokens, h), -1, dtype=torch.int16, device=DEV)
+        idx = torch.full((tokens, k), -1, dtype=torch.int32, device=DEV)
+        wt = torch.full((tokens, k), -1.0, dtype=torch.float32, device=DEV)
+        if noalloc:
+            moe.moe_layer_forward_noalloc(cfg, w, x, tokens, y, idx, wt)
+        else:
+            moe.moe_layer_forward(cfg, w, x, tokens, y, idx, wt, moe.workspace(cfg, tokens, device=DEV))
+        torch.cuda.synchronize()
+        out.append((y, idx, wt))
+    return out
+
+
+@pytest.mark.parametrize("name,first,second", [("decode_t64_h5120_e384", 64, 5),
+                                               ("decode_t1_h5120_e384", 2, 1),
+                                               ("prefill_t4096_h5120_e384_fp8", 40, 17),
+                                               ("tiny_t8_h512_e32", 8, 3)])
+def test_noalloc_matches_workspace_entry_point(name, first, second):
+    cfg = CONFIGS[name].with_(tokens=first)
+    inp = make_inputs(cfg, seed=3, device=DEV)
+    for tokens in (first, second):
+        (y0, i0, w0), (y1, i1, w1) = _both(inp, tokens)
+        assert torch.equal(i0, i1), f"{name} T={tokens}: expert ids differ"
+        assert torch.equal(w0, w1), f"{name} T={tokens}: weights differ"
+        assert torch.equal(y0, y1), f"{name} T={tokens}: outputs differ"
+        assert int((i1 < 0).sum()) == 0
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    cfg = CONFIGS["decode_t64_h5120_e384"]
+    c = moe.config_from(cfg)
+    assert moe.moe_workspace_bytes(c, 128) > (16 << 20)
+    inp = make_inputs(cfg.with_(tokens=1), seed=0, device=DEV)
+    x = torch.zeros((128, cfg.hidden), dtype=torch.int16, device=DEV)
+    y = torch.empty_like(x)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_forward_noalloc(c, moe.weights_from(inp), x, 128, y, None, None)
+    assert ei.value.status == 2 and "scratch" in str(ei.value)
