@@ -7,13 +7,19 @@ resident in HBM.  Successive steps cycle through several independently drawn
 weight sets (as successive layers of a model would), so that the 256 MB
 last-level cache cannot hold the weights a step streams.
 
-Default workload: full-size decode, 1 token (hidden 5120, 384 MXFP4 experts
-of width 2304, top-6, one bf16 shared expert).  `roofline` describes the
-kernel that takes the most time, measured with HIP events on the stream it
-runs on; `cpu_baseline` times the CPU oracle on a few tokens of the same
-workload.  Timed steps are plain launches on one HIP stream by default
-(`--launch graph` replays HIP graphs instead; the other form is timed after
-for reference).
+The headline workload (`--workload`, default the full-size one-token decode:
+hidden 5120, 384 MXFP4 experts of width 2304, top-6, one bf16 shared expert)
+gives `value`, `ms_per_step` and `roofline`.  The same run also times the
+other shapes the metric names (`--also`: 64-token decode, 4096-token prefill
+and the 16384-token skewed layer by default); each gets its own entry under
+`workloads` with its time, tokens/s, the layer's HBM and MFMA fractions and
+the roofline of its dominant kernel.  A workload is bound by HBM or by the
+matrix units, whichever its algorithmic bytes and flops take longer on at the
+published peaks.  Kernel durations come from HIP events on the library's
+stream around every kernel.  `cpu_baseline` times the CPU oracle on a few
+tokens of the headline workload, with its weights already in host memory.
+Timed steps are plain launches on one HIP stream by default (`--launch graph`
+replays HIP graphs; the other form is timed after for reference).
 """
 
 from __future__ import annotations
@@ -31,9 +37,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec on 1 MI355X (decode B=1/64, prefill 4K); % HBM/MFMA roofline"
+# MI355X published peaks (dense)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0  # MXFP4 / MXFP6
+FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
+DEFAULT_ALSO = "decode_t64_h5120_e384,prefill_t4096_h5120_e384,skew_t16384_h5120_e128"
 
 
 def parse():
@@ -42,11 +52,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_t1_h5120_e384")
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated workloads timed in the same run ('' for none); each runs "
+                         "min(steps, 200) timed steps after min(warmup, 20) untimed ones")
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
     ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
-                    help="timed steps as plain launches on one HIP stream (measured ~2 us/step faster at one "
-                         "token) or as replays of HIP graphs (one per cycle over the weight sets); the other "
-                         "form is timed afterwards for reference")
+                    help="timed steps as plain launches on one HIP stream or as replays of HIP graphs (one per "
+                         "cycle over the weight sets); the other form is timed afterwards for reference")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed forwards per weight set for kernel times")
     ap.add_argument("--cpu-sample", type=int, default=16, help="decode tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--json-out", default="")
@@ -120,6 +132,23 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
     }
 
 
+def kernel_flops(cfg) -> dict:
+    """Flops each matrix kernel must do (the selected experts' products only)."""
+    t, h, e, k, i = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.inter
+    i_s = cfg.shared_inter if cfg.n_shared else 0
+    n = t * k
+    return {"routed_gate_up": 2.0 * n * h * 2 * i, "routed_down": 2.0 * n * i * h,
+            "shared_gate_up": 2.0 * t * h * 2 * i_s, "shared_down": 2.0 * t * i_s * h,
+            "router_logits": 2.0 * t * e * h}
+
+
+# the arithmetic each matrix kernel runs in, and that type's published dense peak (TFLOP/s)
+KERNEL_DTYPE = {"routed_gate_up": ("bf16 MFMA on exactly dequantised expert weights", BF16_PEAK_TFLOPS),
+                "routed_down": ("bf16 MFMA on exactly dequantised expert weights", BF16_PEAK_TFLOPS),
+                "shared_gate_up": ("bf16 MFMA", BF16_PEAK_TFLOPS), "shared_down": ("bf16 MFMA", BF16_PEAK_TFLOPS),
+                "router_logits": ("bf16 MFMA on three exact bf16 terms of the fp32 weights", BF16_PEAK_TFLOPS)}
+
+
 def layer_bytes(cfg, touched: float) -> float:
     """Algorithmic bytes of the whole layer: touched experts' and shared weights, router, x and y once."""
     t, h, e, i = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.inter
@@ -129,14 +158,56 @@ def layer_bytes(cfg, touched: float) -> float:
     return touched * per_expert + 3 * i_s * h * 2 + e * h * 4 + 2 * t * h * 2
 
 
-def layer_flops(cfg) -> float:
+def layer_flops(cfg) -> dict:
+    """Algorithmic flops of the layer: routed (selected experts), shared, router."""
     t, h, e, k, i = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.inter
     i_s = cfg.shared_inter if cfg.n_shared else 0
-    return 2.0 * t * (3 * h * i * k + 3 * h * i_s + e * h)
+    return {"routed": 2.0 * t * 3 * h * i * k, "shared": 2.0 * t * 3 * h * i_s, "router": 2.0 * t * e * h}
+
+
+def layer_roofline(cfg, touched: float, ms: float) -> dict:
+    """Time the layer needs at the published peaks, its bound, and the fractions a measured time reaches.
+
+    Matrix time: routed flops at the FP4 (MXFP4/MXFP6) peak, shared flops at the bf16 peak, router flops as three
+    exact bf16 terms at the bf16 peak."""
+    lb = layer_bytes(cfg, touched)
+    f = layer_flops(cfg)
+    t_hbm = lb / (HBM_PEAK_GBS * 1e9)
+    fp4_peak = FP8_PEAK_TFLOPS if cfg.expert_format == "mxfp8" else FP4_PEAK_TFLOPS
+    t_mfma = f["routed"] / (fp4_peak * 1e12) + (f["shared"] + 3 * f["router"]) / (BF16_PEAK_TFLOPS * 1e12)
+    s = ms * 1e-3
+    return {"bound": "mfma" if t_mfma > t_hbm else "hbm", "algorithmic_bytes": lb, "flops": f,
+            "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mfma * 1e6,
+            "hbm_frac": lb / s / (HBM_PEAK_GBS * 1e9),
+            "routed_fp4_frac": f["routed"] / s / (fp4_peak * 1e12),
+            "mfma_frac": t_mfma / s,
+            "roofline_frac": max(t_hbm, t_mfma) / s}
+
+
+def kernel_roofline(cfg, touched: float, kernel: str, kernel_ms: float, bound: str, digest: str) -> dict:
+    """Roofline entry of one kernel: algorithmic bytes (HBM-bound layer) or flops (MFMA-bound layer) over its
+    event-timed duration, against the published peak of that resource (for flops, of the kernel's own dtype)."""
+    algo = algorithmic_bytes(cfg, touched)
+    flops = kernel_flops(cfg)
+    s = kernel_ms * 1e-3
+    if bound == "mfma" and kernel in flops:
+        dtype, peak = KERNEL_DTYPE[kernel]
+        ach = flops[kernel] / s / 1e12
+        out = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+               "dtype": dtype, "flops": flops[kernel], "fp4_peak_frac": ach / FP4_PEAK_TFLOPS}
+    else:
+        ach = algo.get(kernel, 0.0) / s / 1e9
+        out = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+               "algorithmic_bytes": algo.get(kernel, 0.0)}
+        if kernel in flops:
+            out["mfma_tflops"] = flops[kernel] / s / 1e12
+    out.update({"traffic": traffic_from_profile(kernel, cfg.name, digest), "kernel": kernel, "kernel_ms": kernel_ms})
+    return out
 
 
 def cpu_baseline(cfg, inp, sample: int) -> dict:
-    """The oracle, untuned, on `sample` decode tokens of this workload (one call per token)."""
+    """The oracle, untuned, on `sample` decode tokens of this workload (one call per token), its inputs in host
+    memory before the timed region starts."""
     import numpy as np
 
     import oracle
@@ -144,45 +215,43 @@ def cpu_baseline(cfg, inp, sample: int) -> dict:
 
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = [(p.get("internal_api"), p.get("num_threads", 1)) for p in threadpool_info()]
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = []
+    threads = max([n for _, n in blas] + [1])
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     xs, _, _ = make_router_inputs(cfg.with_(tokens=sample), seed=0, device="cpu", x_seed=1234)
-    args = inp.oracle_args()
+    host = inp.to("cpu")  # every weight copied to host memory before timing
+    args = host.oracle_args()
     args.pop("x_bits")
     t0 = time.perf_counter()
     for t in range(sample):
         oracle.layer_forward(x_bits=xs[t:t + 1].numpy().view(np.uint16), **args)
     dt = time.perf_counter() - t0
     return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{sample} decode tokens of {cfg.name}, one oracle call per token (float64 numpy; "
-                      f"expert weights copied from the GPU per expert inside the timed region), {dt:.1f} s"}
+            "sample": f"{sample} decode tokens of {cfg.name}, one oracle call per token (float64 numpy, weights in "
+                      f"host memory), {dt:.1f} s",
+            "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+                     "blas": blas}}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this layer is measured on one MI355X and has no multi-GPU "
-              "path here. Use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: int, kernel_reps: int, dev: str,
+                 keep_inputs: bool = False) -> dict:
     import torch
 
     import mixture_experts_ffn_07_amd as moe
     from moe_synth import CONFIGS, make_inputs
 
-    moe.load()  # raises if the HIP library is missing: there is no other path
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    cfg = CONFIGS[args.workload]
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
+    cfg = CONFIGS[name]
     c = moe.config_from(cfg)
     # enough weight sets that one pass over them exceeds the 256 MB last-level cache 4x over
     per_step = layer_bytes(cfg, min(cfg.n_experts, cfg.tokens * cfg.top_k))
-    sets = args.weight_sets or max(2, min(16, int(4 * 256e6 / per_step) + 1))
+    sets = weight_sets or max(2, min(16, int(4 * 256e6 / per_step) + 1))
     t0 = time.time()
     inputs = [make_inputs(cfg, seed=0, device=dev, weight_set=s) for s in range(sets)]
     for s in range(1, sets):  # one batch of tokens, every weight set
@@ -243,24 +312,23 @@ def main():
                 step_eager(s)
                 i += 1
 
-    use_graph = args.launch == "graph"
-    run(args.warmup, graph=use_graph)
+    use_graph = launch == "graph"
+    run(warmup, graph=use_graph)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record()
-    run(args.steps, offset=args.warmup, graph=use_graph)
+    run(steps, offset=warmup, graph=use_graph)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = ev0.elapsed_time(ev1) / steps
 
     # the other launch form for reference (same steps, from the same weight-set position)
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    n_other = min(args.steps, 200) // sets * sets or sets
+    n_other = min(steps, 200) // sets * sets or sets
     run(sets, graph=not use_graph)
     e0.record()
     run(n_other, graph=not use_graph)
@@ -270,52 +338,95 @@ def main():
 
     # per-kernel durations, HIP events on the library's stream around each kernel
     sums, counts = {}, {}
-    for rep in range(args.kernel_reps):
+    for rep in range(kernel_reps):
         for s in range(sets):
-            for name, ms in moe.moe_layer_forward_timed(c, weights[s], x, t, y, ws):
-                sums[name] = sums.get(name, 0.0) + ms
-                counts[name] = counts.get(name, 0) + 1
+            for kname, ms in moe.moe_layer_forward_timed(c, weights[s], x, t, y, ws):
+                sums[kname] = sums.get(kname, 0.0) + ms
+                counts[kname] = counts.get(kname, 0) + 1
     kernel_ms = {k: sums[k] / counts[k] for k in sums}
     dominant = max(kernel_ms, key=kernel_ms.get)
-    algo = algorithmic_bytes(cfg, touched_avg)
-    achieved = algo[dominant] / (kernel_ms[dominant] * 1e-3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profile(dominant, cfg.name, digest)
+    layer = layer_roofline(cfg, touched_avg, ms_per_step)
+    roof = kernel_roofline(cfg, touched_avg, dominant, kernel_ms[dominant], layer["bound"], digest)
+    out = {
+        "workload": cfg.name, "tokens": t, "ms_per_step": ms_per_step, "tokens_per_s": t / (ms_per_step * 1e-3),
+        "steps": steps, "warmup": warmup,
+        "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
+                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
+                   "expert_weights": ("mxfp8 (e4m3 + e8m0 per 32)" if cfg.expert_format == "mxfp8"
+                                      else "mxfp4 (e2m1 + e8m0 per 32)"), "router_weights": "fp32",
+                   "router_bias": "zipf(1.2)" if cfg.bias == "zipf" else "none",
+                   "pre_ffn_rmsnorm": bool(cfg.norm), "weight_sets_cycled": sets,
+                   "launch": ("hipgraph (one graph per cycle over the weight sets)" if use_graph
+                              else "stream (plain launches on one HIP stream)"),
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "layer": dict(layer, experts_touched_per_step=touched_avg, kernel_ms=kernel_ms,
+                      kernel_source_digest=digest, timed_wall_s=wall, input_gen_s=gen_s,
+                      **{("stream_ms_per_step" if use_graph else "graph_ms_per_step"): other_ms}),
+    }
+    if keep_inputs:
+        out["_inputs"] = inputs[0]
+    del graphs, cycle, inputs, weights, ws, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
-    tokens_per_s = t / (ms_per_step * 1e-3)
-    lb = layer_bytes(cfg, touched_avg)
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this layer is measured on one MI355X and has no multi-GPU "
+              "path here. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_07_amd as moe
+    from moe_synth import CONFIGS
+
+    moe.load()  # raises if the HIP library is missing: there is no other path
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    head = run_workload(args.workload, args.steps, args.warmup, args.launch, args.weight_sets, args.kernel_reps, dev,
+                        keep_inputs=args.cpu_sample > 0)
+    print(f"# {head['workload']}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    head_inputs = head.pop("_inputs", None)
+    others = []
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        if name not in CONFIGS:
+            raise SystemExit(f"unknown workload {name}")
+        r = run_workload(name, min(args.steps, 200), min(args.warmup, 20), args.launch, args.weight_sets,
+                         min(args.kernel_reps, 3), dev)
+        print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        others.append(r)
+
+    cfg = CONFIGS[args.workload]
     result = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
-                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
-                   "expert_weights": ("mxfp8 (e4m3 + e8m0 per 32)" if cfg.expert_format == "mxfp8"
-                                      else "mxfp4 (e2m1 + e8m0 per 32)"), "router_weights": "fp32",
-                   "pre_ffn_rmsnorm": bool(cfg.norm),
-                   "weight_sets_cycled": sets, "launch": ("hipgraph (one graph per cycle over the weight sets)" if use_graph
-                                                       else "stream (plain launches on one HIP stream)"),
-                   "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
-                     "kernel_ms": kernel_ms[dominant], "algorithmic_bytes": algo[dominant]},
-        "layer": {"algorithmic_bytes": lb, "hbm_frac": lb / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                  "flops": layer_flops(cfg), "experts_touched_per_step": touched_avg,
-                  ("stream_ms_per_step" if use_graph else "graph_ms_per_step"): other_ms, "kernel_ms": kernel_ms,
-                  "kernel_source_digest": digest, "timed_wall_s": wall, "input_gen_s": gen_s},
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "layer": head["layer"],
+        "workloads": [{k: v for k, v in r.items()} for r in [head] + others],
         "cpu_baseline": None,
     }
     if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(cfg, inputs[0], args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, head_inputs, args.cpu_sample)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
