@@ -382,7 +382,7 @@ def combine(y_slot, slot_pos, w, y_shared, top_k: int) -> np.ndarray:
 def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn,
                   top_k: int, route_scale: float, swiglu_limit: float,
                   tokens=None, selections=None, norm_gamma=None, norm_eps: float = 1e-20,
-                  expert_format: str = "mxfp4") -> dict:
+                  expert_format: str = "mxfp4", workers: int = 1) -> dict:
     """The whole layer for the rows ``tokens`` of ``x_bits`` (all rows if None).
 
     ``gu_q`` ... ``dn_s`` only need to support ``[e]`` (per-expert arrays of
@@ -392,7 +392,9 @@ def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, 
 
     With ``norm_gamma`` (bf16 bits [H]) the rows are first RMS-normalised
     (``rmsnorm``) and the layer runs on the result.  ``expert_format`` names
-    the routed experts' codec, "mxfp4" or "mxfp8".
+    the routed experts' codec, "mxfp4" or "mxfp8".  ``workers`` > 1 runs the
+    selected experts on that many threads (each writes only its own rows; every
+    expert's arithmetic is the same as with one thread).
 
     Returns the router outputs, the permutation, ``h_slot`` [T*k, I] and
     ``y_slot`` [T*k, H] in position order, ``y_shared`` [T, H] and ``y`` [T, H].
@@ -412,23 +414,27 @@ def layer_forward(x_bits, router_w, router_bias, gu_q, gu_s, dn_q, dn_s, sh_gu, 
     n_experts = np.asarray(router_w).shape[0]
     p = permute(idx, n_experts)
     x = bf16_bits_to_f64(x_bits)
-    inter = None
-    h_slot = y_slot = None
-    for e in range(n_experts):
+    per_byte = EXPERT_FORMATS[expert_format][1]
+    inter = (dn_q.shape[-1] if hasattr(dn_q, "shape") else np.asarray(dn_q[0]).shape[-1]) * per_byte
+    h_slot = np.zeros((t_count * top_k, inter))
+    y_slot = np.zeros((t_count * top_k, hidden))
+
+    def one_expert(e):
         lo, hi = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
-        if hi == lo:
-            continue
-        per_byte = EXPERT_FORMATS[expert_format][1]
-        w_gu, w_dn = routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e, hidden, np.asarray(dn_q[e]).shape[1] * per_byte,
-                                           expert_format)
-        if inter is None:
-            inter = w_dn.shape[1]
-            h_slot = np.zeros((t_count * top_k, inter))
-            y_slot = np.zeros((t_count * top_k, hidden))
+        w_gu, w_dn = routed_expert_weights(gu_q, gu_s, dn_q, dn_s, e, hidden, inter, expert_format)
         rows = p["sorted_slots"][lo:hi] // top_k
         h_slot[lo:hi], y_slot[lo:hi] = expert_mlp(x[rows], w_gu, w_dn, swiglu_limit)
-    if y_slot is None:
-        y_slot = np.zeros((0, hidden))
+
+    used = [e for e in range(n_experts) if p["expert_offsets"][e + 1] > p["expert_offsets"][e]]
+    if workers > 1 and len(used) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(one_expert, used))
+    else:
+        for e in used:
+            one_expert(e)
     if sh_gu is not None:
         h_sh, y_sh = shared_expert(x_bits, sh_gu, sh_dn, swiglu_limit)
     else:

@@ -11,6 +11,8 @@ oracle's result for that selection.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -74,6 +76,33 @@ def match_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, ref: dict, route_scale
             assert abs(gpu_w[t, j] - w_ref[e]) <= w_tol * max(1.0, abs(route_scale)), \
                 f"token {t} expert {e}: weight {gpu_w[t, j]} vs {w_ref[e]}"
     return alt
+
+
+#: threads the oracle may use for the experts of a large layer (the host's share of cores)
+ORACLE_WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def check_layer(inp, tokens=None, gpu=None, workers: int = 1):
+    """Run the GPU layer (or take its results) and compare rows `tokens` (all if None) with the oracle.
+
+    Near-tie tokens whose GPU selection is another valid one are compared with the oracle's result for that
+    selection.  Returns (stats, oracle result, {row: selection} of those tokens)."""
+    y, idx, w = gpu if gpu is not None else gpu_layer(inp)
+    cfg = inp.cfg
+    args = inp.oracle_args()
+    sel_rows = np.arange(cfg.tokens) if tokens is None else np.asarray(tokens)
+    ref = oracle.layer_forward(**args, tokens=sel_rows, workers=workers)
+    g_idx = idx.cpu().numpy()[sel_rows]
+    g_w = w.cpu().numpy()[sel_rows]
+    alt = match_routing(g_idx, g_w, ref, cfg.route_scale)
+    y_ref = ref["y"]
+    if alt:  # near-tie tokens: the oracle's result for the selection the GPU made
+        rows = sorted(alt)
+        y_ref = y_ref.copy()
+        y_ref[rows] = oracle.layer_forward(**args, tokens=sel_rows[rows], selections=[alt[r] for r in rows],
+                                           workers=workers)["y"]
+    stats = assert_bar(bf16_to_f64(y)[sel_rows], y_ref, f"{cfg.name} y")
+    return stats, ref, alt
 
 
 # ------------------------------------------------------------------ GPU calls through the C ABI

@@ -1,0 +1,84 @@
+"""Whole-tensor parity at the full layer sizes, determinism at full size, and the clamp on every kernel path.
+
+* The 64-, 4096- and 16384-token layers are compared with the oracle on every output row (the oracle runs the
+  selected experts on several host threads).
+* Two runs of the one-token and the 4096-token layers give identical bits (outputs, expert ids, weights).
+* Clamp stress: hidden states scaled so that the gate pre-activation passes the limit on a good share of its
+  elements, in the routed experts and in the shared expert, at token counts and shapes that select each kernel
+  path of the library (one and two tokens: the vector-ALU streaming kernels; five: the MFMA GEMVs; 64 at full
+  size: 32-row grouped tiles; 200: 128-row tiles and the K-sliced shared expert; 1100 and 4096: the dense shared
+  expert), for MXFP4 and MXFP8 expert weights.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_synth import CONFIGS, make_inputs
+
+from parity import ORACLE_WORKERS, check_layer, gpu_layer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("name", ["decode_t64_h5120_e384", "prefill_t4096_h5120_e384", "skew_t16384_h5120_e128",
+                                  "verify_t320_h5120_e384"])
+def test_layer_full_tensor(name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    gpu = gpu_layer(inp)
+    load = np.bincount(gpu[1].cpu().numpy().reshape(-1), minlength=cfg.n_experts)
+    stats, ref, alt = check_layer(inp, gpu=gpu, workers=ORACLE_WORKERS)
+    print(f"{name}: all {cfg.tokens} tokens {stats}, experts touched {np.count_nonzero(load)}, hottest load "
+          f"{load.max()} ({load.max() / load.mean():.1f}x mean), near-tie alternatives {len(alt)}")
+
+
+@pytest.mark.parametrize("name", ["decode_t1_h5120_e384", "prefill_t4096_h5120_e384"])
+def test_layer_deterministic_full_size(name):
+    inp = make_inputs(CONFIGS[name], seed=0, device=DEV)
+    a = gpu_layer(inp)
+    b = gpu_layer(inp)
+    for what, u, v in zip(("y", "idx", "w"), a, b):
+        assert torch.equal(u, v), f"{name}: {what} differs between two runs"
+
+
+FULL = CONFIGS["decode_t1_h5120_e384"]
+TINY = CONFIGS["tiny_t8_h512_e32"]
+# x std giving gate pre-activations of std ~14 (full size) and ~18 (tiny): the clamp at 10 fires on ~24%
+CLAMP_CASES = [
+    ("full", 1), ("full", 2), ("full", 5), ("full", 64),
+    ("tiny", 200), ("tiny", 1100), ("tiny", 4096),
+]
+
+
+def _clamp_cfg(shape, tokens, fmt):
+    if shape == "full":
+        return FULL.with_(tokens=tokens, x_std=10.0, expert_format=fmt)
+    return TINY.with_(tokens=tokens, x_std=40.0, expert_format=fmt)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("shape,tokens", CLAMP_CASES)
+def test_layer_clamp_stress_every_path(shape, tokens, fmt):
+    cfg = _clamp_cfg(shape, tokens, fmt)
+    inp = make_inputs(cfg, seed=17, device=DEV)
+    stats, ref, alt = check_layer(inp, workers=ORACLE_WORKERS)
+    a = inp.oracle_args()
+    x = oracle.bf16_bits_to_f64(a["x_bits"])
+    lim = cfg.swiglu_limit
+    # routed: the first token's first expert (the rows the GPU computed for it went through the clamp)
+    e = int(ref["idx"][0, 0])
+    wgu, _ = oracle.routed_expert_weights(a["gu_q"], a["gu_s"], a["dn_q"], a["dn_s"], e, cfg.hidden, cfg.inter,
+                                          cfg.expert_format)
+    rows = x[: min(cfg.tokens, 64)]
+    g = rows @ wgu[:cfg.inter].T
+    u = rows @ wgu[cfg.inter:].T
+    assert np.mean(g > lim) > 0.1 and np.mean(np.abs(u) > lim) > 0.1, (np.mean(g > lim), np.mean(np.abs(u) > lim))
+    # shared expert
+    sg = oracle.bf16_bits_to_f64(a["sh_gu"])
+    gs = rows @ sg[:cfg.shared_inter].T
+    assert np.mean(gs > lim) > 0.1
+    print(f"clamp {shape} T={tokens} {fmt}: {stats}, routed gate clamped {np.mean(g > lim):.2f}, "
+          f"shared {np.mean(gs > lim):.2f}, near-tie alternatives {len(alt)}")

@@ -13,8 +13,8 @@ import mixture_experts_ffn_07_amd as moe
 import oracle
 from moe_synth import CONFIGS, make_inputs, make_router_inputs
 
-from parity import (TIE_TOL, assert_bar, bf16_to_f64, gpu_expert_ffn, gpu_layer, gpu_permute, gpu_route,
-                    match_routing)
+from parity import (ORACLE_WORKERS, TIE_TOL, assert_bar, bf16_to_f64, check_layer, gpu_expert_ffn, gpu_layer,
+                    gpu_permute, gpu_route, match_routing)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -27,20 +27,7 @@ def _oracle_route(cfg, x, router_w, bias):
 
 def _check_layer(inp, tokens=None, gpu=None):
     """Run the GPU layer (or take its results) and compare rows `tokens` (all if None) with the oracle."""
-    y, idx, w = gpu if gpu is not None else gpu_layer(inp)
-    cfg = inp.cfg
-    args = inp.oracle_args()
-    sel_rows = np.arange(cfg.tokens) if tokens is None else np.asarray(tokens)
-    ref = oracle.layer_forward(**args, tokens=sel_rows)
-    g_idx = idx.cpu().numpy()[sel_rows]
-    g_w = w.cpu().numpy()[sel_rows]
-    alt = match_routing(g_idx, g_w, ref, cfg.route_scale)
-    y_ref = ref["y"]
-    if alt:  # near-tie tokens: the oracle's result for the selection the GPU made
-        sels = [alt.get(i, ref["idx"][i].tolist()) for i in range(len(sel_rows))]
-        y_ref = oracle.layer_forward(**args, tokens=sel_rows, selections=sels)["y"]
-    stats = assert_bar(bf16_to_f64(y)[sel_rows], y_ref, f"{cfg.name} y")
-    return stats, ref, alt
+    return check_layer(inp, tokens=tokens, gpu=gpu, workers=ORACLE_WORKERS)
 
 
 # ------------------------------------------------------------------ router

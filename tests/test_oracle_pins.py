@@ -339,6 +339,17 @@ def test_layer_against_per_token_direct_sum():
         assert np.allclose(out["y"][t], y, rtol=1e-12, atol=1e-12)
 
 
+def test_layer_threads_give_the_single_thread_result():
+    """Experts run on several threads write only their own rows: the same bits as one thread, and the per-token
+    direct sum above still holds through them."""
+    inp = _tiny_inputs(tokens=40)
+    a = inp.oracle_args()
+    one = oracle.layer_forward(**a)
+    many = oracle.layer_forward(**a, workers=4)
+    for key in ("idx", "w", "h_slot", "y_slot", "y_shared", "y"):
+        assert np.array_equal(one[key], many[key]), key
+
+
 # ---------------------------------------------------------------- whole-layer invariants
 
 def test_zero_input_gives_zero_output():
