@@ -129,6 +129,9 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
         "route_permute": t * e * 4 + n * 8 + n * 4 * 2 + (e + 1) * 4,
         "gate_up": touched * gu_expert + 2 * i_s * h * 2 + t * h * 2 + n * i * 2 + t * i_s * 2,
         "down": touched * dn_expert + h * i_s * 2 + n * i * 2 + t * i_s * 2 + n * h * 2 + t * h * 2,
+        # many tokens: x and h rows to two-term MXFP6 records (208 bytes per 128 values)
+        "mx6_x": t * h * 2 + t * h * 208 / 128,
+        "mx6_h": n * i * 2 + n * i * 208 / 128,
     }
 
 
@@ -142,7 +145,11 @@ def kernel_flops(cfg) -> dict:
             "router_logits": 2.0 * t * e * h}
 
 
-# the arithmetic each matrix kernel runs in, and that type's published dense peak (TFLOP/s)
+# the arithmetic each matrix kernel runs in, and that type's published dense peak (TFLOP/s); the routed GEMMs
+# for many tokens with MXFP4 experts run on two-term MXFP6 activations (the x and h records, kernels mx6_x and
+# mx6_h): two FP4-rate block-scaled MFMAs per step, so they reach at most half the FP4 peak in algorithmic flops
+KERNEL_DTYPE_MX6 = {"routed_gate_up": ("two-term MXFP6 x MXFP4 block-scaled MFMA", FP4_PEAK_TFLOPS),
+                    "routed_down": ("two-term MXFP6 x MXFP4 block-scaled MFMA", FP4_PEAK_TFLOPS)}
 KERNEL_DTYPE = {"routed_gate_up": ("bf16 MFMA on exactly dequantised expert weights", BF16_PEAK_TFLOPS),
                 "routed_down": ("bf16 MFMA on exactly dequantised expert weights", BF16_PEAK_TFLOPS),
                 "shared_gate_up": ("bf16 MFMA", BF16_PEAK_TFLOPS), "shared_down": ("bf16 MFMA", BF16_PEAK_TFLOPS),
@@ -184,14 +191,15 @@ def layer_roofline(cfg, touched: float, ms: float) -> dict:
             "roofline_frac": max(t_hbm, t_mfma) / s}
 
 
-def kernel_roofline(cfg, touched: float, kernel: str, kernel_ms: float, bound: str, digest: str) -> dict:
+def kernel_roofline(cfg, touched: float, kernel: str, kernel_ms: float, bound: str, digest: str,
+                    mx6: bool = False) -> dict:
     """Roofline entry of one kernel: algorithmic bytes (HBM-bound layer) or flops (MFMA-bound layer) over its
     event-timed duration, against the published peak of that resource (for flops, of the kernel's own dtype)."""
     algo = algorithmic_bytes(cfg, touched)
     flops = kernel_flops(cfg)
     s = kernel_ms * 1e-3
     if bound == "mfma" and kernel in flops:
-        dtype, peak = KERNEL_DTYPE[kernel]
+        dtype, peak = (KERNEL_DTYPE_MX6 if mx6 and kernel in KERNEL_DTYPE_MX6 else KERNEL_DTYPE)[kernel]
         ach = flops[kernel] / s / 1e12
         out = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                "dtype": dtype, "flops": flops[kernel], "fp4_peak_frac": ach / FP4_PEAK_TFLOPS}
@@ -347,7 +355,8 @@ def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: i
     dominant = max(kernel_ms, key=kernel_ms.get)
     digest = kernel_source_digest()
     layer = layer_roofline(cfg, touched_avg, ms_per_step)
-    roof = kernel_roofline(cfg, touched_avg, dominant, kernel_ms[dominant], layer["bound"], digest)
+    roof = kernel_roofline(cfg, touched_avg, dominant, kernel_ms[dominant], layer["bound"], digest,
+                           mx6="mx6_x" in kernel_ms)
     out = {
         "workload": cfg.name, "tokens": t, "ms_per_step": ms_per_step, "tokens_per_s": t / (ms_per_step * 1e-3),
         "steps": steps, "warmup": warmup,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
 OBJ_DIR = os.path.join(os.path.dirname(PKG), "_build")
 SOURCES = ["moe_ffn.cpp", "router.hip", "permute.hip", "expert_gemm.hip", "expert_gemv.hip", "decode.hip",
-           "expert_valu.hip", "combine.hip", "norm.hip"]
+           "expert_valu.hip", "combine.hip", "norm.hip", "expert_mx6.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: hipcc must not form packed fp32 VALU ops on its own.

@@ -1,0 +1,400 @@
+// Routed grouped GEMMs for many tokens on gfx950's block-scaled matrix
+// instruction: two-term MXFP6 activations (mx6_device.h) times the experts'
+// MXFP4 weights as stored (E2M1 codes, E8M0 scale per 32 along K: Strata
+// DEEPSEEK41 notes, opening paragraph; the MAX API's float4_e2m1fnx2),
+// v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation, the clamped
+// SwiGLU (swiglu_limit, DeepseekV41Config) in the gate/up epilogue.
+//
+// FP6 x FP4 runs at the FP4 rate on gfx950 (measured 7.9 PFLOP/s on a
+// register-only probe, against 4.4 for FP8 x FP4 and 2.3 for bf16), so the
+// two terms cost two FP4-rate instructions per 16 x 16 x 128 step: 1.7x the
+// bf16 rate on exactly dequantised weights, with the weights never expanded.
+//
+// Block: 4 waves (one per SIMD), a tile of up to 96 rows of one expert
+// against 512 weight rows (gate/up: 256 columns of h, the gate and up rows
+// of each; down: 512 output columns).  Wave w owns 128 of the weight rows as
+// 8 MFMA column tiles and every row tile, so its accumulators take up to
+// 6 x 8 x 4 registers (the wave runs alone on its SIMD, 512 registers; 128
+// rows would need all 256 accumulation registers and spill the operands).
+//   * Weights go from memory straight to registers (each weight byte is read
+//     by one wave only), two chunks ahead of the MFMAs.
+//   * The tile's activation records go global -> registers -> LDS (two
+//     stages), one chunk ahead, and every wave reads its MFMA operands from
+//     LDS: the record layout is the operand layout, so a row tile costs five
+//     LDS reads per lane and chunk (no bank conflicts on the 16-byte reads:
+//     the 208-byte row stride puts 8 consecutive rows on 8 different bank
+//     quads).
+// Loads are ordinary buffer loads whose waits the compiler places.  The
+// per-lane offset of a row past the end (weight rows beyond N, activation
+// pieces beyond the tile) is kOob, which the buffer range check turns into a
+// zero; the chunk enters as the scalar offset, which that check does not
+// cover, so chunk indices are always clamped into the matrix.
+#include "moe_device.h"
+#include "moe_internal.h"
+#include "mx_device.h"
+#include "mx6_device.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x32_t __attribute__((__vector_size__(32 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef uint32_t u32x16_t __attribute__((__vector_size__(16 * sizeof(uint32_t))));
+
+// E8M0 byte of 2^(floor(log2 amax) - 2), 127 for amax == 0, held in [0, 254].
+__device__ __forceinline__ int mx6_scale_code(float amax) {
+  if (!(amax > 0.f)) return 127;
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xff);  // biased floor(log2 amax) for normal amax
+  return min(max(ex - 2, 0), 254);
+}
+
+// ============================================================== bf16 rows -> two-term MXFP6 records
+// One thread per (row, 128-wide chunk): reads 256 bytes, writes one record.
+__global__ __launch_bounds__(256) void mx6_rows_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int rows,
+                                                       int K, uint8_t* __restrict__ dst, int64_t ld_dst) {
+  const int chunks = K / 128;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * chunks) return;
+  const int r = (int)(t / chunks), c = (int)(t % chunks);
+  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src + (int64_t)r * ld_src + (int64_t)c * 128);
+  u32x4_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load(s + i);
+  uint32_t rec[52];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float x[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        x[8 * q + 2 * w] = __uint_as_float(v[4 * g + q][w] << 16);
+        x[8 * q + 2 * w + 1] = __uint_as_float(v[4 * g + q][w] & 0xffff0000u);
+      }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    const int c1 = mx6_scale_code(amax);
+    const float s1 = __uint_as_float((uint32_t)c1 << 23);
+    u32x16_t xw;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) xw[4 * q + w] = v[4 * g + q][w];
+    const bf16x32_t xb = __builtin_bit_cast(bf16x32_t, xw);  // value 2 w in the low half of dword w
+    // converts divide by the scale, round to nearest even, saturate at +-7.5;
+    // the bf16 form packs value i into bits [6 i, 6 i + 6)
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xb, s1);
+    const auto hv = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(hi, s1);
+    f32x16_t ev, od;  // the f32 form interleaves its two halves: value 2 i from ev, 2 i + 1 from od
+    float amax_r = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ev[i] = x[2 * i] - hv[2 * i];
+      od[i] = x[2 * i + 1] - hv[2 * i + 1];
+      amax_r = fmaxf(amax_r, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+    }
+    const int c2 = mx6_scale_code(amax_r);
+    const auto lo = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, __uint_as_float((uint32_t)c2 << 23));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      rec[4 * g + d] = (uint32_t)hi[d];
+      rec[24 + 4 * g + d] = (uint32_t)lo[d];
+    }
+    rec[16 + 2 * g] = (uint32_t)hi[4];
+    rec[17 + 2 * g] = (uint32_t)hi[5];
+    rec[40 + 2 * g] = (uint32_t)lo[4];
+    rec[41 + 2 * g] = (uint32_t)lo[5];
+    rec[48 + g] = (uint32_t)c1 | ((uint32_t)c2 << 8);
+  }
+  u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + (int64_t)r * ld_dst + (int64_t)c * kMx6Rec);
+#pragma unroll
+  for (int i = 0; i < 13; ++i) d[i] = u32x4_t{rec[4 * i], rec[4 * i + 1], rec[4 * i + 2], rec[4 * i + 3]};
+}
+
+// ============================================================== grouped GEMM
+constexpr int kMx6Rows = kMx6TileRows;             // rows per tile
+// bytes per LDS stage: the tile's records, rounded up to whole rounds of 256
+// 16-byte pieces (every thread writes the same number of pieces, the ones
+// past the records to slots nothing reads, so the writes need no branch)
+constexpr int kMx6Stage = (kMx6Rows * kMx6Rec + 4095) / 4096 * 4096;
+
+__device__ __forceinline__ f32x4_t mfma_f6f4(const i32x8_t& a, const u32x4_t& b, int sa_word, int sb, f32x4_t c,
+                                             int term) {
+  const i32x8_t bw = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // A: FP6 E2M3 (format 2), B: FP4 E2M1 (format 4); the A scale byte is byte `term` of sa_word
+  return term == 0 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 4, 0, sa_word, 0, sb)
+                   : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 4, 1, sa_word, 0, sb);
+}
+
+// Weight scale bytes reach LDS in groups of kMx6SGroup chunks: per weight
+// row of the block 32 contiguous bytes (4 per chunk), two 16-byte pieces per
+// row, instead of one byte per lane, row and chunk from memory.  The byte
+// loads touched a cache line per row and chunk, as many as the weight codes
+// themselves, and measured 35% of the kernel's time.
+constexpr int kMx6SGroup = 8;
+constexpr int kMx6BlockRows = 512;                         // weight rows per block
+constexpr int kMx6SStage = kMx6BlockRows * 4 * kMx6SGroup;  // bytes per scale group in LDS
+
+template <bool SWIGLU, int MT>
+__device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sgrp, const int32_t* src_row,
+                                         int e, int m_begin, int rows, int n0) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int K = p.K, nchunks = K / 128;
+  constexpr int kRowsRun = 16 * MT;
+  constexpr int kPieces = kRowsRun * 13;                    // 16-byte pieces of the tile per chunk
+  constexpr int kPerThread = (kPieces + 255) / 256;
+
+  // activation pieces this thread stages: piece q = tid + 256 i of the
+  // stage (row q / 13, part q % 13); LDS byte 16 q
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)p.a_rows * p.a_stride));
+  uint32_t a_off[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int q = (int)threadIdx.x + 256 * i;
+    a_off[i] = q < kPieces ? (uint32_t)src_row[q / 13] * (uint32_t)p.a_stride + 16u * (uint32_t)(q % 13) : kOob;
+  }
+  // weight rows of this lane's 8 column tiles (expert-relative)
+  const int64_t qbytes = p.b_expert_rows * (K / 2), sbytes = p.b_expert_rows * (K / 32);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, (uint32_t)qbytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sbytes, (uint32_t)sbytes);
+  // block row r (= 128 w + 16 j + n: wave w, column tile j, lane column n)
+  // -> expert-relative weight row, or -1 past N
+  auto weight_row = [&](int r) {
+    const int w = r >> 7, j = (r >> 4) & 7, nn = r & 15;
+    if constexpr (SWIGLU) {
+      const int col = n0 + 64 * w + 16 * (j & 3) + nn;
+      return col < p.N ? col + (j >> 2) * p.b_row_second : -1;
+    } else {
+      const int col = n0 + 128 * w + 16 * j + nn;
+      return col < p.N ? col : -1;
+    }
+  };
+  uint32_t q_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = weight_row(128 * wave + 16 * j + n);
+    q_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)g : kOob;
+  }
+  // scale pieces this thread stages: piece i = tid + 256 i of a group (block
+  // row (tid + 256 i) / 2, half (tid + 256 i) % 2), LDS byte 16 (tid + 256 i)
+  constexpr int kSPieces = kMx6SStage / 16 / 256;
+  uint32_t s_off[kSPieces];
+#pragma unroll
+  for (int i = 0; i < kSPieces; ++i) {
+    const int q = (int)threadIdx.x + 256 * i;
+    const int row = weight_row(q >> 1);
+    s_off[i] = row >= 0 ? (uint32_t)row * (uint32_t)(K / 32) + 16u * (uint32_t)(q & 1) : kOob;
+  }
+
+  // NB weight buffers: the weights of chunk c + NB - 1 are issued while chunk
+  // c is computed (more buffers for fewer row tiles, whose chunks are short)
+  constexpr int NB = 4;
+  u32x4_t areg[2][kPerThread];
+  u32x4_t bq[NB][8];
+  u32x4_t sreg[kSPieces];
+  f32x4_t acc[MT][8];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // per-lane offsets stay fixed; the chunk enters as the scalar offset
+  // (a piece or row past the end has a per-lane offset of kOob and reads zero)
+  auto load_a = [&](int c, int abuf) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      areg[abuf][i] =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)a_off[i], kMx6Rec * c, 0));
+  };
+  // no branch around the writes: a divergent one makes the compiler wait for
+  // every load in flight before the write
+  auto store_a = [&](int s, int abuf) {
+    uint8_t* st = stage + s * kMx6Stage + 16 * threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) *reinterpret_cast<u32x4_t*>(st + 4096 * i) = areg[abuf][i];
+  };
+  auto load_b = [&](int c, int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bq[buf][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c, 0));
+  };
+  // scale group G (chunks [8 G, 8 G + 8)): the group enters the per-lane
+  // offset, so pieces past the matrix read zero; bytes past a row's end (the
+  // last group of a K that is not a multiple of 1024) are never used
+  auto load_s = [&](int G) {
+#pragma unroll
+    for (int i = 0; i < kSPieces; ++i)
+      sreg[i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       rs, (int)(s_off[i] == kOob ? kOob : s_off[i] + (uint32_t)(4 * kMx6SGroup * G)), 0, 0));
+  };
+  auto store_s = [&](int slot) {
+    uint8_t* st = sgrp + slot * kMx6SStage + 16 * threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kSPieces; ++i) *reinterpret_cast<u32x4_t*>(st + 4096 * i) = sreg[i];
+  };
+  // A operands of one row tile: the hi and lo terms and the scale word
+  struct AFrag {
+    i32x8_t hi, lo;
+    int sc;
+  };
+  auto read_a = [&](const uint8_t* rec) {
+    const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(rec + 16 * g);
+    const u32x2_t h1 = *reinterpret_cast<const u32x2_t*>(rec + 64 + 8 * g);
+    const u32x4_t l0 = *reinterpret_cast<const u32x4_t*>(rec + 96 + 16 * g);
+    const u32x2_t l1 = *reinterpret_cast<const u32x2_t*>(rec + 160 + 8 * g);
+    AFrag f;
+    f.sc = *reinterpret_cast<const int*>(rec + 192 + 4 * g);
+    f.hi = i32x8_t{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], 0, 0};
+    f.lo = i32x8_t{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], 0, 0};
+    return f;
+  };
+  // row tile m + 1's LDS reads are issued before row tile m's MFMAs (two
+  // operand sets live), fenced so the compiler does not hoist further
+  auto compute = [&](int s, int buf, int c) {
+    // this lane's scale byte of each column tile: block row 128 w + 16 j + n, chunk c % 8, lane group g
+    const uint8_t* sb_row = sgrp + ((c / kMx6SGroup) & 1) * kMx6SStage + (128 * wave + n) * 32 + 4 * (c % kMx6SGroup) + g;
+    int sb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sb[j] = sb_row[16 * 32 * j];
+    const uint8_t* st = stage + s * kMx6Stage + n * kMx6Rec;
+    AFrag cur = read_a(st);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      AFrag nxt;
+      if (m + 1 < MT) nxt = read_a(st + (m + 1) * 16 * kMx6Rec);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[m][j] = mfma_f6f4(cur.hi, bq[buf][j], cur.sc, sb[j], acc[m][j], 0);
+        acc[m][j] = mfma_f6f4(cur.lo, bq[buf][j], cur.sc, sb[j], acc[m][j], 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + 1 < MT) cur = nxt;
+    }
+  };
+  // One chunk c (weights in register buffer c % NB, activations in LDS
+  // stage c % 2): publish chunk c + 1's activations (issued two steps ago,
+  // register buffer (c + 1) % 2) to the other LDS stage, reuse that buffer
+  // for chunk c + 3's activation loads, issue chunk c + NB - 1's weight
+  // loads, compute chunk c.  Loads complete in issue order, so the wait for
+  // chunk c + 1's activations also covers every load issued before them:
+  // the weights of chunk c and older, never newer ones.  Weights thus get
+  // NB - 1 steps to arrive and activations two.  Scale group G + 1 is issued
+  // in the first step of group G (after the activation loads) and published
+  // in its fifth, to the LDS slot group G - 1 used.  The last steps load the
+  // last chunk (group) again instead of chunks past the end (the scalar
+  // offset is outside the buffer range check) and never use it, so the loop
+  // has no branch but the compute guard of its last steps.
+  const int last = nchunks - 1, last_group = last / kMx6SGroup;
+  auto step = [&](int c, int buf, int abuf, int u) {
+    store_a((c + 1) & 1, abuf ^ 1);
+    if (u == kMx6SGroup / 2) store_s((c / kMx6SGroup + 1) & 1);
+    load_a(min(c + 3, last), abuf ^ 1);
+    if (u == 0) load_s(min(c / kMx6SGroup + 1, last_group));
+    load_b(min(c + NB - 1, last), (buf + NB - 1) % NB);
+    if (c < nchunks) compute(c & 1, buf, c);
+    __syncthreads();
+  };
+
+  load_s(0);
+  load_a(0, 0);
+  load_a(min(1, last), 1);
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) load_b(min(b, last), b);
+  store_s(0);
+  store_a(0, 0);
+  load_a(min(2, last), 0);
+  __syncthreads();
+  static_assert(kMx6SGroup % NB == 0 && kMx6SGroup % 2 == 0, "a loop iteration is one scale group");
+  for (int c = 0; c < nchunks; c += kMx6SGroup) {
+#pragma unroll
+    for (int u = 0; u < kMx6SGroup; ++u) step(c + u, u % NB, u % 2, u);
+  }
+
+  // epilogue: lane 16 g + n holds rows 4 g + i of each row tile, column n of each column tile
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * m + 4 * g + i;
+      if (r >= rows) continue;
+      uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
+      if constexpr (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + 64 * wave + 16 * j + n;
+          if (col < p.N) crow[col] = f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + 4][i], p.limit));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = n0 + 128 * wave + 16 * j + n;
+          if (col < p.N) crow[col] = f32_to_bf16(acc[m][j][i]);
+        }
+      }
+    }
+}
+
+// XCD-aware block order (as the pipelined kernels): block b runs on XCD
+// b % 8, which takes the tiles t with t % 8 == its index and runs a tile's
+// column blocks back to back, so the tile's activation records stay in that
+// XCD's L2 while its column blocks read them.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void expert_mx6_kernel(const Mx6Params p, int n_tiles, int col_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kMx6Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t sgrp[2 * kMx6SStage];
+  __shared__ int32_t src_row[kMx6Rows];
+  const int b = (int)blockIdx.x, x = b & 7, q = b >> 3;
+  const int tile = 8 * (q / col_blocks) + x, cb = q % col_blocks;
+  if (tile >= n_tiles || tile >= *p.tile_count) return;
+  const GemmTile tl = p.tiles[tile];
+  const int m_begin = tl.m_begin, rows = min(tl.m_end, tl.m_begin + kMx6Rows) - tl.m_begin;
+  if (rows <= 0) return;
+  for (int r = threadIdx.x; r < kMx6Rows; r += 256) {
+    const int pos = m_begin + min(r, rows - 1);
+    const int src = p.gather ? p.gather[pos] / p.gather_div : pos;
+    src_row[r] = min(max(src, 0), p.a_rows - 1);
+  }
+  __syncthreads();
+  const int n0 = cb * (SWIGLU ? 256 : 512);
+  const int mt = min(kMx6Rows / 16, 2 * ((rows + 31) / 32));
+  switch (mt) {
+    case 2: mx6_tile<SWIGLU, 2>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
+    case 4: mx6_tile<SWIGLU, 4>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
+    default: mx6_tile<SWIGLU, 6>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
+  }
+}
+
+}  // namespace
+
+bool mx6_supported(int hidden, int inter) { return hidden % 128 == 0 && inter % 128 == 0; }
+
+int mx6_tile_rows() { return kMx6TileRows; }
+
+int64_t mx6_bytes(int64_t rows, int K) { return rows * mx6_row_bytes(K); }
+
+hipError_t launch_mx6_rows(const uint16_t* src, int64_t ld_src, int rows, int K, uint8_t* dst, hipStream_t stream) {
+  const int64_t threads = (int64_t)rows * (K / 128);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx6_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, src, ld_src, rows,
+                     K, dst, mx6_row_bytes(K));
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_mx6(const Mx6Params& p, bool swiglu, int n_tiles, hipStream_t stream) {
+  const int cols = swiglu ? 256 : 512;
+  const int col_blocks = (p.N + cols - 1) / cols;
+  const dim3 grid((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
+  if (swiglu)
+    hipLaunchKernelGGL(expert_mx6_kernel<true>, grid, dim3(256), 0, stream, p, n_tiles, col_blocks);
+  else
+    hipLaunchKernelGGL(expert_mx6_kernel<false>, grid, dim3(256), 0, stream, p, n_tiles, col_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -202,7 +202,8 @@ struct WsLayout {
   bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
                               // down; routed down + combine
   bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
-  Region x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
+  bool mx6 = false;             // many tokens, MXFP4: routed GEMMs on two-term MXFP6 activations (expert_mx6.hip)
+  Region xq, hq, x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh, sh_part;
   size_t total = 0;
 };
@@ -236,6 +237,10 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
     L.bm = 16 * L.gemm_mt;
+    // 128-row tiles of MXFP4 experts with K multiples of 128: the block-scaled
+    // MFMA on two-term MXFP6 rows, in tiles of its own height
+    L.mx6 = L.fmt == moe::kWMxfp4 && L.bm == 128 && moe::mx6_supported(c->hidden, c->inter);
+    if (L.mx6) L.bm = moe::mx6_tile_rows();
   }
   L.max_tiles = moe::max_gemm_tiles(n, E, L.bm);
   {
@@ -285,6 +290,8 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
   take(L.offsets, sizeof(int32_t) * (E + 1));
   take(L.sorted, sizeof(int32_t) * n);
   take(L.slot_pos, sizeof(int32_t) * n);
+  take(L.xq, L.mx6 ? (size_t)moe::mx6_bytes(tokens, c->hidden) : 0);
+  take(L.hq, L.mx6 ? (size_t)moe::mx6_bytes(n, c->inter) : 0);
   take(L.h, sizeof(uint16_t) * n * c->inter);
   take(L.y_slot, sizeof(uint16_t) * n * c->hidden);
   const int64_t is = c->n_shared ? c->shared_inter : 0;
@@ -734,6 +741,9 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
   return MOE_OK;
 }
 
+moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, uint16_t* y_shared,
+                      void* ws, const WsLayout& L, hipStream_t st, Timeline* tl);
+
 // Routed gate/up + down over the tile table in ws, then the shared expert.
 moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
                        const int32_t* sorted, uint16_t* y_slot, uint16_t* y_shared, void* ws, const WsLayout& L,
@@ -742,6 +752,56 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   uint16_t* h = at<uint16_t>(ws, L.h);
   // few-token expert kernels exist for MXFP4 weights; MXFP8 ones take the grouped GEMM
   if (L.decode && L.fmt == moe::kWMxfp4) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
+  hipError_t err;
+  if (L.mx6) {
+    const int n = (int)(T * c->top_k);
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    err = moe::launch_mx6_rows(x, H, (int)T, H, xq, st);
+    if (err == hipSuccess) err = mark(tl, "mx6_x", st);
+    if (err != hipSuccess) return fail_hip(err, "x to MXFP6 launch");
+    moe::Mx6Params q{};
+    q.tiles = at<moe::GemmTile>(ws, L.tiles);
+    q.tile_count = at<int32_t>(ws, L.tile_count);
+    // gate/up: A = x records of the tile's tokens, B = W_gu[e] [2I][H], C = h [n][I]
+    q.gather = sorted;
+    q.gather_div = c->top_k;
+    q.A = xq;
+    q.a_stride = moe::mx6_bytes(1, H);
+    q.a_rows = (int)T;
+    q.K = H;
+    q.bq = w->gu_q;
+    q.bs = w->gu_s;
+    q.b_expert_rows = 2 * (int64_t)I;
+    q.b_row_second = I;
+    q.N = I;
+    q.C = h;
+    q.ldc = I;
+    q.limit = c->swiglu_limit;
+    err = moe::launch_expert_mx6(q, true, (int)L.max_tiles, st);
+    if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
+    if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+    err = moe::launch_mx6_rows(h, I, n, I, hq, st);
+    if (err == hipSuccess) err = mark(tl, "mx6_h", st);
+    if (err != hipSuccess) return fail_hip(err, "h to MXFP6 launch");
+    // down: A = h records in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
+    q.gather = nullptr;
+    q.A = hq;
+    q.a_stride = moe::mx6_bytes(1, I);
+    q.a_rows = n;
+    q.K = I;
+    q.bq = w->dn_q;
+    q.bs = w->dn_s;
+    q.b_expert_rows = H;
+    q.b_row_second = 0;
+    q.N = H;
+    q.C = y_slot;
+    q.ldc = H;
+    err = moe::launch_expert_mx6(q, false, (int)L.max_tiles, st);
+    if (err == hipSuccess) err = mark(tl, "routed_down", st);
+    if (err != hipSuccess) return fail_hip(err, "routed down launch");
+    return run_shared(c, w, x, T, y_shared, ws, L, st, tl);
+  }
   moe::GemmParams p{};
   p.tiles = at<moe::GemmTile>(ws, L.tiles);
   p.tile_count = at<int32_t>(ws, L.tile_count);
@@ -760,7 +820,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   p.C = h;
   p.ldc = I;
   p.limit = c->swiglu_limit;
-  hipError_t err = moe::launch_expert_gemm(p, true, L.fmt, L.gemm_mt, L.max_tiles, st);
+  err = moe::launch_expert_gemm(p, true, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
   // down: A = h rows in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
@@ -779,6 +839,14 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   err = moe::launch_expert_gemm(p, false, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");
+  return run_shared(c, w, x, T, y_shared, ws, L, st, tl);
+}
+
+// The shared expert for the general path (after the routed GEMMs).
+moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, uint16_t* y_shared,
+                      void* ws, const WsLayout& L, hipStream_t st, Timeline* tl) {
+  const int H = c->hidden;
+  hipError_t err;
   if (c->n_shared == 1) {
     const int Is = c->shared_inter;
     uint16_t* hs = at<uint16_t>(ws, L.h_sh);
@@ -799,7 +867,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     err = L.shared_ks_gu ? moe::launch_dense_sliced(q, true, L.shared_ks_gu, sh_part, st)
                          : moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
-  if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
+    if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
     q.A = hs;
     q.lda = Is;
     q.a_rows = (int)T;
@@ -813,7 +881,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     err = L.shared_ks_dn ? moe::launch_dense_sliced(q, false, L.shared_ks_dn, sh_part, st)
                          : moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_down", st);
-  if (err != hipSuccess) return fail_hip(err, "shared down launch");
+    if (err != hipSuccess) return fail_hip(err, "shared down launch");
   }
   return MOE_OK;
 }

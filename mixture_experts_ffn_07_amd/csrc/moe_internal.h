@@ -294,6 +294,35 @@ hipError_t launch_route_permute_small(const float* part, int ksplit, const float
                                       int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, int bm,
                                       int max_tiles, GemmTile* tiles, int32_t* tile_count, hipStream_t stream);
 
+// ---------------------------------------------------------------- two-term MXFP6 grouped GEMM (expert_mx6.hip)
+// Activation rows in two-term MXFP6 records (mx6_device.h) times MXFP4
+// weights on the block-scaled MFMA, tiles of up to mx6_tile_rows() rows of
+// one expert.
+struct Mx6Params {
+  const GemmTile* tiles;       // [n_tiles] from the permutation, tile_count entries valid
+  const int32_t* tile_count;
+  const int32_t* gather;       // A record row of position p: gather[p] / gather_div, or p if NULL
+  int gather_div;
+  const uint8_t* A;            // [a_rows][mx6_row_bytes(K)]
+  int64_t a_stride;
+  int a_rows;
+  int K;                       // multiple of 128
+  const uint8_t* bq;           // [E][b_expert_rows][K/2] E2M1 codes
+  const uint8_t* bs;           // [E][b_expert_rows][K/32] E8M0 scales
+  int64_t b_expert_rows;
+  int b_row_second;            // SwiGLU: first row of the up half
+  int N;                       // output columns (h columns for gate/up)
+  uint16_t* C;                 // bf16 [.][ldc], row = position p
+  int64_t ldc;
+  float limit;
+};
+bool mx6_supported(int hidden, int inter);
+int mx6_tile_rows();
+int64_t mx6_bytes(int64_t rows, int K);
+// bf16 rows [rows][K] (row stride ld_src elements) -> records [rows][mx6_row_bytes(K)]
+hipError_t launch_mx6_rows(const uint16_t* src, int64_t ld_src, int rows, int K, uint8_t* dst, hipStream_t stream);
+hipError_t launch_expert_mx6(const Mx6Params& p, bool swiglu, int n_tiles, hipStream_t stream);
+
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(const uint16_t* y_slot, const int32_t* slot_pos, const float* w, const uint16_t* y_shared,
                           int tokens, int top_k, int hidden, uint16_t* y, hipStream_t stream);
