@@ -202,7 +202,8 @@ struct WsLayout {
   bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
                               // down; routed down + combine
   bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
-  bool mx6 = false;             // many tokens, MXFP4: routed GEMMs on two-term MXFP6 activations (expert_mx6.hip)
+  bool mx6 = false;             // many tokens, MXFP4: routed gate/up on two-term MXFP6 activations (expert_mx6.hip)
+  bool mx6_dn = false;          // ... and the routed down projection too
   Region xq, hq, x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
       y_slot, h_sh, y_sh, sh_part;
   size_t total = 0;
@@ -241,6 +242,11 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     // MFMA on two-term MXFP6 rows, in tiles of its own height
     L.mx6 = L.fmt == moe::kWMxfp4 && L.bm == 128 && moe::mx6_supported(c->hidden, c->inter);
     if (L.mx6) L.bm = moe::mx6_tile_rows();
+    // the down projection (K = I, 18 chunks at I = 2304) measured slower on
+    // it than on the 512-row bf16 kernel, counting the pass that writes h as
+    // MXFP6 (4096 tokens: 838 + 94 us against 813 us; 16384 tokens: 1253 +
+    // 178 against 1133 us), so it keeps bf16 h and the wide kernel
+    L.mx6_dn = false;
   }
   L.max_tiles = moe::max_gemm_tiles(n, E, L.bm);
   {
@@ -291,7 +297,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
   take(L.sorted, sizeof(int32_t) * n);
   take(L.slot_pos, sizeof(int32_t) * n);
   take(L.xq, L.mx6 ? (size_t)moe::mx6_bytes(tokens, c->hidden) : 0);
-  take(L.hq, L.mx6 ? (size_t)moe::mx6_bytes(n, c->inter) : 0);
+  take(L.hq, L.mx6_dn ? (size_t)moe::mx6_bytes(n, c->inter) : 0);
   take(L.h, sizeof(uint16_t) * n * c->inter);
   take(L.y_slot, sizeof(uint16_t) * n * c->hidden);
   const int64_t is = c->n_shared ? c->shared_inter : 0;
@@ -744,6 +750,10 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
 moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, uint16_t* y_shared,
                       void* ws, const WsLayout& L, hipStream_t st, Timeline* tl);
 
+moe_status run_down(const moe_config* c, const moe_weights* w, int64_t T, const uint16_t* h, uint16_t* y_slot,
+                    uint16_t* y_shared, const uint16_t* x, void* ws, const WsLayout& L, hipStream_t st,
+                    Timeline* tl);
+
 // Routed gate/up + down over the tile table in ws, then the shared expert.
 moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
                        const int32_t* sorted, uint16_t* y_slot, uint16_t* y_shared, void* ws, const WsLayout& L,
@@ -781,6 +791,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     err = moe::launch_expert_mx6(q, true, (int)L.max_tiles, st);
     if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
     if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+    if (!L.mx6_dn) return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl);
     err = moe::launch_mx6_rows(h, I, n, I, hq, st);
     if (err == hipSuccess) err = mark(tl, "mx6_h", st);
     if (err != hipSuccess) return fail_hip(err, "h to MXFP6 launch");
@@ -823,6 +834,18 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   err = moe::launch_expert_gemm(p, true, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+  return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl);
+}
+
+// Routed down projection on bf16 h over the tile table, then the shared expert.
+moe_status run_down(const moe_config* c, const moe_weights* w, int64_t T, const uint16_t* h, uint16_t* y_slot,
+                    uint16_t* y_shared, const uint16_t* x, void* ws, const WsLayout& L, hipStream_t st,
+                    Timeline* tl) {
+  const int H = c->hidden, I = c->inter;
+  moe::GemmParams p{};
+  p.tiles = at<moe::GemmTile>(ws, L.tiles);
+  p.tile_count = at<int32_t>(ws, L.tile_count);
+  p.limit = c->swiglu_limit;
   // down: A = h rows in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
   p.gather = nullptr;
   p.A = h;
@@ -836,7 +859,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   p.N = H;
   p.C = y_slot;
   p.ldc = H;
-  err = moe::launch_expert_gemm(p, false, L.fmt, L.gemm_mt, L.max_tiles, st);
+  hipError_t err = moe::launch_expert_gemm(p, false, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");
   return run_shared(c, w, x, T, y_shared, ws, L, st, tl);
