@@ -125,6 +125,17 @@ def algorithmic_bytes(cfg, touched: float) -> dict:
         "route_shared_gate_up": 2 * t * e * 4 + n * 8 + n * 4 * 2 + 2 * i_s * h * 2 + t * h * 2 + t * i_s * 2,
         "routed_gate_up_shared_down": touched * gu_expert + t * h * 2 + n * i * 2 + h * i_s * 2 + t * i_s * 2
         + t * h * 2,
+        # one or two tokens, three launches: routed gate/up (every wave routing from the scores) beside the
+        # shared gate/up; routed down with the shared down and the combine
+        "route_gate_up_shared_gate_up": touched * gu_expert + 2 * i_s * h * 2 + t * h * 2 + 2 * t * e * 4
+        + n * i * 2 + t * i_s * 2 + n * 16,
+        "routed_down_shared_down_combine": touched * dn_expert + h * i_s * 2 + n * i * 2 + t * i_s * 2 + n * 12
+        + t * h * 2,
+        # one or two tokens without the pre-FFN norm: router scores beside the shared gate/up; routed gate/up
+        # (every wave routing from the scores) beside the shared down; routed down with the combine
+        "router_scores_shared_gate_up": e * h * 4 + t * h * 2 + 2 * t * e * 4 + 2 * i_s * h * 2 + t * i_s * 2,
+        "route_gate_up_shared_down": touched * gu_expert + t * h * 2 + 2 * t * e * 4 + n * i * 2 + n * 16
+        + h * i_s * 2 + t * i_s * 2 + t * h * 2,
         # few-token path: routed and shared experts share a launch, routing is one fused kernel
         "route_permute": t * e * 4 + n * 8 + n * 4 * 2 + (e + 1) * 4,
         "gate_up": touched * gu_expert + 2 * i_s * h * 2 + t * h * 2 + n * i * 2 + t * i_s * 2,

@@ -243,23 +243,9 @@ __global__ __launch_bounds__(256) void decode_route_shared_gu_kernel(FrontValuPa
     route_small_block<MPL>(p);
     return;
   }
-  uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int H = f.hidden, T = f.tokens, Is = f.shared_inter;
-  const int nrow = ((int)blockIdx.x - 1) * 4 + wave;  // gate/up pair
-  const bool ok = nrow < Is;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.sh_gu, (uint32_t)((int64_t)2 * Is * H * 2));
-  const uint32_t off[2] = {ok ? (uint32_t)nrow * (uint32_t)H * 2u : kOob,
-                           ok ? (uint32_t)(Is + nrow) * (uint32_t)H * 2u : kOob};
-  ValuRows<8, 10, 2> st;
-  valu_issue<8, 10, 2>(st, rw, off, H);
-  valu_stage_rows(f.x, H, T, H, x_lds);
-  __syncthreads();
-  float out2[2][kValuMaxTokens];
-  valu_compute<8, 10, 2, kValuMaxTokens>(st, x_lds, H, T, H, out2);
-  if (lane == 0 && ok)
-    for (int t = 0; t < T; ++t)
-      f.h_sh[(int64_t)t * Is + nrow] = f32_to_bf16(clamped_swiglu(out2[0][t], out2[1][t], f.limit));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  shared_gate_up_pair(f.x, f.sh_gu, f.h_sh, f.tokens, f.hidden, f.shared_inter, f.limit,
+                      ((int)blockIdx.x - 1) * 4 + wave, reinterpret_cast<uint16_t*>(lds));
 }
 
 bool decode_valu_supported(int tokens, int hidden, int shared_inter) {

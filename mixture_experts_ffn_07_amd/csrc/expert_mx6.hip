@@ -17,18 +17,20 @@
 // 6 x 8 x 4 registers (the wave runs alone on its SIMD, 512 registers; 128
 // rows would need all 256 accumulation registers and spill the operands).
 //   * Weights go from memory straight to registers (each weight byte is read
-//     by one wave only), two chunks ahead of the MFMAs.
+//     by one wave only), two chunks per burst, two to three chunks ahead of
+//     the MFMAs.
 //   * The tile's activation records go global -> registers -> LDS (two
-//     stages), one chunk ahead, and every wave reads its MFMA operands from
+//     stages), four chunks ahead, and every wave reads its MFMA operands from
 //     LDS: the record layout is the operand layout, so a row tile costs five
 //     LDS reads per lane and chunk (no bank conflicts on the 16-byte reads:
 //     the 208-byte row stride puts 8 consecutive rows on 8 different bank
 //     quads).
-// Loads are ordinary buffer loads whose waits the compiler places.  The
-// per-lane offset of a row past the end (weight rows beyond N, activation
-// pieces beyond the tile) is kOob, which the buffer range check turns into a
-// zero; the chunk enters as the scalar offset, which that check does not
-// cover, so chunk indices are always clamped into the matrix.
+//   * The weight scales of the block's rows go to LDS whole in the prologue.
+// Chunk loads are ordinary buffer loads whose waits the compiler places.
+// The per-lane offset of a row past the end (weight rows beyond N,
+// activation pieces beyond the tile) is kOob, which the buffer range check
+// turns into a zero; the chunk enters as the scalar offset, which that check
+// does not cover, so chunk indices are always clamped into the matrix.
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "mx_device.h"
@@ -115,6 +117,20 @@ __global__ __launch_bounds__(256) void mx6_rows_kernel(const uint16_t* __restric
 }
 
 // ============================================================== grouped GEMM
+// Global-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16 l.  Written in asm so that the compiler does not treat
+// the LDS it writes as possibly read by every later LDS load (it would then
+// wait for all loads in flight before each one); the kernel waits for these
+// loads itself.  M0 carries the LDS address as an input operand ("{m0}"),
+// so the compiler writes M0 itself; the asm opens with the one wait state
+// gfx950 needs between an SALU write of M0 and the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
 constexpr int kMx6Rows = kMx6TileRows;             // rows per tile
 // bytes per LDS stage: the tile's records, rounded up to whole rounds of 256
 // 16-byte pieces (every thread writes the same number of pieces, the ones
@@ -129,18 +145,26 @@ __device__ __forceinline__ f32x4_t mfma_f6f4(const i32x8_t& a, const u32x4_t& b,
                    : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 4, 1, sa_word, 0, sb);
 }
 
-// Weight scale bytes reach LDS in groups of kMx6SGroup chunks: per weight
-// row of the block 32 contiguous bytes (4 per chunk), two 16-byte pieces per
-// row, instead of one byte per lane, row and chunk from memory.  The byte
-// loads touched a cache line per row and chunk, as many as the weight codes
-// themselves, and measured 35% of the kernel's time.
-constexpr int kMx6SGroup = 8;
-constexpr int kMx6BlockRows = 512;                         // weight rows per block
-constexpr int kMx6SStage = kMx6BlockRows * 4 * kMx6SGroup;  // bytes per scale group in LDS
+// The block's weight scale bytes (K / 32 per weight row) go to LDS whole,
+// once, in the block's prologue: the weight rows of a block are one or two
+// runs of consecutive matrix rows, so their scales are one or two contiguous
+// byte ranges, read as 16-byte pieces.  (Per-lane byte loads touched a cache
+// line per row and chunk and measured 35% of the kernel's time; groups of a
+// few chunks per row re-fetched each scale line once per group, because the
+// weight stream evicts it from L2 in between.)
+constexpr int kMx6WaveTiles = 8;                            // MFMA column tiles (16 weight rows) per wave
+constexpr int kMx6WaveRows = 16 * kMx6WaveTiles;            // weight rows per wave
+constexpr int kMx6BlockRows = 4 * kMx6WaveRows;             // weight rows per block
+constexpr int kMx6MaxK = 5120;                              // scales of kMx6BlockRows rows fit kMx6SBytes
+constexpr int kMx6SBytes = kMx6BlockRows * (kMx6MaxK / 32);  // LDS bytes of the block's scales
+constexpr int kMx6SPieces = kMx6SBytes / 16 / 256;           // 16-byte scale pieces per thread (at most)
+constexpr int kMx6ABufs = 4;                                // activation register buffers (chunks in flight)
+constexpr int kMx6Unroll = 8;                               // steps per loop iteration
 
 template <bool SWIGLU, int MT>
-__device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sgrp, const int32_t* src_row,
-                                         int e, int m_begin, int rows, int n0) {
+__device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sall, int e, int m_begin,
+                                         int rows, int n0) {
+  constexpr int JW = kMx6WaveTiles;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int K = p.K, nchunks = K / 128;
@@ -148,59 +172,82 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   constexpr int kPieces = kRowsRun * 13;                    // 16-byte pieces of the tile per chunk
   constexpr int kPerThread = (kPieces + 255) / 256;
 
+  // weight rows of this block (expert-relative): SwiGLU, two runs of
+  // kMx6BlockRows / 2 rows (gate rows n0.., up rows b_row_second + n0..);
+  // otherwise one run of kMx6BlockRows rows from n0
+  const int64_t qbytes = p.b_expert_rows * (K / 2), sbytes = p.b_expert_rows * (K / 32);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, (uint32_t)qbytes);
   // activation pieces this thread stages: piece q = tid + 256 i of the
-  // stage (row q / 13, part q % 13); LDS byte 16 q
+  // stage (row q / 13, part q % 13); LDS byte 16 q.  Rows past the tile
+  // repeat its last row.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)p.a_rows * p.a_stride));
+  // (the gather reads go out together, with no branch between them)
+  int src[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) src[i] = m_begin + min(((int)threadIdx.x + 256 * i) / 13, rows - 1);
+  if (p.gather) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) src[i] = p.gather[src[i]];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) src[i] /= p.gather_div;
+  }
   uint32_t a_off[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int q = (int)threadIdx.x + 256 * i;
-    a_off[i] = q < kPieces ? (uint32_t)src_row[q / 13] * (uint32_t)p.a_stride + 16u * (uint32_t)(q % 13) : kOob;
+    const int r = min(max(src[i], 0), p.a_rows - 1);
+    a_off[i] = q < kPieces ? (uint32_t)r * (uint32_t)p.a_stride + 16u * (uint32_t)(q % 13) : kOob;
   }
-  // weight rows of this lane's 8 column tiles (expert-relative)
-  const int64_t qbytes = p.b_expert_rows * (K / 2), sbytes = p.b_expert_rows * (K / 32);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, (uint32_t)qbytes);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sbytes, (uint32_t)sbytes);
-  // block row r (= 128 w + 16 j + n: wave w, column tile j, lane column n)
-  // -> expert-relative weight row, or -1 past N
+  // the block's scales: piece q = tid + 256 i of the runs laid end to end
+  // (run bytes = run rows * K / 32, a multiple of 16) -> LDS byte 16 q, by
+  // global-to-LDS loads issued before the chunk loads (no registers; waited
+  // for at the end of the prologue).  A piece past the runs, or past the
+  // expert's matrix, re-reads the expert's first piece into LDS no one
+  // reads.
+  constexpr int kRuns = SWIGLU ? 2 : 1, kRunRows = kMx6BlockRows / kRuns;
+  const int srow_bytes = K / 32, run_pieces = kRunRows * srow_bytes / 16;
+  {
+    const uint8_t* sbase = p.bs + (int64_t)e * sbytes;
+#pragma unroll
+    for (int i = 0; i < kMx6SPieces; ++i) {
+      const int q = (int)threadIdx.x + 256 * i;
+      const int run = q / run_pieces, part = q - run * run_pieces;
+      const int64_t off = (int64_t)(run * p.b_row_second + n0) * srow_bytes + 16 * part;
+      const bool ok = run < kRuns && off + 16 <= sbytes;
+      load_lds16(sbase + (ok ? off : 0), lds_addr(sall + 16 * (256 * i + 64 * wave)));
+    }
+  }
+
+  // block row r (= kMx6WaveRows w + 16 j + n: wave w, column tile j, lane
+  // column n) -> expert-relative weight row, or -1 past N.  Gate/up: the
+  // first JW / 2 tiles of a wave are gate rows, the others the matching up
+  // rows, so the wave's SwiGLU pairs stay in its registers.
   auto weight_row = [&](int r) {
-    const int w = r >> 7, j = (r >> 4) & 7, nn = r & 15;
+    const int w = r / kMx6WaveRows, j = (r >> 4) % JW, nn = r & 15;
     if constexpr (SWIGLU) {
-      const int col = n0 + 64 * w + 16 * (j & 3) + nn;
-      return col < p.N ? col + (j >> 2) * p.b_row_second : -1;
+      const int col = n0 + (kMx6WaveRows / 2) * w + 16 * (j % (JW / 2)) + nn;
+      return col < p.N ? col + (j / (JW / 2)) * p.b_row_second : -1;
     } else {
-      const int col = n0 + 128 * w + 16 * j + nn;
+      const int col = n0 + kMx6WaveRows * w + 16 * j + nn;
       return col < p.N ? col : -1;
     }
   };
-  uint32_t q_off[8];
+  uint32_t q_off[JW];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = weight_row(128 * wave + 16 * j + n);
+  for (int j = 0; j < JW; ++j) {
+    const int row = weight_row(kMx6WaveRows * wave + 16 * j + n);
     q_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)g : kOob;
   }
-  // scale pieces this thread stages: piece i = tid + 256 i of a group (block
-  // row (tid + 256 i) / 2, half (tid + 256 i) % 2), LDS byte 16 (tid + 256 i)
-  constexpr int kSPieces = kMx6SStage / 16 / 256;
-  uint32_t s_off[kSPieces];
-#pragma unroll
-  for (int i = 0; i < kSPieces; ++i) {
-    const int q = (int)threadIdx.x + 256 * i;
-    const int row = weight_row(q >> 1);
-    s_off[i] = row >= 0 ? (uint32_t)row * (uint32_t)(K / 32) + 16u * (uint32_t)(q & 1) : kOob;
-  }
 
-  // NB weight buffers: the weights of chunk c + NB - 1 are issued while chunk
-  // c is computed (more buffers for fewer row tiles, whose chunks are short)
+  // NB weight buffers, filled two chunks at a time (see step)
   constexpr int NB = 4;
-  u32x4_t areg[2][kPerThread];
-  u32x4_t bq[NB][8];
-  u32x4_t sreg[kSPieces];
-  f32x4_t acc[MT][8];
+  u32x4_t areg[kMx6ABufs][kPerThread];
+  u32x4_t bq[NB][JW];
+  f32x4_t acc[MT][JW];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JW; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // per-lane offsets stay fixed; the chunk enters as the scalar offset
   // (a piece or row past the end has a per-lane offset of kOob and reads zero)
@@ -217,25 +264,14 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) *reinterpret_cast<u32x4_t*>(st + 4096 * i) = areg[abuf][i];
   };
-  auto load_b = [&](int c, int buf) {
+  // two chunks per burst, the same rows back to back: each row is read 128
+  // contiguous bytes (a whole cache line) at a time
+  auto load_b2 = [&](int c0, int c1, int buf0, int buf1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bq[buf][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c, 0));
-  };
-  // scale group G (chunks [8 G, 8 G + 8)): the group enters the per-lane
-  // offset, so pieces past the matrix read zero; bytes past a row's end (the
-  // last group of a K that is not a multiple of 1024) are never used
-  auto load_s = [&](int G) {
-#pragma unroll
-    for (int i = 0; i < kSPieces; ++i)
-      sreg[i] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                       rs, (int)(s_off[i] == kOob ? kOob : s_off[i] + (uint32_t)(4 * kMx6SGroup * G)), 0, 0));
-  };
-  auto store_s = [&](int slot) {
-    uint8_t* st = sgrp + slot * kMx6SStage + 16 * threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kSPieces; ++i) *reinterpret_cast<u32x4_t*>(st + 4096 * i) = sreg[i];
+    for (int j = 0; j < JW; ++j) {
+      bq[buf0][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c0, 0));
+      bq[buf1][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c1, 0));
+    }
   };
   // A operands of one row tile: the hi and lo terms and the scale word
   struct AFrag {
@@ -253,14 +289,20 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
     f.lo = i32x8_t{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], 0, 0};
     return f;
   };
+  // LDS scale rows: column tile j's lane column n sits at row
+  // scale_row0 + scale_drow(j) of the runs (the step is wave-uniform)
+  const int scale_row0 = SWIGLU ? (kMx6WaveRows / 2) * wave + n : kMx6WaveRows * wave + n;
+  auto scale_drow = [&](int j) {
+    return SWIGLU ? (j / (JW / 2)) * kRunRows + 16 * (j % (JW / 2)) : 16 * j;
+  };
+  const uint8_t* sb_lane = sall + scale_row0 * srow_bytes + g;
   // row tile m + 1's LDS reads are issued before row tile m's MFMAs (two
   // operand sets live), fenced so the compiler does not hoist further
   auto compute = [&](int s, int buf, int c) {
-    // this lane's scale byte of each column tile: block row 128 w + 16 j + n, chunk c % 8, lane group g
-    const uint8_t* sb_row = sgrp + ((c / kMx6SGroup) & 1) * kMx6SStage + (128 * wave + n) * 32 + 4 * (c % kMx6SGroup) + g;
-    int sb[8];
+    // this lane's scale byte of each column tile: chunk c, lane group g
+    int sb[JW];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sb[j] = sb_row[16 * 32 * j];
+    for (int j = 0; j < JW; ++j) sb[j] = sb_lane[scale_drow(j) * srow_bytes + 4 * c];
     const uint8_t* st = stage + s * kMx6Stage + n * kMx6Rec;
     AFrag cur = read_a(st);
 #pragma unroll
@@ -268,7 +310,7 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
       AFrag nxt;
       if (m + 1 < MT) nxt = read_a(st + (m + 1) * 16 * kMx6Rec);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < JW; ++j) {
         acc[m][j] = mfma_f6f4(cur.hi, bq[buf][j], cur.sc, sb[j], acc[m][j], 0);
         acc[m][j] = mfma_f6f4(cur.lo, bq[buf][j], cur.sc, sb[j], acc[m][j], 1);
       }
@@ -277,42 +319,40 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
     }
   };
   // One chunk c (weights in register buffer c % NB, activations in LDS
-  // stage c % 2): publish chunk c + 1's activations (issued two steps ago,
-  // register buffer (c + 1) % 2) to the other LDS stage, reuse that buffer
-  // for chunk c + 3's activation loads, issue chunk c + NB - 1's weight
-  // loads, compute chunk c.  Loads complete in issue order, so the wait for
-  // chunk c + 1's activations also covers every load issued before them:
-  // the weights of chunk c and older, never newer ones.  Weights thus get
-  // NB - 1 steps to arrive and activations two.  Scale group G + 1 is issued
-  // in the first step of group G (after the activation loads) and published
-  // in its fifth, to the LDS slot group G - 1 used.  The last steps load the
-  // last chunk (group) again instead of chunks past the end (the scalar
-  // offset is outside the buffer range check) and never use it, so the loop
-  // has no branch but the compute guard of its last steps.
-  const int last = nchunks - 1, last_group = last / kMx6SGroup;
-  auto step = [&](int c, int buf, int abuf, int u) {
-    store_a((c + 1) & 1, abuf ^ 1);
-    if (u == kMx6SGroup / 2) store_s((c / kMx6SGroup + 1) & 1);
-    load_a(min(c + 3, last), abuf ^ 1);
-    if (u == 0) load_s(min(c / kMx6SGroup + 1, last_group));
-    load_b(min(c + NB - 1, last), (buf + NB - 1) % NB);
+  // stage c % 2): publish chunk c + 1's activations (register buffer
+  // (c + 1) % kMx6ABufs) to the other LDS stage and reuse that buffer for
+  // chunk c + 1 + kMx6ABufs; on even steps issue the weights of chunks
+  // c + 2 and c + 3 (one burst); compute chunk c.  Loads complete in issue
+  // order, so the wait for chunk c + 1's activations also covers every load
+  // issued before them.  The last steps load the last chunk again instead of
+  // chunks past the end (the scalar offset is outside the buffer range
+  // check) and never use it, so the loop has no branch but the compute
+  // guard of its last steps.
+  const int last = nchunks - 1;
+  auto step = [&](int c, int buf, int u) {
+    const int ab = (u + 1) % kMx6ABufs;
+    store_a((c + 1) & 1, ab);
+    load_a(min(c + 1 + kMx6ABufs, last), ab);
+    if ((u & 1) == 0) load_b2(min(c + 2, last), min(c + 3, last), (buf + 2) % NB, (buf + 3) % NB);
     if (c < nchunks) compute(c & 1, buf, c);
     __syncthreads();
   };
 
-  load_s(0);
-  load_a(0, 0);
-  load_a(min(1, last), 1);
 #pragma unroll
-  for (int b = 0; b < NB - 1; ++b) load_b(min(b, last), b);
-  store_s(0);
+  for (int i = 0; i < kMx6ABufs; ++i) load_a(min(i, last), i);
+  load_b2(0, min(1, last), 0, 1);
   store_a(0, 0);
-  load_a(min(2, last), 0);
+  load_a(min(kMx6ABufs, last), 0);
+  // the scale loads were issued before the (kMx6ABufs + 1) kPerThread
+  // activation and 2 JW weight loads above, and loads complete in issue
+  // order: this wait leaves at most those in flight (any other load issued
+  // after the scales only makes it stricter)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kMx6ABufs + 1) * kPerThread + 2 * JW) : "memory");
   __syncthreads();
-  static_assert(kMx6SGroup % NB == 0 && kMx6SGroup % 2 == 0, "a loop iteration is one scale group");
-  for (int c = 0; c < nchunks; c += kMx6SGroup) {
+  static_assert(kMx6Unroll % NB == 0 && kMx6Unroll % kMx6ABufs == 0, "the buffer indices repeat per iteration");
+  for (int c = 0; c < nchunks; c += kMx6Unroll) {
 #pragma unroll
-    for (int u = 0; u < kMx6SGroup; ++u) step(c + u, u % NB, u % 2, u);
+    for (int u = 0; u < kMx6Unroll; ++u) step(c + u, u % NB, u);
   }
 
   // epilogue: lane 16 g + n holds rows 4 g + i of each row tile, column n of each column tile
@@ -325,54 +365,57 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
       uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
       if constexpr (SWIGLU) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + 64 * wave + 16 * j + n;
-          if (col < p.N) crow[col] = f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + 4][i], p.limit));
+        for (int j = 0; j < JW / 2; ++j) {
+          const int col = n0 + (kMx6WaveRows / 2) * wave + 16 * j + n;
+          if (col < p.N) crow[col] = f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + JW / 2][i], p.limit));
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + 128 * wave + 16 * j + n;
+        for (int j = 0; j < JW; ++j) {
+          const int col = n0 + kMx6WaveRows * wave + 16 * j + n;
           if (col < p.N) crow[col] = f32_to_bf16(acc[m][j][i]);
         }
       }
     }
 }
 
+// h columns (gate/up) or output columns (down) per block
+template <bool SWIGLU>
+constexpr int kMx6BlockCols = SWIGLU ? kMx6BlockRows / 2 : kMx6BlockRows;
+
 // XCD-aware block order (as the pipelined kernels): block b runs on XCD
 // b % 8, which takes the tiles t with t % 8 == its index and runs a tile's
 // column blocks back to back, so the tile's activation records stay in that
-// XCD's L2 while its column blocks read them.
+// XCD's L2 while its column blocks read them.  An expert's consecutive row
+// tiles run at about the same time on different XCDs and share their weight
+// reads through the memory-side cache (grouping them on one XCD measured
+// slower: 1873 -> 1930-2130 us for the 16384-token gate/up).  One block per
+// CU, one wave per SIMD (512 registers a wave).
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void expert_mx6_kernel(const Mx6Params p, int n_tiles, int col_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kMx6Stage];
-  __shared__ __attribute__((aligned(16))) uint8_t sgrp[2 * kMx6SStage];
-  __shared__ int32_t src_row[kMx6Rows];
+  __shared__ __attribute__((aligned(16))) uint8_t sall[kMx6SBytes];
   const int b = (int)blockIdx.x, x = b & 7, q = b >> 3;
   const int tile = 8 * (q / col_blocks) + x, cb = q % col_blocks;
   if (tile >= n_tiles || tile >= *p.tile_count) return;
   const GemmTile tl = p.tiles[tile];
   const int m_begin = tl.m_begin, rows = min(tl.m_end, tl.m_begin + kMx6Rows) - tl.m_begin;
   if (rows <= 0) return;
-  for (int r = threadIdx.x; r < kMx6Rows; r += 256) {
-    const int pos = m_begin + min(r, rows - 1);
-    const int src = p.gather ? p.gather[pos] / p.gather_div : pos;
-    src_row[r] = min(max(src, 0), p.a_rows - 1);
-  }
-  __syncthreads();
-  const int n0 = cb * (SWIGLU ? 256 : 512);
+  const int n0 = cb * kMx6BlockCols<SWIGLU>;
   const int mt = min(kMx6Rows / 16, 2 * ((rows + 31) / 32));
   switch (mt) {
-    case 2: mx6_tile<SWIGLU, 2>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
-    case 4: mx6_tile<SWIGLU, 4>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
-    default: mx6_tile<SWIGLU, 6>(p, stage, sgrp, src_row, tl.e, m_begin, rows, n0); break;
+    case 2: mx6_tile<SWIGLU, 2>(p, stage, sall, tl.e, m_begin, rows, n0); break;
+    case 4: mx6_tile<SWIGLU, 4>(p, stage, sall, tl.e, m_begin, rows, n0); break;
+    default: mx6_tile<SWIGLU, 6>(p, stage, sall, tl.e, m_begin, rows, n0); break;
   }
 }
 
 }  // namespace
 
-bool mx6_supported(int hidden, int inter) { return hidden % 128 == 0 && inter % 128 == 0; }
+bool mx6_supported(int hidden, int inter) {
+  return hidden % 128 == 0 && inter % 128 == 0 && hidden <= kMx6MaxK && inter <= kMx6MaxK;
+}
 
 int mx6_tile_rows() { return kMx6TileRows; }
 
@@ -387,7 +430,7 @@ hipError_t launch_mx6_rows(const uint16_t* src, int64_t ld_src, int rows, int K,
 }
 
 hipError_t launch_expert_mx6(const Mx6Params& p, bool swiglu, int n_tiles, hipStream_t stream) {
-  const int cols = swiglu ? 256 : 512;
+  const int cols = swiglu ? kMx6BlockCols<true> : kMx6BlockCols<false>;
   const int col_blocks = (p.N + cols - 1) / cols;
   const dim3 grid((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
   if (swiglu)

@@ -28,6 +28,7 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "mx_device.h"
+#include "router_device.h"
 
 namespace moe {
 
@@ -76,21 +77,19 @@ __device__ __forceinline__ void gu_issue(ColBuf<JM>& b, const uint8_t* gu_q, con
   }
 }
 
-// blocks blk of nblk run the gate/up loop; lds holds x rows [T][H] bf16
-template <int JM, int TM, bool FP8>
+// blocks blk of nblk run the gate/up loop; lds holds x rows [T][H] bf16.
+// MPL = 0: the tiles come from the one-block routing's records (tiles,
+// tile_rows); MPL > 0: every wave routes for itself from the scores
+// (route_wave_small, MPL = experts per lane), and wave 0 of block 0 writes
+// the routing for the launches that follow.
+template <int JM, int TM, bool FP8, int MPL = 0>
 __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, int max_tiles, int blk, int nblk,
                                                     uint8_t* lds) {
   uint16_t* x_lds = reinterpret_cast<uint16_t*>(lds);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.tokens, H = p.hidden, I = p.inter, VR = H / kVecElems<FP8>;
 
-  // tile records: lane t < max_tiles loads record t and its first two token
-  // rows (one round trip, every wave for itself); the live ones are moved to
-  // the lowest lanes in order, so lane i holds live tile i
-  const bool in = lane < max_tiles;
-  const GemmTile tl = in ? p.tiles[lane] : GemmTile{0, 0, 0, 0};
-  const int r0 = in ? p.tile_rows[lane * kTileRows] : 0, r1 = in ? p.tile_rows[lane * kTileRows + 1] : 0;
-  // x staging loads go out together with the records
+  // x staging loads go out first (they need no routing)
   const int x_pieces = T * (H / 8);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(T * H * 2));
   auto x_off = [&](int q) {
@@ -98,18 +97,41 @@ __device__ __forceinline__ void gate_up_valu_blocks(const GateUpValuParams& p, i
     return (uint32_t)((t * H + 8 * c) * 2);
   };
   StageBatch<4> xb;
-  stage_issue<4>(xb, rx, x_pieces, 0, x_off);
-
-  const int rows = min(tl.m_end - tl.m_begin, T);
-  const bool live = in && rows > 0;
-  const uint64_t live_mask = __ballot(live);
-  const int n_live = __popcll(live_mask);
-  const int rank = __popcll(live_mask & ((1ull << lane) - 1ull));
-  const int dst = 4 * (live ? rank : n_live + (lane - rank));
-  const int c_e = __builtin_amdgcn_ds_permute(dst, tl.e);
-  const int c_m = __builtin_amdgcn_ds_permute(dst, tl.m_begin);
-  const int c_r = __builtin_amdgcn_ds_permute(dst, rows);
-  const int c_s = __builtin_amdgcn_ds_permute(dst, min(max(r0, 0), T - 1) | (min(max(r1, 0), T - 1) << 16));
+  int c_e, c_m, c_r, c_s, n_live;
+  if constexpr (MPL > 0) {
+    stage_issue<4>(xb, rx, x_pieces, 0, x_off);
+    const WaveRoute rt = route_wave_small<MPL>(p.scores, T, p.n_experts, p.top_k, p.route_scale);
+    c_e = min(max(rt.t_e, 0), p.n_experts - 1);
+    c_m = rt.t_m;
+    c_r = min(rt.t_r, T);
+    c_s = rt.t_src;
+    n_live = rt.n_tiles;
+    if (blk == 0 && wave == 0 && lane < T * p.top_k) {
+      p.idx[lane] = rt.e;
+      p.w[lane] = rt.w;
+      p.slot_pos[lane] = rt.pos;
+      p.sorted_slots[rt.pos] = lane;
+    }
+  } else {
+    // tile records: lane t < max_tiles loads record t and its first two token
+    // rows (one round trip, every wave for itself); the live ones are moved to
+    // the lowest lanes in order, so lane i holds live tile i
+    const bool in = lane < max_tiles;
+    const GemmTile tl = in ? p.tiles[lane] : GemmTile{0, 0, 0, 0};
+    const int r0 = in ? p.tile_rows[lane * kTileRows] : 0, r1 = in ? p.tile_rows[lane * kTileRows + 1] : 0;
+    // x staging loads go out together with the records
+    stage_issue<4>(xb, rx, x_pieces, 0, x_off);
+    const int rows = min(tl.m_end - tl.m_begin, T);
+    const bool live = in && rows > 0;
+    const uint64_t live_mask = __ballot(live);
+    n_live = __popcll(live_mask);
+    const int rank = __popcll(live_mask & ((1ull << lane) - 1ull));
+    const int dst = 4 * (live ? rank : n_live + (lane - rank));
+    c_e = __builtin_amdgcn_ds_permute(dst, tl.e);
+    c_m = __builtin_amdgcn_ds_permute(dst, tl.m_begin);
+    c_r = __builtin_amdgcn_ds_permute(dst, rows);
+    c_s = __builtin_amdgcn_ds_permute(dst, min(max(r0, 0), T - 1) | (min(max(r1, 0), T - 1) << 16));
+  }
   const int total = n_live * I;
   const int W = nblk * kValuWaves;
   const int wg = blk * kValuWaves + wave;
@@ -224,28 +246,53 @@ __device__ __forceinline__ void shared_down_blocks(const MidValuParams& m, int b
   }
 }
 
-// Launch 3 of the streaming few-token layer: blocks [0, gu_blocks) run the
-// routed gate/up loop, the rest the shared expert's down loop; the two are
-// independent and stream together.
-template <int JM, int TM, int KVD, bool FP8>
+// Blocks [0, gu_blocks) run the routed gate/up loop, the rest the shared
+// expert's down loop; the two are independent and stream together.  MPL > 0:
+// the gate/up waves route for themselves from the router's scores (no
+// routing launch between the router and the routed weights).
+template <int JM, int TM, int KVD, bool FP8, int MPL = 0>
 __global__ __launch_bounds__(kValuBlock) void gate_up_shared_down_kernel(GateUpValuParams p, int max_tiles,
                                                                          MidValuParams m, int gu_blocks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int b = (int)blockIdx.x;
   if (b < gu_blocks)
-    gate_up_valu_blocks<JM, TM, FP8>(p, max_tiles, b, gu_blocks, lds);
+    gate_up_valu_blocks<JM, TM, FP8, MPL>(p, MPL > 0 ? kMaxLiveTiles : max_tiles, b, gu_blocks, lds);
   else
     shared_down_blocks<KVD, TM>(m, b - gu_blocks, (int)gridDim.x - gu_blocks, lds);
 }
 
+// Launch 2 of the three-launch streaming layer: blocks [0, gu_blocks) run the
+// routed gate/up loop, each wave routing for itself from the router's scores
+// (so no routing launch sits between the router and the routed weights), the
+// rest stream the shared expert's gate/up row pairs, one pair per wave.
+template <int JM, int TM, bool FP8, int MPL>
+__global__ __launch_bounds__(kValuBlock) void route_gate_up_shared_gu_kernel(GateUpValuParams p, FrontValuParams f,
+                                                                             int gu_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int b = (int)blockIdx.x;
+  if (b < gu_blocks) {
+    gate_up_valu_blocks<JM, TM, FP8, MPL>(p, kMaxLiveTiles, b, gu_blocks, lds);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    shared_gate_up_pair(f.x, f.sh_gu, f.h_sh, f.tokens, f.hidden, f.shared_inter, f.limit, (b - gu_blocks) * 4 + wave,
+                        reinterpret_cast<uint16_t*>(lds));
+  }
+}
+
 // ---------------------------------------------------------------- down + combine
-template <int JM, int TM, bool FP8>
+// KVS > 0: the shared expert's down projection is folded in: column n also
+// reads row n of sh_dn (KVS 16-byte vectors of bf16 per lane) against h_sh
+// staged after the slots' h rows, and its product is added in fp32 to every
+// token's sum before the one rounding to bf16.
+template <int JM, int TM, bool FP8, int KVS = 0>
 __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // h of every slot [n][I] bf16
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // h of every slot [n][I] bf16, then h_sh [T][I_s]
   uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.tokens, k = p.top_k, n = T * k;
   const int H = p.hidden, I = p.inter, VR = I / kVecElems<FP8>, row_bytes = FP8 ? I : I / 2;
+  const int Is = KVS > 0 ? p.shared_inter : 0;
+  uint16_t* hs_lds = h_lds + n * I;
   // lane s < n holds slot s: expert, position of its h row, weight
   const int ls = min(lane, n - 1);
   const int my_e = p.idx[ls];
@@ -273,14 +320,23 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
   const int wg = (int)blockIdx.x * kValuWaves + wave;
   // a column past the end re-reads column H - 1 (cached) and is not stored
   const __amdgpu_buffer_rsrc_t rsh = make_rsrc(p.y_shared, p.y_shared ? (uint32_t)(T * H * 2) : 0u);
-  auto issue = [&](ColBuf<JM>& b, int col) {
+  const __amdgpu_buffer_rsrc_t rsd = make_rsrc(p.sh_dn, KVS > 0 ? (uint32_t)((int64_t)H * Is * 2) : 0u);
+  constexpr int KVS1 = KVS > 0 ? KVS : 1;
+  ValuRows<8, KVS1, 1> sd0, sd1;  // the shared row of each column buffer
+  auto issue = [&](ColBuf<JM>& b, ValuRows<8, KVS1, 1>& sd, int col) {
     const int64_t c = min(col, H - 1);
 #pragma unroll
     for (int jj = 0; jj < JM; ++jj) {
       b.q[jj] = *reinterpret_cast<const u32x4_t*>(qrow[jj] + c * row_bytes);
       b.s[jj] = srow[jj][c * (I / 32)];
     }
-    b.ysh = __builtin_amdgcn_raw_buffer_load_b16(rsh, (int)(lane < T ? (uint32_t)((lane * H + c) * 2) : kOob), 0, 0);
+    if constexpr (KVS > 0) {
+      const uint32_t off[1] = {(uint32_t)c * (uint32_t)Is * 2u};
+      valu_issue<8, KVS1, 1>(sd, rsd, off, Is);
+    } else {
+      b.ysh =
+          __builtin_amdgcn_raw_buffer_load_b16(rsh, (int)(lane < T ? (uint32_t)((lane * H + c) * 2) : kOob), 0, 0);
+    }
   };
 
   // h staging (slot order): the first batch goes out before the first
@@ -294,16 +350,25 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
   StageBatch<8> hb;
   stage_issue<8>(hb, rh, h_pieces, 0, h_off);
   ColBuf<JM> b0, b1;
-  issue(b0, wg);
+  issue(b0, sd0, wg);
   stage_commit<8>(hb, h_pieces, 0, lds);
   stage_pieces<8>(rh, h_pieces, lds, h_off, 8 * kValuBlock);
+  if constexpr (KVS > 0) valu_stage_rows(p.h_sh, Is, T, Is, hs_lds);
   __syncthreads();
   if (wg >= H) return;
 
-  auto compute = [&](const ColBuf<JM>& b, int col) {
+  auto compute = [&](const ColBuf<JM>& b, const ValuRows<8, KVS1, 1>& sd, int col) {
     float acc[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+    if constexpr (KVS > 0) {
+      float sh[1][TM];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) sh[0][t] = 0.f;
+      valu_accumulate<8, KVS1, 1, TM>(sd, hs_lds, Is, T, Is, sh);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) acc[t] = sh[0][t];
+    }
 #pragma unroll
     for (int jj = 0; jj < JM; ++jj) {
       __builtin_amdgcn_sched_barrier(0);  // one vector at a time (registers)
@@ -321,14 +386,14 @@ __global__ __launch_bounds__(kValuBlock) void down_combine_valu_kernel(DownValuP
       const float st = wave_sum_f32(acc[t]);
       r = lane == t ? st : r;
     }
-    if (lane < T) p.y[(int64_t)lane * H + col] = f32_to_bf16(r + bf16_to_f32((uint16_t)b.ysh));
+    if (lane < T) p.y[(int64_t)lane * H + col] = f32_to_bf16(KVS > 0 ? r : r + bf16_to_f32((uint16_t)b.ysh));
   };
 
   for (int col = wg; col < H; col += 2 * W) {
-    issue(b1, col + W);
-    compute(b0, col);
-    issue(b0, col + 2 * W);
-    if (col + W < H) compute(b1, col + W);
+    issue(b1, sd1, col + W);
+    compute(b0, sd0, col);
+    issue(b0, sd0, col + 2 * W);
+    if (col + W < H) compute(b1, sd1, col + W);
   }
 }
 
@@ -362,36 +427,48 @@ int down_jm(int slots, int inter, bool fp8) {
 using GateUpKernel = void (*)(GateUpValuParams, int);
 using GateUpSdKernel = void (*)(GateUpValuParams, int, MidValuParams, int);
 using DownKernel = void (*)(DownValuParams);
+using GateUpSdKernel2 = void (*)(GateUpValuParams, FrontValuParams, int);
 
-template <int TM, int KVD, bool FP8>
+template <int TM, int KVD, bool FP8, int MPL>
 GateUpSdKernel pick_gate_up_sd_t(int jm) {
   if constexpr (FP8) {
     switch (jm) {
-      case 2: return gate_up_shared_down_kernel<2, TM, KVD, true>;
-      case 4: return gate_up_shared_down_kernel<4, TM, KVD, true>;
-      case 10: return gate_up_shared_down_kernel<10, TM, KVD, true>;
-      case 14: return gate_up_shared_down_kernel<14, TM, KVD, true>;
+      case 2: return gate_up_shared_down_kernel<2, TM, KVD, true, MPL>;
+      case 4: return gate_up_shared_down_kernel<4, TM, KVD, true, MPL>;
+      case 10: return gate_up_shared_down_kernel<10, TM, KVD, true, MPL>;
+      case 14: return gate_up_shared_down_kernel<14, TM, KVD, true, MPL>;
       default: return nullptr;
     }
   } else {
     switch (jm) {
-      case 2: return gate_up_shared_down_kernel<2, TM, KVD, false>;
-      case 4: return gate_up_shared_down_kernel<4, TM, KVD, false>;
-      case 5: return gate_up_shared_down_kernel<5, TM, KVD, false>;
-      case 7: return gate_up_shared_down_kernel<7, TM, KVD, false>;
-      case 8: return gate_up_shared_down_kernel<8, TM, KVD, false>;
+      case 2: return gate_up_shared_down_kernel<2, TM, KVD, false, MPL>;
+      case 4: return gate_up_shared_down_kernel<4, TM, KVD, false, MPL>;
+      case 5: return gate_up_shared_down_kernel<5, TM, KVD, false, MPL>;
+      case 7: return gate_up_shared_down_kernel<7, TM, KVD, false, MPL>;
+      case 8: return gate_up_shared_down_kernel<8, TM, KVD, false, MPL>;
       default: return nullptr;
     }
   }
 }
-template <bool FP8>
+template <bool FP8, int MPL>
 GateUpSdKernel pick_gate_up_sd_f(int jm, int tokens, int kvd) {
-  if (kvd == 5) return tokens == 1 ? pick_gate_up_sd_t<1, 5, FP8>(jm) : pick_gate_up_sd_t<2, 5, FP8>(jm);
-  if (kvd == 10) return tokens == 1 ? pick_gate_up_sd_t<1, 10, FP8>(jm) : pick_gate_up_sd_t<2, 10, FP8>(jm);
+  if (kvd == 5) return tokens == 1 ? pick_gate_up_sd_t<1, 5, FP8, MPL>(jm) : pick_gate_up_sd_t<2, 5, FP8, MPL>(jm);
+  if (kvd == 10) return tokens == 1 ? pick_gate_up_sd_t<1, 10, FP8, MPL>(jm) : pick_gate_up_sd_t<2, 10, FP8, MPL>(jm);
   return nullptr;
 }
-GateUpSdKernel pick_gate_up_sd(int jm, int tokens, int kvd, bool fp8) {
-  return fp8 ? pick_gate_up_sd_f<true>(jm, tokens, kvd) : pick_gate_up_sd_f<false>(jm, tokens, kvd);
+template <int MPL>
+GateUpSdKernel pick_gate_up_sd_m(int jm, int tokens, int kvd, bool fp8) {
+  return fp8 ? pick_gate_up_sd_f<true, MPL>(jm, tokens, kvd) : pick_gate_up_sd_f<false, MPL>(jm, tokens, kvd);
+}
+// mpl = 0: tiles from the routing launch; 2, 6, 16: in-wave routing (route_mpl)
+GateUpSdKernel pick_gate_up_sd(int jm, int tokens, int kvd, bool fp8, int mpl = 0) {
+  switch (mpl) {
+    case 0: return pick_gate_up_sd_m<0>(jm, tokens, kvd, fp8);
+    case 2: return pick_gate_up_sd_m<2>(jm, tokens, kvd, fp8);
+    case 6: return pick_gate_up_sd_m<6>(jm, tokens, kvd, fp8);
+    case 16: return pick_gate_up_sd_m<16>(jm, tokens, kvd, fp8);
+    default: return nullptr;
+  }
 }
 
 template <int TM, bool FP8>
@@ -444,6 +521,69 @@ DownKernel pick_down_t(int jm) {
 DownKernel pick_down(int jm, int tokens, bool fp8) {
   if (fp8) return tokens == 1 ? pick_down_t<1, true>(jm) : pick_down_t<2, true>(jm);
   return tokens == 1 ? pick_down_t<1, false>(jm) : pick_down_t<2, false>(jm);
+}
+
+template <int TM, bool FP8, int MPL>
+GateUpSdKernel2 pick_route_gate_up_t(int jm) {
+  if constexpr (FP8) {
+    switch (jm) {
+      case 2: return route_gate_up_shared_gu_kernel<2, TM, true, MPL>;
+      case 4: return route_gate_up_shared_gu_kernel<4, TM, true, MPL>;
+      case 10: return route_gate_up_shared_gu_kernel<10, TM, true, MPL>;
+      case 14: return route_gate_up_shared_gu_kernel<14, TM, true, MPL>;
+      default: return nullptr;
+    }
+  } else {
+    switch (jm) {
+      case 2: return route_gate_up_shared_gu_kernel<2, TM, false, MPL>;
+      case 4: return route_gate_up_shared_gu_kernel<4, TM, false, MPL>;
+      case 5: return route_gate_up_shared_gu_kernel<5, TM, false, MPL>;
+      case 7: return route_gate_up_shared_gu_kernel<7, TM, false, MPL>;
+      case 8: return route_gate_up_shared_gu_kernel<8, TM, false, MPL>;
+      default: return nullptr;
+    }
+  }
+}
+// experts per lane of the in-wave routing: 2 (E <= 128), 6 (E <= 384) or 16 (E <= 1024)
+int route_mpl(int n_experts) { return n_experts <= 128 ? 2 : n_experts <= 384 ? 6 : 16; }
+template <bool FP8>
+GateUpSdKernel2 pick_route_gate_up_f(int jm, int tokens, int mpl) {
+  if (mpl == 2) return tokens == 1 ? pick_route_gate_up_t<1, FP8, 2>(jm) : pick_route_gate_up_t<2, FP8, 2>(jm);
+  if (mpl == 6) return tokens == 1 ? pick_route_gate_up_t<1, FP8, 6>(jm) : pick_route_gate_up_t<2, FP8, 6>(jm);
+  return tokens == 1 ? pick_route_gate_up_t<1, FP8, 16>(jm) : pick_route_gate_up_t<2, FP8, 16>(jm);
+}
+GateUpSdKernel2 pick_route_gate_up(int jm, int tokens, int mpl, bool fp8) {
+  return fp8 ? pick_route_gate_up_f<true>(jm, tokens, mpl) : pick_route_gate_up_f<false>(jm, tokens, mpl);
+}
+
+template <int TM, bool FP8, int KVS>
+DownKernel pick_down_shared_t(int jm) {
+  if constexpr (FP8) {
+    switch (jm) {
+      case 2: return down_combine_valu_kernel<2, TM, true, KVS>;
+      case 4: return down_combine_valu_kernel<4, TM, true, KVS>;
+      case 7: return down_combine_valu_kernel<7, TM, true, KVS>;
+      case 14: return down_combine_valu_kernel<14, TM, true, KVS>;
+      default: return nullptr;
+    }
+  } else {
+    switch (jm) {
+      case 2: return down_combine_valu_kernel<2, TM, false, KVS>;
+      case 4: return down_combine_valu_kernel<4, TM, false, KVS>;
+      case 7: return down_combine_valu_kernel<7, TM, false, KVS>;
+      case 9: return down_combine_valu_kernel<9, TM, false, KVS>;
+      case 14: return down_combine_valu_kernel<14, TM, false, KVS>;
+      default: return nullptr;
+    }
+  }
+}
+template <bool FP8>
+DownKernel pick_down_shared_f(int jm, int tokens, int kvs) {
+  if (kvs == 5) return tokens == 1 ? pick_down_shared_t<1, FP8, 5>(jm) : pick_down_shared_t<2, FP8, 5>(jm);
+  return tokens == 1 ? pick_down_shared_t<1, FP8, 10>(jm) : pick_down_shared_t<2, FP8, 10>(jm);
+}
+DownKernel pick_down_shared(int jm, int tokens, int kvs, bool fp8) {
+  return fp8 ? pick_down_shared_f<true>(jm, tokens, kvs) : pick_down_shared_f<false>(jm, tokens, kvs);
 }
 
 int device_cus() {
@@ -501,6 +641,52 @@ hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, 
   const size_t lx = (size_t)p.tokens * p.hidden * 2, lh = (size_t)m.tokens * m.shared_inter * 2;
   hipLaunchKernelGGL(kern, dim3((unsigned)(gu_blocks + sd_blocks)), dim3(kValuBlock), lx > lh ? lx : lh, stream, p,
                      max_tiles, m, gu_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_gate_up_shared_down(const GateUpValuParams& p, const MidValuParams& m, hipStream_t stream) {
+  // as many (tile, column) items as the routing can produce: T * k tiles of I columns
+  const int gu_blocks = valu_grid((int64_t)p.tokens * p.top_k * p.inter, kGateUpBlocksPerCu);
+  const int sd_blocks = valu_grid(m.hidden, kSharedDownBlocksPerCu);
+  const int kvd = m.shared_inter <= 5 * 8 * 64 ? 5 : 10;
+  auto kern = pick_gate_up_sd(gate_up_jm(p.hidden, p.fp8), p.tokens, kvd, p.fp8, route_mpl(p.n_experts));
+  if (!kern) return hipErrorInvalidValue;
+  const size_t lx = (size_t)p.tokens * p.hidden * 2, lh = (size_t)m.tokens * m.shared_inter * 2;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gu_blocks + sd_blocks)), dim3(kValuBlock), lx > lh ? lx : lh, stream, p,
+                     kMaxLiveTiles, m, gu_blocks);
+  return hipGetLastError();
+}
+
+bool route_gate_up_shared_gu_supported(int tokens, int hidden, int n_experts, int top_k, int shared_inter, bool fp8) {
+  return gate_up_valu_supported(tokens, hidden, kMaxLiveTiles, fp8) && tokens * top_k <= 64 && n_experts <= 1024 &&
+         (shared_inter == 0 || shared_inter <= 5120);
+}
+
+hipError_t launch_route_gate_up_shared_gu(const GateUpValuParams& p, const FrontValuParams& f, hipStream_t stream) {
+  // as many (tile, column) items as the routing can produce: T * k tiles of I columns
+  const int gu_blocks = valu_grid((int64_t)p.tokens * p.top_k * p.inter, kGateUpBlocksPerCu);
+  const int sh_blocks = f.sh_gu ? (f.shared_inter + 3) / 4 : 0;
+  auto kern = pick_route_gate_up(gate_up_jm(p.hidden, p.fp8), p.tokens, route_mpl(p.n_experts), p.fp8);
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gu_blocks + sh_blocks)), dim3(kValuBlock), (size_t)p.tokens * p.hidden * 2,
+                     stream, p, f, gu_blocks);
+  return hipGetLastError();
+}
+
+bool down_combine_shared_supported(int tokens, int top_k, int inter, int shared_inter, bool fp8) {
+  return down_valu_supported(tokens, top_k, inter, fp8) && shared_inter > 0 && shared_inter % 8 == 0 &&
+         shared_inter <= 10 * 8 * 64 &&
+         (int64_t)tokens * top_k * inter * 2 + (int64_t)tokens * shared_inter * 2 <= 64 * 1024;
+}
+
+hipError_t launch_down_combine_shared(const DownValuParams& p, hipStream_t stream) {
+  const dim3 grid(valu_grid(p.hidden, kDownBlocksPerCu));
+  const int n = p.tokens * p.top_k;
+  const size_t lds = (size_t)n * p.inter * 2 + (size_t)p.tokens * p.shared_inter * 2;
+  const int kvs = p.shared_inter <= 5 * 8 * 64 ? 5 : 10;
+  auto kern = pick_down_shared(down_jm(n, p.inter, p.fp8), p.tokens, kvs, p.fp8);
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, grid, dim3(kValuBlock), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -43,17 +43,13 @@ __device__ __forceinline__ void valu_issue(ValuRows<EPV, KV, NR>& st, const __am
     }
 }
 
-// out[r][t] = sum_k W[r][k] * x[t][k] for t < T (TM >= T), x_lds: T rows of
-// K bf16 at stride x_stride elements.  Every lane ends with the full sums.
+// out[r][t] += this lane's part of sum_k W[r][k] * x[t][k] for t < T (TM >=
+// T), x_lds: T rows of K bf16 at stride x_stride elements.
 template <int EPV, int KV, int NR, int TM>
-__device__ __forceinline__ void valu_compute(const ValuRows<EPV, KV, NR>& st, const uint16_t* x_lds, int x_stride,
-                                             int T, int K, float (&out)[NR][TM]) {
+__device__ __forceinline__ void valu_accumulate(const ValuRows<EPV, KV, NR>& st, const uint16_t* x_lds,
+                                                int x_stride, int T, int K, float (&out)[NR][TM]) {
   const int lane = threadIdx.x & 63;
   const int nv = K / EPV;
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int t = 0; t < TM; ++t) out[r][t] = 0.f;
 #pragma unroll
   for (int i = 0; i < KV; ++i) {
     const int v = min(lane + 64 * i, nv - 1);  // past the row the weights are zero; keep the read in range
@@ -92,6 +88,18 @@ __device__ __forceinline__ void valu_compute(const ValuRows<EPV, KV, NR>& st, co
       }
     }
   }
+}
+
+// out[r][t] = sum_k W[r][k] * x[t][k] for t < T (TM >= T), x_lds: T rows of
+// K bf16 at stride x_stride elements.  Every lane ends with the full sums.
+template <int EPV, int KV, int NR, int TM>
+__device__ __forceinline__ void valu_compute(const ValuRows<EPV, KV, NR>& st, const uint16_t* x_lds, int x_stride,
+                                             int T, int K, float (&out)[NR][TM]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) out[r][t] = 0.f;
+  valu_accumulate<EPV, KV, NR, TM>(st, x_lds, x_stride, T, K, out);
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -210,6 +218,29 @@ __device__ __forceinline__ void valu_stage_rows(const uint16_t* src, int64_t ld,
     const int t = q / per_row, c = q - t * per_row;
     return (uint32_t)(((int64_t)t * ld + 8 * c) * 2);
   });
+}
+
+// One gate/up row pair of the shared expert (gate row nrow and up row
+// I_s + nrow of sh_gu [2 I_s][H] bf16) against the T rows of x, by the
+// calling wave; the block stages x into x_lds (every thread of the block must
+// call it).  h_sh[t][nrow] = bf16(clamped SwiGLU).  Rows past I_s read zero
+// and write nothing.
+__device__ __forceinline__ void shared_gate_up_pair(const uint16_t* x, const uint16_t* sh_gu, uint16_t* h_sh, int T,
+                                                    int H, int Is, float limit, int nrow, uint16_t* x_lds) {
+  const int lane = threadIdx.x & 63;
+  const bool ok = nrow < Is;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(sh_gu, (uint32_t)((int64_t)2 * Is * H * 2));
+  const uint32_t off[2] = {ok ? (uint32_t)nrow * (uint32_t)H * 2u : kOob,
+                           ok ? (uint32_t)(Is + nrow) * (uint32_t)H * 2u : kOob};
+  ValuRows<8, 10, 2> st;
+  valu_issue<8, 10, 2>(st, rw, off, H);
+  valu_stage_rows(x, H, T, H, x_lds);
+  __syncthreads();
+  float out2[2][kValuMaxTokens];
+  valu_compute<8, 10, 2, kValuMaxTokens>(st, x_lds, H, T, H, out2);
+  if (lane == 0 && ok)
+    for (int t = 0; t < T; ++t)
+      h_sh[(int64_t)t * Is + nrow] = f32_to_bf16(clamped_swiglu(out2[0][t], out2[1][t], limit));
 }
 
 }  // namespace moe

@@ -202,6 +202,8 @@ struct WsLayout {
   bool stream4 = false;       // decode, T <= 2: router; routing + shared gate/up; routed gate/up + shared
                               // down; routed down + combine
   bool norm_in_router = false;  // stream4 with the pre-FFN norm folded into the router launch
+  bool stream3 = false;         // stream4 in three launches: every routed gate/up wave routes for itself,
+                                // the shared gate/up streams beside it, the shared down joins the combine
   bool mx6 = false;             // many tokens, MXFP4: routed gate/up on two-term MXFP6 activations (expert_mx6.hip)
   bool mx6_dn = false;          // ... and the routed down projection too
   Region xq, hq, x_norm, w3, logits, scores, xmx, tile_rows, hmx, rank, chunk_counts, chunk_base, tiles, tile_count, idx, w, offsets, sorted, slot_pos, h,
@@ -263,6 +265,11 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
               (c->n_shared == 0 ||
                moe::gate_up_shared_down_supported((int)tokens, c->hidden, (int)L.max_tiles, c->shared_inter, fp8));
     L.norm_in_router = L.stream4 && moe::router_norm_gemv_supported((int)tokens, c->hidden);
+    L.stream3 = L.stream4 &&
+                moe::route_gate_up_shared_gu_supported((int)tokens, c->hidden, E, c->top_k,
+                                                       c->n_shared ? c->shared_inter : 0, fp8) &&
+                (c->n_shared == 0 ||
+                 moe::down_combine_shared_supported((int)tokens, c->top_k, c->inter, c->shared_inter, fp8));
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
   if (c->n_shared == 1 && !L.decode && tokens >= 128 && tokens < 1024) {
@@ -509,6 +516,59 @@ moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, cons
   rp.tile_rows = at<int32_t>(ws, L.tile_rows);
   rp.max_tiles = (int)L.max_tiles;
   hipError_t err;
+  if (L.stream3 && !norm_gamma && c->n_shared) {
+    // 1. router scores beside the shared gate/up; 2. routed gate/up (in-wave
+    // routing) beside the shared down; 3. routed down + combine
+    err = moe::launch_decode_front_valu(f, st);
+    if (err == hipSuccess) err = mark(tl, "router_scores_shared_gate_up", st);
+    if (err != hipSuccess) return fail_hip(err, "router/shared gate-up launch");
+    moe::GateUpValuParams g{};
+    g.x = x;
+    g.gu_q = w->gu_q;
+    g.gu_s = w->gu_s;
+    g.h = at<uint16_t>(ws, L.h);
+    g.tokens = (int)T;
+    g.hidden = c->hidden;
+    g.inter = c->inter;
+    g.limit = c->swiglu_limit;
+    g.fp8 = L.fmt == moe::kWMxfp8;
+    g.scores = f.scores;
+    g.n_experts = E;
+    g.top_k = c->top_k;
+    g.route_scale = c->route_scale;
+    g.idx = idx;
+    g.w = wts;
+    g.slot_pos = slot_pos;
+    g.sorted_slots = rp.sorted_slots;
+    moe::MidValuParams m{};
+    m.sh_dn = w->sh_dn;
+    m.h_sh = h_sh;
+    m.y_sh = y_sh;
+    m.shared_inter = c->shared_inter;
+    m.tokens = (int)T;
+    m.hidden = c->hidden;
+    err = moe::launch_route_gate_up_shared_down(g, m, st);
+    if (err == hipSuccess) err = mark(tl, "route_gate_up_shared_down", st);
+    if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
+    moe::DownValuParams dv{};
+    dv.h = g.h;
+    dv.idx = idx;
+    dv.topk_w = wts;
+    dv.slot_pos = slot_pos;
+    dv.dn_q = w->dn_q;
+    dv.dn_s = w->dn_s;
+    dv.y_shared = y_sh;
+    dv.y = y;
+    dv.tokens = (int)T;
+    dv.top_k = c->top_k;
+    dv.hidden = c->hidden;
+    dv.inter = c->inter;
+    dv.fp8 = g.fp8;
+    err = moe::launch_down_combine_valu(dv, st);
+    if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
+    if (err != hipSuccess) return fail_hip(err, "down/combine launch");
+    return MOE_OK;
+  }
   if (norm_gamma) {
     err = moe::launch_router_norm_gemv(x_in, norm_gamma, (double)c->norm_eps, at<uint16_t>(ws, L.x_norm),
                                        w->router_w, (int)T, E, c->hidden, f.scores, w->router_bias, st);
@@ -518,6 +578,54 @@ moe_status layer_forward_decode4(const moe_config* c, const moe_weights* w, cons
     if (err == hipSuccess) err = mark(tl, "router_scores", st);
   }
   if (err != hipSuccess) return fail_hip(err, "router launch");
+  if (L.stream3) {
+    moe::GateUpValuParams g{};
+    g.x = x;
+    g.gu_q = w->gu_q;
+    g.gu_s = w->gu_s;
+    g.h = at<uint16_t>(ws, L.h);
+    g.tokens = (int)T;
+    g.hidden = c->hidden;
+    g.inter = c->inter;
+    g.limit = c->swiglu_limit;
+    g.fp8 = L.fmt == moe::kWMxfp8;
+    g.scores = f.scores;
+    g.n_experts = E;
+    g.top_k = c->top_k;
+    g.route_scale = c->route_scale;
+    g.idx = idx;
+    g.w = wts;
+    g.slot_pos = slot_pos;
+    g.sorted_slots = rp.sorted_slots;
+    err = moe::launch_route_gate_up_shared_gu(g, f, st);
+    if (err == hipSuccess) err = mark(tl, "route_gate_up_shared_gate_up", st);
+    if (err != hipSuccess) return fail_hip(err, "routed and shared gate/up launch");
+    moe::DownValuParams dv{};
+    dv.h = g.h;
+    dv.idx = idx;
+    dv.topk_w = wts;
+    dv.slot_pos = slot_pos;
+    dv.dn_q = w->dn_q;
+    dv.dn_s = w->dn_s;
+    dv.y = y;
+    dv.tokens = (int)T;
+    dv.top_k = c->top_k;
+    dv.hidden = c->hidden;
+    dv.inter = c->inter;
+    dv.fp8 = g.fp8;
+    if (c->n_shared) {
+      dv.sh_dn = w->sh_dn;
+      dv.h_sh = h_sh;
+      dv.shared_inter = c->shared_inter;
+      err = moe::launch_down_combine_shared(dv, st);
+      if (err == hipSuccess) err = mark(tl, "routed_down_shared_down_combine", st);
+    } else {
+      err = moe::launch_down_combine_valu(dv, st);
+      if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
+    }
+    if (err != hipSuccess) return fail_hip(err, "down/combine launch");
+    return MOE_OK;
+  }
   err = moe::launch_decode_route_shared_gu(f, rp, st);
   if (err == hipSuccess) err = mark(tl, "route_shared_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routing/shared gate-up launch");

@@ -261,6 +261,16 @@ struct GateUpValuParams {
   int tokens, hidden, inter;
   float limit;
   bool fp8;                   // MXFP8 (E4M3) codes instead of MXFP4
+  // routing in every wave (launch_route_gate_up_shared_gu): the router's
+  // scores [2][T][E] instead of tiles/tile_rows; the first wave writes the
+  // routing the later launches read (idx, w [T][k], slot_pos, sorted_slots [T*k])
+  const float* scores;
+  int n_experts, top_k;
+  float route_scale;
+  int32_t* idx;
+  float* w;
+  int32_t* slot_pos;
+  int32_t* sorted_slots;
 };
 struct DownValuParams {
   const uint16_t* h;          // [T*k][I] bf16, row = position
@@ -273,6 +283,11 @@ struct DownValuParams {
   uint16_t* y;                // [T][H]
   int tokens, top_k, hidden, inter;
   bool fp8;                   // MXFP8 (E4M3) codes instead of MXFP4
+  // shared expert folded in (launch_down_combine_shared): row n of sh_dn
+  // [H][I_s] bf16 against h_sh [T][I_s] is added to y[t][n] in fp32 (y_shared unused)
+  const uint16_t* sh_dn;
+  const uint16_t* h_sh;
+  int shared_inter;
 };
 bool gate_up_valu_supported(int tokens, int hidden, int max_tiles, bool fp8 = false);
 bool down_valu_supported(int tokens, int top_k, int inter, bool fp8 = false);
@@ -287,6 +302,21 @@ hipError_t launch_decode_route_shared_gu(const FrontValuParams& f, const RouteSm
 bool gate_up_shared_down_supported(int tokens, int hidden, int max_tiles, int shared_inter, bool fp8 = false);
 hipError_t launch_gate_up_shared_down(const GateUpValuParams& p, int max_tiles, const MidValuParams& m,
                                       hipStream_t stream);
+// The three-launch streaming layer (T <= 2, T * k <= 64):
+//   1. router GEMV writing the scores (launch_router_gemv / launch_router_norm_gemv);
+//   2. routed gate/up, every wave routing for itself from the scores, beside
+//      the shared expert's gate/up (f: x, sh_gu, h_sh, shared_inter, limit);
+//   3. routed down with the combine and the shared expert's down projection
+//      folded in (launch_down_combine_shared).
+bool route_gate_up_shared_gu_supported(int tokens, int hidden, int n_experts, int top_k, int shared_inter, bool fp8);
+hipError_t launch_route_gate_up_shared_gu(const GateUpValuParams& p, const FrontValuParams& f, hipStream_t stream);
+// Without the pre-FFN norm: 1. router GEMV beside the shared gate/up
+// (launch_decode_front_valu); 2. routed gate/up routing in every wave beside
+// the shared down (this launcher); 3. routed down with the combine
+// (launch_down_combine_valu).
+hipError_t launch_route_gate_up_shared_down(const GateUpValuParams& p, const MidValuParams& m, hipStream_t stream);
+bool down_combine_shared_supported(int tokens, int top_k, int inter, int shared_inter, bool fp8);
+hipError_t launch_down_combine_shared(const DownValuParams& p, hipStream_t stream);
 
 // Fused few-token routing: top-k of every token + permutation + tile table (T*k <= 1024).
 hipError_t launch_route_permute_small(const float* part, int ksplit, const float* bias, int tokens, int n_experts,
@@ -316,6 +346,7 @@ struct Mx6Params {
   int64_t ldc;
   float limit;
 };
+// hidden and inter multiples of 128, at most 5120 (the scales of a block's weight rows fit its LDS)
 bool mx6_supported(int hidden, int inter);
 int mx6_tile_rows();
 int64_t mx6_bytes(int64_t rows, int K);

@@ -22,6 +22,84 @@ __device__ __forceinline__ bool ranks_above(float u, int e, float bu, int be) {
   return u > bu || (u == bu && e < be);
 }
 
+// The selection of topk_token, from each lane's scores: u (selection) and s
+// (weights) of experts lane, lane + 64, ... (valid bits mark the ones that
+// exist).  Each lane sorts its slots once by (u desc, index asc) with an
+// odd-even transposition network (taken and unused slots rank last); a round
+// then takes the wave's best list head (max score, then lowest index among
+// the lanes holding it, with DPP reductions) and only the owner lane advances
+// its list.  Lane r < k ends with selection r (expert my_e, score my_s);
+// every lane gets gap = u(k) - u(k+1) (+inf when k == n_experts, or when
+// want_gap is false and the extra round is skipped).
+template <int kMaxPerLane>
+__device__ __forceinline__ void topk_select(const float (&u)[kMaxPerLane], const float (&s)[kMaxPerLane],
+                                            uint32_t valid, int n_experts, int top_k, int& my_e_out,
+                                            float& my_s_out, float& gap_out, bool want_gap = true) {
+  const int lane = threadIdx.x & 63;
+  float su[kMaxPerLane], ss[kMaxPerLane];
+  int se[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const bool v = (valid >> j) & 1u;
+    su[j] = v ? u[j] : -INFINITY;
+    se[j] = v ? lane + 64 * j : 0x7fffffff;
+    ss[j] = s[j];
+  }
+#pragma unroll
+  for (int pass = 0; pass < kMaxPerLane; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < kMaxPerLane; i += 2) {
+      const bool sw = (su[i + 1] > su[i]) | ((su[i + 1] == su[i]) & (se[i + 1] < se[i]));
+      const float tu = su[i], ts = ss[i];
+      const int te = se[i];
+      su[i] = sw ? su[i + 1] : su[i];
+      se[i] = sw ? se[i + 1] : se[i];
+      ss[i] = sw ? ss[i + 1] : ss[i];
+      su[i + 1] = sw ? tu : su[i + 1];
+      se[i + 1] = sw ? te : se[i + 1];
+      ss[i + 1] = sw ? ts : ss[i + 1];
+    }
+  }
+  float hu = su[0], hs = ss[0];
+  int he = se[0], ptr = 0;
+  float my_s = 0.f;
+  int my_e = 0;
+  float u_kth = 0.f, gap = INFINITY;
+  const int rounds = want_gap && top_k < n_experts ? top_k + 1 : top_k;
+  for (int r = 0; r < rounds; ++r) {
+    const float M = wave_max_f32(hu);
+    const int ew = wave_min_i32(hu == M ? he : 0x7fffffff);
+    if (r == top_k) {
+      gap = u_kth - M;
+      break;
+    }
+    const int owner = ew & 63;  // expert e lives in lane e % 64
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hs), owner));
+    if (lane == owner) {
+      ++ptr;
+      float nu = -INFINITY, ns = 0.f;
+      int ne = 0x7fffffff;
+#pragma unroll
+      for (int j = 1; j < kMaxPerLane; ++j) {
+        nu = (j == ptr) ? su[j] : nu;
+        ne = (j == ptr) ? se[j] : ne;
+        ns = (j == ptr) ? ss[j] : ns;
+      }
+      hu = nu;
+      he = ne;
+      hs = ns;
+    }
+    if (lane == r) {
+      my_s = sw;
+      my_e = ew;
+    }
+    u_kth = M;
+  }
+  my_e_out = my_e;
+  my_s_out = my_s;
+  gap_out = gap;
+}
+
 // Top-k of one token by one wave.  Lane l holds experts l, l+64, ... (at
 // most 16 each); logit e is the sum of `ksplit` partials at
 // part[z * part_stride + e], added in z order.  Top-k is k rounds of a
@@ -88,70 +166,9 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
     }
   }
   }
-  // Each lane sorts its slots once by (u desc, index asc) with an odd-even
-  // transposition network (taken and unused slots rank last); a round then
-  // takes the wave's best list head (max score, then lowest index among the
-  // lanes holding it, with DPP reductions) and only the owner lane advances
-  // its list.  Selection r is kept by lane r (k <= 16).
-  float su[kMaxPerLane], ss[kMaxPerLane];
-  int se[kMaxPerLane];
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const bool v = (valid >> j) & 1u;
-    su[j] = v ? u[j] : -INFINITY;
-    se[j] = v ? lane + 64 * j : 0x7fffffff;
-    ss[j] = s[j];
-  }
-#pragma unroll
-  for (int pass = 0; pass < kMaxPerLane; ++pass) {
-#pragma unroll
-    for (int i = pass & 1; i + 1 < kMaxPerLane; i += 2) {
-      const bool sw = (su[i + 1] > su[i]) | ((su[i + 1] == su[i]) & (se[i + 1] < se[i]));
-      const float tu = su[i], ts = ss[i];
-      const int te = se[i];
-      su[i] = sw ? su[i + 1] : su[i];
-      se[i] = sw ? se[i + 1] : se[i];
-      ss[i] = sw ? ss[i + 1] : ss[i];
-      su[i + 1] = sw ? tu : su[i + 1];
-      se[i + 1] = sw ? te : se[i + 1];
-      ss[i + 1] = sw ? ts : ss[i + 1];
-    }
-  }
-  float hu = su[0], hs = ss[0];
-  int he = se[0], ptr = 0;
-  float my_s = 0.f;
-  int my_e = 0;
-  float u_kth = 0.f, gap = INFINITY;
-  const int rounds = top_k < n_experts ? top_k + 1 : top_k;
-  for (int r = 0; r < rounds; ++r) {
-    const float M = wave_max_f32(hu);
-    const int ew = wave_min_i32(hu == M ? he : 0x7fffffff);
-    if (r == top_k) {
-      gap = u_kth - M;
-      break;
-    }
-    const int owner = ew & 63;  // expert e lives in lane e % 64
-    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hs), owner));
-    if (lane == owner) {
-      ++ptr;
-      float nu = -INFINITY, ns = 0.f;
-      int ne = 0x7fffffff;
-#pragma unroll
-      for (int j = 1; j < kMaxPerLane; ++j) {
-        nu = (j == ptr) ? su[j] : nu;
-        ne = (j == ptr) ? se[j] : ne;
-        ns = (j == ptr) ? ss[j] : ns;
-      }
-      hu = nu;
-      he = ne;
-      hs = ns;
-    }
-    if (lane == r) {
-      my_s = sw;
-      my_e = ew;
-    }
-    u_kth = M;
-  }
+  int my_e;
+  float my_s, gap;
+  topk_select<kMaxPerLane>(u, s, valid, n_experts, top_k, my_e, my_s, gap);
   // sum of the selected scores in selection order, then each lane r < k writes selection r
   float total = 0.f;
   for (int r = 0; r < top_k; ++r) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), r));
@@ -266,6 +283,92 @@ __device__ __forceinline__ void topk_token_pair(const float* const (&s_row)[2], 
       w_row[tt][lane] = total > 0.f ? route_scale * my_s[tt] / total : route_scale / (float)top_k;
     }
   }
+}
+
+// Routing of T <= 2 tokens (T * k <= 64) by the calling wave from the
+// router's scores (s at scores[t][e], selection scores u at scores[T + t][e]),
+// kept in registers.  Every wave that calls it gets the same values: the
+// same selection as topk_token, weights rho * s / sum s (rho / k for a zero
+// sum), and the stable permutation of the flat slots f = t * k + j by
+// expert.  Lane f < T * k holds slot f (expert e, weight w, position pos);
+// lane d < n_tiles holds the d-th distinct expert in ascending order (tile):
+// its expert, first position, rows, and the tokens of its rows (first |
+// second << 16; an expert has at most one row per token).
+struct WaveRoute {
+  int e, pos;
+  float w;
+  int t_e, t_m, t_r, t_src;
+  int n_tiles;
+};
+
+template <int kMaxPerLane>
+__device__ __forceinline__ WaveRoute route_wave_small(const float* __restrict__ scores, int tokens, int n_experts,
+                                                      int top_k, float route_scale) {
+  const int lane = threadIdx.x & 63;
+  const int n = tokens * top_k;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j)
+    if (lane + 64 * j < n_experts) valid |= 1u << j;
+  int sel_e[2] = {0, 0};
+  float sel_w[2] = {0.f, 0.f};
+  // both tokens' score loads issue before the first selection
+  float s[2][kMaxPerLane], u[2][kMaxPerLane];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tt = t < tokens ? t : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = min(lane + 64 * j, n_experts - 1);
+      s[t][j] = scores[(size_t)tt * n_experts + e];
+      const float uu = scores[(size_t)(tokens + tt) * n_experts + e];
+      u[t][j] = ((valid >> j) & 1u) && uu == uu ? uu : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t >= tokens) break;  // wave-uniform
+    float my_s, gap;
+    topk_select<kMaxPerLane>(u[t], s[t], valid, n_experts, top_k, sel_e[t], my_s, gap, false);
+    float total = 0.f;
+    for (int r = 0; r < top_k; ++r) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), r));
+    sel_w[t] = total > 0.f ? route_scale * my_s / total : route_scale / (float)top_k;
+  }
+  WaveRoute out;
+  // slot f = lane: token 0's selections are in lanes 0..k-1 already, token 1's move up by k
+  const int src = max(lane - top_k, 0);
+  const int e1 = __shfl(sel_e[1], src);
+  const float w1 = __shfl(sel_w[1], src);
+  const int e = lane < top_k ? sel_e[0] : e1;
+  out.w = lane < top_k ? sel_w[0] : w1;
+  const int ee = lane < n ? e : 0x7fffffff;
+  out.e = ee;
+  // position = slots with a smaller expert, plus earlier slots of the same one
+  int pos = 0, dup_before = 0, count = 0;
+  for (int j = 0; j < n; ++j) {
+    const int ej = __builtin_amdgcn_readlane(ee, j);
+    pos += (ej < ee) || (ej == ee && j < lane);
+    dup_before += (ej == ee && j < lane);
+    count += (ej == ee);
+  }
+  out.pos = pos;
+  const bool first = lane < n && dup_before == 0;
+  const uint64_t firsts = __ballot(first);
+  int distinct_smaller = 0;
+  for (int j = 0; j < n; ++j) {
+    const int ej = __builtin_amdgcn_readlane(ee, j);
+    distinct_smaller += (((firsts >> j) & 1ull) && ej < ee);
+  }
+  out.n_tiles = __popcll(firsts);
+  // tile records to lane distinct_smaller (the other lanes fill the rest, a bijection)
+  const int rank_other = lane - __popcll(firsts & ((1ull << lane) - 1ull));
+  const int dst = 4 * (first ? distinct_smaller : out.n_tiles + rank_other);
+  const int r0 = lane < n ? lane / top_k : 0, r1 = count > 1 ? 1 : r0;
+  out.t_e = __builtin_amdgcn_ds_permute(dst, first ? ee : 0);
+  out.t_m = __builtin_amdgcn_ds_permute(dst, pos);
+  out.t_r = __builtin_amdgcn_ds_permute(dst, first ? count : 0);
+  out.t_src = __builtin_amdgcn_ds_permute(dst, r0 | (r1 << 16));
+  return out;
 }
 
 // Few tokens: logits as a weight-streaming GEMV on the vector ALUs.  One

@@ -438,7 +438,7 @@ def test_layer_with_norm(tokens, variant):
 
 
 def test_layer_with_norm_decode_t1_full():
-    """Full-size one-token layer with the norm: four launches, the norm inside the first."""
+    """Full-size one-token layer with the norm: three launches, the norm inside the first."""
     inp = make_inputs(CONFIGS["decode_t1_h5120_e384_norm"], seed=0, device=DEV)
     stats, _, alt = _check_layer(inp)
     print("decode_t1 norm:", stats, "near-tie alternatives", len(alt))
@@ -446,8 +446,7 @@ def test_layer_with_norm_decode_t1_full():
     y = torch.empty((1, inp.cfg.hidden), dtype=torch.int16, device=DEV)
     names = [n for n, _ in moe.moe_layer_forward_timed(cfg, moe.weights_from(inp), inp.x, 1, y,
                                                        moe.workspace(cfg, 1, device=DEV))]
-    assert names == ["norm_router_scores", "route_shared_gate_up", "routed_gate_up_shared_down",
-                     "routed_down_combine"]
+    assert names == ["norm_router_scores", "route_gate_up_shared_gate_up", "routed_down_shared_down_combine"]
 
 
 def test_layer_with_norm_prefill_sampled():
@@ -521,7 +520,7 @@ def test_layer_fp8_decode_t1_full():
     y = torch.empty((1, inp.cfg.hidden), dtype=torch.int16, device=DEV)
     names = [n for n, _ in moe.moe_layer_forward_timed(cfg, moe.weights_from(inp), inp.x, 1, y,
                                                        moe.workspace(cfg, 1, device=DEV))]
-    assert names == ["router_scores", "route_shared_gate_up", "routed_gate_up_shared_down", "routed_down_combine"]
+    assert names == ["router_scores_shared_gate_up", "route_gate_up_shared_down", "routed_down_combine"]
 
 
 def test_layer_fp8_prefill_sampled():
