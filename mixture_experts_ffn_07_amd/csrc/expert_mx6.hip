@@ -159,7 +159,7 @@ constexpr int kMx6MaxK = 5120;                              // scales of kMx6Blo
 constexpr int kMx6SBytes = kMx6BlockRows * (kMx6MaxK / 32);  // LDS bytes of the block's scales
 constexpr int kMx6SPieces = kMx6SBytes / 16 / 256;           // 16-byte scale pieces per thread (at most)
 constexpr int kMx6ABufs = 4;                                // activation register buffers (chunks in flight)
-constexpr int kMx6Unroll = 8;                               // steps per loop iteration
+constexpr int kMx6Unroll = 4;                               // steps per loop iteration
 
 template <bool SWIGLU, int MT>
 __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sall, int e, int m_begin,

@@ -240,10 +240,15 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
     L.bm = 16 * L.gemm_mt;
-    // 128-row tiles of MXFP4 experts with K multiples of 128: the block-scaled
-    // MFMA on two-term MXFP6 rows, in tiles of its own height
-    L.mx6 = L.fmt == moe::kWMxfp4 && L.bm == 128 && moe::mx6_supported(c->hidden, c->inter);
-    if (L.mx6) L.bm = moe::mx6_tile_rows();
+    // MXFP4 experts with K multiples of 128: the block-scaled MFMA on two-term
+    // MXFP6 rows, in tiles of its own height, at any row count past the
+    // few-token kernels (it streams the weights straight to registers: 64
+    // tokens, routed gate/up 664 -> 533 us against the 32-row bf16 kernel)
+    L.mx6 = L.fmt == moe::kWMxfp4 && moe::mx6_supported(c->hidden, c->inter);
+    // it takes tiles of up to mx6_tile_rows() rows: 128-row tiles become
+    // tiles of that height; 32-row tiles stay, since the down projection's
+    // 32-row kernel, which shares the tile table, computes 32 rows per tile
+    if (L.mx6 && L.bm > moe::mx6_tile_rows()) L.bm = moe::mx6_tile_rows();
     // the down projection (K = I, 18 chunks at I = 2304) measured slower on
     // it than on the 512-row bf16 kernel, counting the pass that writes h as
     // MXFP6 (4096 tokens: 838 + 94 us against 813 us; 16384 tokens: 1253 +
@@ -870,6 +875,10 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   uint16_t* h = at<uint16_t>(ws, L.h);
   // few-token expert kernels exist for MXFP4 weights; MXFP8 ones take the grouped GEMM
   if (L.decode && L.fmt == moe::kWMxfp4) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
+  // every grouped kernel below computes up to 16 * gemm_mt rows of a tile
+  // (the MXFP6 one up to mx6_tile_rows()): a taller tile table would leave rows out
+  if (L.bm > 16 * L.gemm_mt || (L.mx6 && L.bm > moe::mx6_tile_rows()))
+    return fail(MOE_ERR_UNSUPPORTED, "internal: tile table taller than the grouped kernels' tiles");
   hipError_t err;
   if (L.mx6) {
     const int n = (int)(T * c->top_k);
