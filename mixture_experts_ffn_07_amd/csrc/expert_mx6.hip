@@ -53,18 +53,18 @@ __device__ __forceinline__ int mx6_scale_code(float amax) {
 }
 
 // ============================================================== bf16 rows -> two-term MXFP6 records
-// One thread per (row, 128-wide chunk): reads 256 bytes, writes one record.
-__global__ __launch_bounds__(256) void mx6_rows_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int rows,
-                                                       int K, uint8_t* __restrict__ dst, int64_t ld_dst) {
-  const int chunks = K / 128;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)rows * chunks) return;
-  const int r = (int)(t / chunks), c = (int)(t % chunks);
-  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src + (int64_t)r * ld_src + (int64_t)c * 128);
-  u32x4_t v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load(s + i);
-  uint32_t rec[52];
+// A unit is one row and 128-wide chunk: 256 bytes in, one 208-byte record
+// out.  With contiguous rows (ld_src = K, ld_dst = the record row) the units
+// of a block are one contiguous input range and one contiguous output range,
+// so both go through LDS as whole 16-byte pieces per lane (every load and
+// store instruction covers 4 KB); each thread converts one unit from LDS
+// (unit stride 272 bytes: the 16-byte reads of 8 consecutive units fall on
+// 8 different bank quads).
+constexpr int kMx6ConvUnits = 256;                 // units per block, one per thread
+constexpr int kMx6ConvIn = 272;                    // LDS bytes per staged input unit
+
+// one unit: 16 input pieces (bf16 x 8 each) -> 52 record dwords
+__device__ __forceinline__ void mx6_convert_unit(const u32x4_t (&v)[16], uint32_t (&rec)[52]) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     float x[32];
@@ -111,6 +111,62 @@ __global__ __launch_bounds__(256) void mx6_rows_kernel(const uint16_t* __restric
     rec[41 + 2 * g] = (uint32_t)lo[5];
     rec[48 + g] = (uint32_t)c1 | ((uint32_t)c2 << 8);
   }
+}
+
+// contiguous rows: block b converts units [256 b, 256 b + 256) of `units`
+__global__ __launch_bounds__(256) void mx6_rows_kernel(const uint16_t* __restrict__ src, int64_t units,
+                                                       uint8_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kMx6ConvUnits * kMx6ConvIn];
+  const int t = (int)threadIdx.x;
+  const int64_t u0 = (int64_t)blockIdx.x * kMx6ConvUnits;
+  const int nu = (int)min((int64_t)kMx6ConvUnits, units - u0);
+  const u32x4_t* in = reinterpret_cast<const u32x4_t*>(src) + u0 * 16;
+  // 16 pieces per unit: piece p -> unit p / 16, slot p % 16
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int p = t + 256 * i;
+    if (p < 16 * nu)
+      *reinterpret_cast<u32x4_t*>(buf + (p >> 4) * kMx6ConvIn + 16 * (p & 15)) = __builtin_nontemporal_load(in + p);
+  }
+  __syncthreads();
+  uint32_t rec[52];
+  if (t < nu) {
+    u32x4_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(buf + t * kMx6ConvIn + 16 * i);
+    mx6_convert_unit(v, rec);
+  }
+  __syncthreads();
+  if (t < nu) {
+#pragma unroll
+    for (int i = 0; i < 13; ++i)
+      *reinterpret_cast<u32x4_t*>(buf + t * kMx6Rec + 16 * i) =
+          u32x4_t{rec[4 * i], rec[4 * i + 1], rec[4 * i + 2], rec[4 * i + 3]};
+  }
+  __syncthreads();
+  u32x4_t* out = reinterpret_cast<u32x4_t*>(dst + u0 * kMx6Rec);
+#pragma unroll
+  for (int i = 0; i < 13; ++i) {
+    const int p = t + 256 * i;
+    if (p < 13 * nu) out[p] = *reinterpret_cast<const u32x4_t*>(buf + 16 * p);
+  }
+}
+
+// strided rows (ld_src != K or ld_dst != the record row): one thread per
+// unit, reading and writing directly
+__global__ __launch_bounds__(256) void mx6_rows_strided_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                               int rows, int K, uint8_t* __restrict__ dst,
+                                                               int64_t ld_dst) {
+  const int chunks = K / 128;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * chunks) return;
+  const int r = (int)(t / chunks), c = (int)(t % chunks);
+  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src + (int64_t)r * ld_src + (int64_t)c * 128);
+  u32x4_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load(s + i);
+  uint32_t rec[52];
+  mx6_convert_unit(v, rec);
   u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + (int64_t)r * ld_dst + (int64_t)c * kMx6Rec);
 #pragma unroll
   for (int i = 0; i < 13; ++i) d[i] = u32x4_t{rec[4 * i], rec[4 * i + 1], rec[4 * i + 2], rec[4 * i + 3]};
@@ -422,10 +478,14 @@ int mx6_tile_rows() { return kMx6TileRows; }
 int64_t mx6_bytes(int64_t rows, int K) { return rows * mx6_row_bytes(K); }
 
 hipError_t launch_mx6_rows(const uint16_t* src, int64_t ld_src, int rows, int K, uint8_t* dst, hipStream_t stream) {
-  const int64_t threads = (int64_t)rows * (K / 128);
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx6_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, src, ld_src, rows,
-                     K, dst, mx6_row_bytes(K));
+  const int64_t units = (int64_t)rows * (K / 128);
+  if (units == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((units + 255) / 256);
+  if (ld_src == K)  // contiguous rows in, contiguous records out
+    hipLaunchKernelGGL(mx6_rows_kernel, dim3(blocks), dim3(256), 0, stream, src, units, dst);
+  else
+    hipLaunchKernelGGL(mx6_rows_strided_kernel, dim3(blocks), dim3(256), 0, stream, src, ld_src, rows, K, dst,
+                       mx6_row_bytes(K));
   return hipGetLastError();
 }
 

@@ -72,6 +72,19 @@ def _e2m1_boundaries(device) -> torch.Tensor:
                         dtype=torch.float32, device=device)
 
 
+def _block_amax(blocks: torch.Tensor) -> torch.Tensor:
+    """max |x| over the last dimension (32) by pairwise elementwise maxima.
+
+    The same values as ``blocks.abs().amax(dim=-1)`` (a maximum is exact in any
+    order), without a reduction kernel: under rocprofv3 counter collection the
+    host process crashed inside the launch of torch's reduce kernel for amax.
+    """
+    a = blocks.abs()
+    while a.shape[-1] > 1:
+        a = torch.maximum(a[..., 0::2], a[..., 1::2])
+    return a.squeeze(-1)
+
+
 def mxfp4_encode(w: torch.Tensor):
     """Encode fp32 rows [R, K] (K % 32 == 0) to MXFP4 (OCP Microscaling v1.0 rule).
 
@@ -84,7 +97,7 @@ def mxfp4_encode(w: torch.Tensor):
     rows, k = w.shape
     assert k % 32 == 0
     blocks = w.reshape(rows, k // 32, 32)
-    amax = blocks.abs().amax(dim=-1)
+    amax = _block_amax(blocks)
     _, exp = torch.frexp(amax)  # amax = m * 2^exp, m in [0.5, 1)
     code = (exp.to(torch.int32) - 1 - 2 + 127).clamp(0, 254)
     code = torch.where(amax == 0, torch.full_like(code, 127), code)
@@ -108,7 +121,7 @@ def mxfp8_encode(w: torch.Tensor):
     rows, k = w.shape
     assert k % 32 == 0
     blocks = w.reshape(rows, k // 32, 32)
-    amax = blocks.abs().amax(dim=-1)
+    amax = _block_amax(blocks)
     _, exp = torch.frexp(amax)
     code = (exp.to(torch.int32) - 1 - 8 + 127).clamp(0, 254)
     code = torch.where(amax == 0, torch.full_like(code, 127), code)
