@@ -1058,25 +1058,32 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_wide_kernel(GemmParams p, 
 // multiplies the weight matrix bh + z * b_slice_stride over the k-part's range
 // of K chunks and writes Cf + slice * c_slice_stride (the router's three-term
 // split logits, summed later).
-template <int DS>
+// MR: 16-row MFMA tiles per wave along M, so a block tile is 32 MR rows
+// (MR = 4: 128 rows, two blocks per CU; MR = 8: 256 rows, one block per CU,
+// each weight chunk feeding twice the rows: the kernel is bound by moving
+// operands from L2 into LDS, so rows per weight byte is what counts).
+template <int DS, int MR = 4>
 constexpr int dense_pool_bytes() {
-  return DS * (128 + 256) * 64;
+  return DS * (32 * MR + 256) * 64;
 }
-template <bool SWIGLU, int DS, bool F32 = false>
+template <bool SWIGLU, int DS, bool F32 = false, int MR = 4>
 __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel(GemmParams p, int n_tiles,
                                                                                   int col_blocks) {
   static_assert(!(F32 && SWIGLU), "fp32 slices are plain products");
-  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS>()];
-  auto a_lds = [&](int i) { return pool + i * (128 * 64); };
-  auto b_lds = [&](int i) { return pool + DS * (128 * 64) + i * (256 * 64); };
+  static_assert(MR == 4 || MR == 8, "128- or 256-row block tiles");
+  constexpr int kRows = 32 * MR;    // block tile rows
+  constexpr int kALoads = MR / 4;   // activation loads (16 rows each) per wave and chunk
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS, MR>()];
+  auto a_lds = [&](int i) { return pool + i * (kRows * 64); };
+  auto b_lds = [&](int i) { return pool + DS * (kRows * 64) + i * (256 * 64); };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int cg = wave & 3, mh = wave >> 2;
 
   const PipeBlock pb = pipe_block(col_blocks);
   if (pb.tile >= n_tiles) return;
-  const int m_begin = pb.tile * 128;
-  const int rows = min(128, p.M - m_begin);
+  const int m_begin = pb.tile * kRows;
+  const int rows = min(kRows, p.M - m_begin);
   const int K = p.K;
   int c_lo = 0, nchunks = K / 32;
   const uint16_t* bh = p.bh;
@@ -1094,12 +1101,13 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
   // load sources: 16 rows x 64 bytes per instruction, lane l fills slot
   // l & 3 of row l >> 2 of its group
   const int lrow = lane >> 2;
-  const uint8_t* a_src;
-  {
-    const int r = 16 * wave + lrow;
+  const uint8_t* a_src[kALoads];
+#pragma unroll
+  for (int t = 0; t < kALoads; ++t) {
+    const int r = 16 * (wave + 8 * t) + lrow;
     const int q = (lane & 3) ^ ((r >> 2) & 3);
     const int src = min(m_begin + r, p.M - 1);
-    a_src = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src * p.lda) + 64 * c_lo + 16 * q;
+    a_src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)src * p.lda) + 64 * c_lo + 16 * q;
   }
   auto brow_col = [&](int brow) {
     int c;
@@ -1121,15 +1129,16 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
   }
   auto issue = [&](int c) {
     const int cc = min(c, nchunks - 1);
-    load_lds16(a_src + 64 * cc, lds_addr(a_lds(c % DS) + 1024 * wave));
+#pragma unroll
+    for (int t = 0; t < kALoads; ++t) load_lds16(a_src[t] + 64 * cc, lds_addr(a_lds(c % DS) + 1024 * (wave + 8 * t)));
     const uint32_t dst = lds_addr(b_lds(c % DS) + 2048 * wave);
 #pragma unroll
     for (int t = 0; t < 2; ++t) load_lds16(b_src[t] + 64 * cc, dst + 1024 * t);
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MR][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -1139,7 +1148,7 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 
   // at the top of iteration c, chunk c was issued DS - 1 iterations earlier;
   // the loads of the DS - 2 iterations since then may stay in flight
-  constexpr int kWait = (DS - 2) * 3;
+  constexpr int kWait = (DS - 2) * (kALoads + 2);
   for (int c = 0; c < nchunks; ++c) {
     if (c > 0) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait) : "memory");
@@ -1147,20 +1156,20 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
     }
     const uint8_t* al = a_lds(c % DS);
     const uint8_t* bl = b_lds(c % DS);
-    bf16x8_t a[4], b[4];
+    bf16x8_t a[MR], b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int br = 64 * cg + 16 * j + col;
       b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ar = 64 * mh + 16 * m + col;
+    for (int m = 0; m < MR; ++m) {
+      const int ar = 16 * MR * mh + 16 * m + col;
       a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
     }
     issue(c + DS - 1);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
   }
@@ -1168,10 +1177,10 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 
   const int n0w = n0 + cg * CW;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MR; ++m) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 64 * mh + 16 * m + 4 * grp + i;
+      const int r = 16 * MR * mh + 16 * m + 4 * grp + i;
       if (r < rows) {
         if constexpr (SWIGLU) {
 #pragma unroll
@@ -1202,6 +1211,7 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 // three stages, two blocks per CU (measured against four stages, one block
 // per CU: 274 -> 252 us for the gate/up projection at 4096 tokens)
 constexpr int kDenseStages = 3;
+constexpr int kDenseWideRows = 8192;  // rows from which the shared expert takes 256-row block tiles
 
 // MXFP4 weights with K a multiple of 128 at up to this many rows per expert
 // on average: 32-row tiles for the pipelined kernel
@@ -1259,11 +1269,21 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     }
     if constexpr (BF == kWBf16) {
       if (!p.tiles && !p.gather) {  // one dense bf16 matrix (the shared expert): the pipelined dense kernel
-        const int n_tiles = (p.M + 127) / 128;
+        // 256-row block tiles from 8192 rows (16384 tokens: gate/up 843 -> 751 us, down 424 -> 387 us);
+        // below that they leave too few blocks for the CUs (4096 tokens: 243 -> 278 us), and 128-row
+        // tiles at two blocks per CU stay
         const int col_blocks = (int)g.y;
-        const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
-        hipLaunchKernelGGL((expert_gemm_dense_kernel<SWIGLU, kDenseStages>), g1, dim3(512), 0, stream, p, n_tiles,
-                           col_blocks);
+        if (p.M >= kDenseWideRows) {
+          const int n_tiles = (p.M + 255) / 256;
+          const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
+          hipLaunchKernelGGL((expert_gemm_dense_kernel<SWIGLU, kDenseStages, false, 8>), g1, dim3(512), 0, stream,
+                             p, n_tiles, col_blocks);
+        } else {
+          const int n_tiles = (p.M + 127) / 128;
+          const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
+          hipLaunchKernelGGL((expert_gemm_dense_kernel<SWIGLU, kDenseStages>), g1, dim3(512), 0, stream, p,
+                             n_tiles, col_blocks);
+        }
         return;
       }
     }
