@@ -1058,22 +1058,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_wide_kernel(GemmParams p, 
 // multiplies the weight matrix bh + z * b_slice_stride over the k-part's range
 // of K chunks and writes Cf + slice * c_slice_stride (the router's three-term
 // split logits, summed later).
-// MR: 16-row MFMA tiles per wave along M, so a block tile is 32 MR rows
-// (MR = 4: 128 rows, two blocks per CU; MR = 8: 256 rows, one block per CU,
-// each weight chunk feeding twice the rows: the kernel is bound by moving
-// operands from L2 into LDS, so rows per weight byte is what counts).
-template <int DS, int MR = 4>
+template <int DS>
 constexpr int dense_pool_bytes() {
-  return DS * (32 * MR + 256) * 64;
+  return DS * (128 + 256) * 64;
 }
-template <bool SWIGLU, int DS, bool F32 = false, int MR = 4>
+template <bool SWIGLU, int DS, bool F32 = false>
 __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel(GemmParams p, int n_tiles,
                                                                                   int col_blocks) {
   static_assert(!(F32 && SWIGLU), "fp32 slices are plain products");
-  static_assert(MR == 4 || MR == 8, "128- or 256-row block tiles");
+  constexpr int MR = 4;             // 16-row MFMA tiles per wave
   constexpr int kRows = 32 * MR;    // block tile rows
   constexpr int kALoads = MR / 4;   // activation loads (16 rows each) per wave and chunk
-  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS, MR>()];
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_pool_bytes<DS>()];
   auto a_lds = [&](int i) { return pool + i * (kRows * 64); };
   auto b_lds = [&](int i) { return pool + DS * (kRows * 64) + i * (256 * 64); };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1142,10 +1138,34 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // one chunk's MFMA operands: this wave's MR row tiles and 4 column tiles
+  struct Frag {
+    bf16x8_t a[MR], b[4];
+  };
+  auto read_frags = [&](int c, Frag& f) {
+    const uint8_t* al = a_lds(c % DS);
+    const uint8_t* bl = b_lds(c % DS);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int br = 64 * cg + 16 * j + col;
+      f.b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int ar = 16 * MR * mh + 16 * m + col;
+      f.a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
+    }
+  };
+  auto mfmas = [&](const Frag& f) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_16x16x32(f.a[m], f.b[j], acc[m][j]);
+  };
+
 #pragma unroll
   for (int c = 0; c < DS - 1; ++c) issue(c);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-
   // at the top of iteration c, chunk c was issued DS - 1 iterations earlier;
   // the loads of the DS - 2 iterations since then may stay in flight
   constexpr int kWait = (DS - 2) * (kALoads + 2);
@@ -1154,24 +1174,10 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait) : "memory");
       asm volatile("s_barrier" ::: "memory");
     }
-    const uint8_t* al = a_lds(c % DS);
-    const uint8_t* bl = b_lds(c % DS);
-    bf16x8_t a[MR], b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int br = 64 * cg + 16 * j + col;
-      b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
-    }
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int ar = 16 * MR * mh + 16 * m + col;
-      a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
-    }
+    Frag f;
+    read_frags(c, f);
     issue(c + DS - 1);
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
+    mfmas(f);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the block ends
 
@@ -1208,10 +1214,177 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
     }
   }
 }
+// ---------------------------------------------------------------- dense bf16, whole rounds
+// The shared expert from a few thousand rows: block tiles of 256 rows x NT
+// weight rows, one block per CU, eight waves.  The widths give whole rounds
+// of blocks at the layer's shapes, where the 256-column tiles of the kernel
+// above leave a partial last round (4096 rows: 288 or 320 tiles for 256 CUs):
+// NT = 288 for SwiGLU (144 h columns: 9 gate MFMA tiles, then their 9 up
+// tiles) makes 16 column blocks of I = 2304, NT = 320 makes 16 of H = 5120,
+// so 4096 rows give 16 x 16 tiles, one round.
+// Waves, SwiGLU: rows 64 (w & 3) .. + 63; waves 0-3 take h tiles 0..4
+// (10 MFMA column tiles), waves 4-7 h tiles 5..8 (8), so each SIMD, running
+// waves w and w + 4, does 18 column tiles.  Otherwise: rows 128 (w >> 2) ..
+// + 127 against column tiles 5 (w & 3) .. + 4.
+// Operands come in chunks of 32 K (64 bytes per row) by global-to-LDS loads,
+// DS stages, with the XOR swizzle of the kernel above.  A chunk is 16
+// activation and NT / 16 weight load instructions (16 rows x 64 bytes each),
+// instruction i issued by wave i % 8: waves below the remainder issue one
+// more, and each wave's wait counts its own loads.
+template <bool SWIGLU>
+constexpr int dense_nt_cols() {
+  return SWIGLU ? 288 : 320;
+}
+template <bool SWIGLU, int DS>
+constexpr int dense_nt_pool_bytes() {
+  return DS * (256 + dense_nt_cols<SWIGLU>()) * 64;
+}
+
+// one wave's share: MRW row tiles from row r0 of the block tile, NJW column
+// tiles (block tile columns 16 bt[j] ..), LW load instructions per chunk
+template <bool SWIGLU, int DS, int MRW, int NJW, int LW>
+__device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool, int m_begin, int rows, int n0,
+                                              int r0, const int (&bt)[NJW], int wave) {
+  constexpr int NT = dense_nt_cols<SWIGLU>();
+  constexpr int kStage = (256 + NT) * 64;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4, lrow = lane >> 2;
+  const int K = p.K, nchunks = K / 32;
+  const uint8_t* src[LW];
+  int dst[LW];
+#pragma unroll
+  for (int t = 0; t < LW; ++t) {
+    const int i = wave + 8 * t;  // load instruction: activation rows 16 i.., or weight tile i - 16
+    const int r = 16 * (i < 16 ? i : i - 16) + lrow;
+    const int q = (lane & 3) ^ ((r >> 2) & 3);
+    if (i < 16) {
+      const int srow = min(m_begin + r, p.M - 1);
+      src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)srow * p.lda) + 16 * q;
+    } else {
+      int64_t c;
+      if constexpr (SWIGLU) {
+        const int tj = r >> 4, n = r & 15;  // gate tiles 0..8, up tiles 9..17
+        const int h = min(n0 + 16 * (tj < 9 ? tj : tj - 9) + n, p.N - 1);
+        c = h + (tj < 9 ? 0 : p.b_row_second);
+      } else {
+        c = min(n0 + r, p.N - 1);
+      }
+      src[t] = reinterpret_cast<const uint8_t*>(p.bh + c * K) + 16 * q;
+    }
+    dst[t] = 1024 * i;  // activation rows, then weight rows, 64 bytes each
+  }
+  auto issue = [&](int c) {
+    const int cc = min(c, nchunks - 1);
+    uint8_t* st = pool + (c % DS) * kStage;
+#pragma unroll
+    for (int t = 0; t < LW; ++t) load_lds16(src[t] + 64 * cc, lds_addr(st + dst[t]));
+  };
+
+  f32x4_t acc[MRW][NJW];
+#pragma unroll
+  for (int m = 0; m < MRW; ++m)
+#pragma unroll
+    for (int j = 0; j < NJW; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int c = 0; c < DS - 1; ++c) issue(c);
+  // at the top of iteration c, chunk c was issued DS - 1 iterations earlier;
+  // the loads of the DS - 2 iterations since then may stay in flight
+  constexpr int kWait = (DS - 2) * LW;
+  for (int c = 0; c < nchunks; ++c) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kWait) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c + DS - 1);  // into the stage read in the previous iteration
+    const uint8_t* al = pool + (c % DS) * kStage;
+    const uint8_t* bl = al + 256 * 64;
+    bf16x8_t a[MRW], b[NJW];
+#pragma unroll
+    for (int m = 0; m < MRW; ++m) {
+      const int ar = r0 + 16 * m + col;
+      a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < NJW; ++j) {
+      const int br = 16 * bt[j] + col;
+      b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < NJW; ++j)
+#pragma unroll
+      for (int m = 0; m < MRW; ++m) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the block ends
+
+#pragma unroll
+  for (int m = 0; m < MRW; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + 16 * m + 4 * grp + i;
+      if (r < rows) {
+        uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
+        if constexpr (SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < NJW / 2; ++j) {
+            const int n = n0 + 16 * bt[j] + col;
+            if (n < p.N) crow[n] = f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + NJW / 2][i], p.limit));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJW; ++j) {
+            const int n = n0 + 16 * bt[j] + col;
+            if (n < p.N) crow[n] = f32_to_bf16(acc[m][j][i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool SWIGLU, int DS>
+__global__ __launch_bounds__(512) void expert_gemm_dense_nt_kernel(GemmParams p, int n_tiles, int col_blocks) {
+  constexpr int NT = dense_nt_cols<SWIGLU>();
+  constexpr int kInstr = 16 + NT / 16;  // load instructions per chunk
+  constexpr int kLo = kInstr / 8, kRem = kInstr % 8;
+  static_assert(kRem > 0 && kRem <= 4, "waves 0 .. kRem - 1 issue one load more");
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_nt_pool_bytes<SWIGLU, DS>()];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const PipeBlock pb = pipe_block(col_blocks);
+  if (pb.tile >= n_tiles) return;
+  const int m_begin = pb.tile * 256;
+  const int rows = min(256, p.M - m_begin);
+  const int n0 = pb.cb * (SWIGLU ? NT / 2 : NT);
+  if constexpr (SWIGLU) {
+    const int r0 = 64 * (wave & 3);
+    if (wave < 4) {
+      const int p0 = 0;
+      const int bt[10] = {p0, p0 + 1, p0 + 2, p0 + 3, p0 + 4, 9 + p0, 10 + p0, 11 + p0, 12 + p0, 13 + p0};
+      if (wave < kRem)
+        dense_nt_wave<true, DS, 4, 10, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      else
+        dense_nt_wave<true, DS, 4, 10, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+    } else {
+      const int bt[8] = {5, 6, 7, 8, 14, 15, 16, 17};
+      dense_nt_wave<true, DS, 4, 8, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+    }
+  } else {
+    const int r0 = 128 * (wave >> 2), j0 = 5 * (wave & 3);
+    const int bt[5] = {j0, j0 + 1, j0 + 2, j0 + 3, j0 + 4};
+    if (wave < kRem)
+      dense_nt_wave<false, DS, 8, 5, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
+    else
+      dense_nt_wave<false, DS, 8, 5, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+  }
+}
+
 // three stages, two blocks per CU (measured against four stages, one block
 // per CU: 274 -> 252 us for the gate/up projection at 4096 tokens)
 constexpr int kDenseStages = 3;
-constexpr int kDenseWideRows = 8192;  // rows from which the shared expert takes 256-row block tiles
+// rows from which the shared expert takes the whole-round tiles (4096 rows:
+// gate/up 253 -> 182 us, down 128 -> 100 us; 16384 rows, against 256-row tiles
+// of the kernel above: 741 -> 686 us, 385 -> 375 us)
+constexpr int kDenseNtRows = 2048;
+constexpr int kDenseNtStages = 4;
 
 // MXFP4 weights with K a multiple of 128 at up to this many rows per expert
 // on average: 32-row tiles for the pipelined kernel
@@ -1269,15 +1442,15 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
     }
     if constexpr (BF == kWBf16) {
       if (!p.tiles && !p.gather) {  // one dense bf16 matrix (the shared expert): the pipelined dense kernel
-        // 256-row block tiles from 8192 rows (16384 tokens: gate/up 843 -> 751 us, down 424 -> 387 us);
-        // below that they leave too few blocks for the CUs (4096 tokens: 243 -> 278 us), and 128-row
-        // tiles at two blocks per CU stay
+        // from kDenseNtRows rows the whole-round tiles, below that 128-row tiles at two blocks per CU
         const int col_blocks = (int)g.y;
-        if (p.M >= kDenseWideRows) {
+        if (p.M >= kDenseNtRows) {
           const int n_tiles = (p.M + 255) / 256;
-          const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
-          hipLaunchKernelGGL((expert_gemm_dense_kernel<SWIGLU, kDenseStages, false, 8>), g1, dim3(512), 0, stream,
-                             p, n_tiles, col_blocks);
+          const int cols_nt = SWIGLU ? dense_nt_cols<SWIGLU>() / 2 : dense_nt_cols<SWIGLU>();
+          const int col_blocks_nt = (p.N + cols_nt - 1) / cols_nt;
+          const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks_nt));
+          hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages>), g1, dim3(512), 0, stream, p,
+                             n_tiles, col_blocks_nt);
         } else {
           const int n_tiles = (p.M + 127) / 128;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));

@@ -113,12 +113,20 @@ def test_permute_bit_exact(t, e, k, skew):
 
 
 @pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k",
-                                     "fp8_t2", "t200_sliced_shared", "t1100_dense_shared"])
+                                     "fp8_t2", "t200_sliced_shared", "t1100_dense_shared", "t2100_whole_round_shared",
+                                     "t2048_whole_round_one_chunk"])
 def test_expert_ffn(variant):
+    """Routed slots and the shared expert against the oracle over every row.  From 2048 tokens the shared
+    expert takes the whole-round dense kernel: at 2100 tokens with a ragged last row tile, 160 h columns (a
+    144-column block and a ragged one), 352 output columns (320 and a ragged block) and K of 11 and 5 chunks;
+    at 2048 tokens with K of one chunk and fewer columns than one block."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
            "t200_sliced_shared": base.with_(tokens=200, shared_inter=160),
            "t1100_dense_shared": base.with_(tokens=1100, hidden=384, shared_inter=224),
+           "t2100_whole_round_shared": base.with_(tokens=2100, hidden=352, shared_inter=160),
+           "t2048_whole_round_one_chunk": base.with_(tokens=2048, hidden=32, inter=32, shared_inter=32, n_experts=4,
+                                                     top_k=2),
            "fp8": base.with_(tokens=40, expert_format="mxfp8"),
            "fp8_t2": base.with_(tokens=2, expert_format="mxfp8"),
            "fp8_ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224, expert_format="mxfp8"),
@@ -259,7 +267,7 @@ def test_layer_many_rows_per_expert(variant):
     """Tiles of up to 128 rows (the pipelined grouped GEMM when K is a multiple of 128), sampled rows; from 1024
     tokens the shared expert takes the dense pipelined kernel (ragged last row tile and column block), from 128 to
     1023 tokens the same kernel over K slices plus their sum (one-chunk slices, fewer weight rows than a block);
-    from 8192 tokens the dense kernel's 256-row block tiles."""
+    from 2048 tokens the whole-round dense kernel's 256-row block tiles."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"two_tiles_per_expert": base.with_(tokens=1024),             # ~192 rows per expert
            "three_chunks": base.with_(tokens=600, n_experts=8, hidden=384, inter=128, shared_inter=256),
@@ -268,7 +276,7 @@ def test_layer_many_rows_per_expert(variant):
            "dense_shared_ragged": base.with_(tokens=1100, n_experts=8, hidden=384, inter=128, shared_inter=96),
            "dense_shared_one_chunk": base.with_(tokens=1031, n_experts=8, hidden=32, inter=32,
                                                 shared_inter=32),
-           # from 8192 tokens: 256-row block tiles, ragged last row tile and column block
+           # whole-round dense kernel: 256-row block tiles, ragged last row tile and column blocks
            "dense_shared_256_ragged": base.with_(tokens=8300, n_experts=8, hidden=256, inter=128,
                                                  shared_inter=160),
            "sliced_shared_t128": base.with_(tokens=128, n_experts=8, hidden=352, inter=128, shared_inter=96),
