@@ -1226,37 +1226,47 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 // (10 MFMA column tiles), waves 4-7 h tiles 5..8 (8), so each SIMD, running
 // waves w and w + 4, does 18 column tiles.  Otherwise: rows 128 (w >> 2) ..
 // + 127 against column tiles 5 (w & 3) .. + 4.
-// Operands come in chunks of 32 K (64 bytes per row) by global-to-LDS loads,
-// DS stages, with the XOR swizzle of the kernel above.  A chunk is 16
-// activation and NT / 16 weight load instructions (16 rows x 64 bytes each),
-// instruction i issued by wave i % 8: waves below the remainder issue one
-// more, and each wave's wait counts its own loads.
+// Operands come in chunks of KC = 64 K (128 bytes per row: a probe moved
+// 1.6x the bytes per CU with 128-byte row pieces as with 64-byte ones) or 32
+// K, by global-to-LDS loads, DS stages, XOR-swizzled.  A chunk's load
+// instructions (1 KB each: 8 rows x 128 bytes, or 16 x 64) are dealt to the
+// waves round-robin: waves below the remainder issue one more, and each
+// wave's wait counts its own loads.
 template <bool SWIGLU>
 constexpr int dense_nt_cols() {
   return SWIGLU ? 288 : 320;
 }
-template <bool SWIGLU, int DS>
+// KC: K per chunk, 32 (64-byte row pieces) or 64 (128-byte pieces)
+template <bool SWIGLU, int DS, int KC>
 constexpr int dense_nt_pool_bytes() {
-  return DS * (256 + dense_nt_cols<SWIGLU>()) * 64;
+  return DS * (256 + dense_nt_cols<SWIGLU>()) * 2 * KC;
 }
 
 // one wave's share: MRW row tiles from row r0 of the block tile, NJW column
 // tiles (block tile columns 16 bt[j] ..), LW load instructions per chunk
-template <bool SWIGLU, int DS, int MRW, int NJW, int LW>
+template <bool SWIGLU, int DS, int KC, int MRW, int NJW, int LW>
 __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool, int m_begin, int rows, int n0,
                                               int r0, const int (&bt)[NJW], int wave) {
   constexpr int NT = dense_nt_cols<SWIGLU>();
-  constexpr int kStage = (256 + NT) * 64;
-  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4, lrow = lane >> 2;
-  const int K = p.K, nchunks = K / 32;
+  constexpr int kRowB = 2 * KC;          // bytes of a row per chunk
+  constexpr int kPieces = kRowB / 16;    // 16-byte pieces per row
+  constexpr int kRpi = 64 / kPieces;     // rows per load instruction
+  constexpr int kAInstr = 256 / kRpi;    // activation load instructions per chunk
+  constexpr int kStage = (256 + NT) * kRowB;
+  // piece q of row r sits in slot q ^ swz(r): the 16 lanes reading one MFMA
+  // operand column (16 rows, one piece) hit 16 different bank groups
+  auto swz = [](int r) { return kPieces == 4 ? (r >> 2) & 3 : (r >> 1) & 7; };
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int lrow = lane / kPieces, lslot = lane % kPieces;
+  const int K = p.K, nchunks = K / KC;
   const uint8_t* src[LW];
   int dst[LW];
 #pragma unroll
   for (int t = 0; t < LW; ++t) {
-    const int i = wave + 8 * t;  // load instruction: activation rows 16 i.., or weight tile i - 16
-    const int r = 16 * (i < 16 ? i : i - 16) + lrow;
-    const int q = (lane & 3) ^ ((r >> 2) & 3);
-    if (i < 16) {
+    const int i = wave + 8 * t;  // load instruction: activation rows kRpi i.., or weight rows kRpi (i - kAInstr)..
+    const int r = kRpi * (i < kAInstr ? i : i - kAInstr) + lrow;
+    const int q = lslot ^ swz(r);
+    if (i < kAInstr) {
       const int srow = min(m_begin + r, p.M - 1);
       src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)srow * p.lda) + 16 * q;
     } else {
@@ -1270,13 +1280,13 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
       }
       src[t] = reinterpret_cast<const uint8_t*>(p.bh + c * K) + 16 * q;
     }
-    dst[t] = 1024 * i;  // activation rows, then weight rows, 64 bytes each
+    dst[t] = 1024 * i;  // activation rows, then weight rows, kRowB bytes each
   }
   auto issue = [&](int c) {
     const int cc = min(c, nchunks - 1);
     uint8_t* st = pool + (c % DS) * kStage;
 #pragma unroll
-    for (int t = 0; t < LW; ++t) load_lds16(src[t] + 64 * cc, lds_addr(st + dst[t]));
+    for (int t = 0; t < LW; ++t) load_lds16(src[t] + kRowB * cc, lds_addr(st + dst[t]));
   };
 
   f32x4_t acc[MRW][NJW];
@@ -1296,23 +1306,26 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
     __builtin_amdgcn_sched_barrier(0);
     issue(c + DS - 1);  // into the stage read in the previous iteration
     const uint8_t* al = pool + (c % DS) * kStage;
-    const uint8_t* bl = al + 256 * 64;
-    bf16x8_t a[MRW], b[NJW];
+    const uint8_t* bl = al + 256 * kRowB;
 #pragma unroll
-    for (int m = 0; m < MRW; ++m) {
-      const int ar = r0 + 16 * m + col;
-      a[m] = *reinterpret_cast<const bf16x8_t*>(al + 64 * ar + 16 * (grp ^ ((ar >> 2) & 3)));
+    for (int s = 0; s < KC / 32; ++s) {  // MFMA K steps of 32
+      bf16x8_t a[MRW], b[NJW];
+#pragma unroll
+      for (int m = 0; m < MRW; ++m) {
+        const int ar = r0 + 16 * m + col;
+        a[m] = *reinterpret_cast<const bf16x8_t*>(al + kRowB * ar + 16 * ((4 * s + grp) ^ swz(ar)));
+      }
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int br = 16 * bt[j] + col;
+        b[j] = *reinterpret_cast<const bf16x8_t*>(bl + kRowB * br + 16 * ((4 * s + grp) ^ swz(br)));
+      }
+#pragma unroll
+      for (int j = 0; j < NJW; ++j)
+#pragma unroll
+        for (int m = 0; m < MRW; ++m) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int j = 0; j < NJW; ++j) {
-      const int br = 16 * bt[j] + col;
-      b[j] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * br + 16 * (grp ^ ((br >> 2) & 3)));
-    }
-#pragma unroll
-    for (int j = 0; j < NJW; ++j)
-#pragma unroll
-      for (int m = 0; m < MRW; ++m) acc[m][j] = mfma_16x16x32(a[m], b[j], acc[m][j]);
-    __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the block ends
 
@@ -1341,13 +1354,13 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
   }
 }
 
-template <bool SWIGLU, int DS>
+template <bool SWIGLU, int DS, int KC>
 __global__ __launch_bounds__(512) void expert_gemm_dense_nt_kernel(GemmParams p, int n_tiles, int col_blocks) {
   constexpr int NT = dense_nt_cols<SWIGLU>();
-  constexpr int kInstr = 16 + NT / 16;  // load instructions per chunk
+  constexpr int kInstr = (256 + NT) * 2 * KC / 1024;  // load instructions per chunk
   constexpr int kLo = kInstr / 8, kRem = kInstr % 8;
-  static_assert(kRem > 0 && kRem <= 4, "waves 0 .. kRem - 1 issue one load more");
-  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_nt_pool_bytes<SWIGLU, DS>()];
+  static_assert(kRem <= 4, "waves 0 .. kRem - 1 issue one load more");
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_nt_pool_bytes<SWIGLU, DS, KC>()];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const PipeBlock pb = pipe_block(col_blocks);
   if (pb.tile >= n_tiles) return;
@@ -1357,23 +1370,22 @@ __global__ __launch_bounds__(512) void expert_gemm_dense_nt_kernel(GemmParams p,
   if constexpr (SWIGLU) {
     const int r0 = 64 * (wave & 3);
     if (wave < 4) {
-      const int p0 = 0;
-      const int bt[10] = {p0, p0 + 1, p0 + 2, p0 + 3, p0 + 4, 9 + p0, 10 + p0, 11 + p0, 12 + p0, 13 + p0};
+      const int bt[10] = {0, 1, 2, 3, 4, 9, 10, 11, 12, 13};
       if (wave < kRem)
-        dense_nt_wave<true, DS, 4, 10, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
+        dense_nt_wave<true, DS, KC, 4, 10, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
       else
-        dense_nt_wave<true, DS, 4, 10, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+        dense_nt_wave<true, DS, KC, 4, 10, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
     } else {
       const int bt[8] = {5, 6, 7, 8, 14, 15, 16, 17};
-      dense_nt_wave<true, DS, 4, 8, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      dense_nt_wave<true, DS, KC, 4, 8, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
     }
   } else {
     const int r0 = 128 * (wave >> 2), j0 = 5 * (wave & 3);
     const int bt[5] = {j0, j0 + 1, j0 + 2, j0 + 3, j0 + 4};
     if (wave < kRem)
-      dense_nt_wave<false, DS, 8, 5, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      dense_nt_wave<false, DS, KC, 8, 5, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
     else
-      dense_nt_wave<false, DS, 8, 5, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      dense_nt_wave<false, DS, KC, 8, 5, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
   }
 }
 
@@ -1382,9 +1394,12 @@ __global__ __launch_bounds__(512) void expert_gemm_dense_nt_kernel(GemmParams p,
 constexpr int kDenseStages = 3;
 // rows from which the shared expert takes the whole-round tiles (4096 rows:
 // gate/up 253 -> 182 us, down 128 -> 100 us; 16384 rows, against 256-row tiles
-// of the kernel above: 741 -> 686 us, 385 -> 375 us)
+// of the kernel above: 741 -> 686 us, 385 -> 375 us).  With K a multiple of
+// 64 it takes 64-wide chunks, two stages (4096 rows: 176 -> 160 us, 98 -> 89
+// us; 16384 rows: 676 -> 617 us, 370 -> 339 us), else 32-wide chunks, four.
 constexpr int kDenseNtRows = 2048;
 constexpr int kDenseNtStages = 4;
+constexpr int kDenseNtStages64 = 2;
 
 // MXFP4 weights with K a multiple of 128 at up to this many rows per expert
 // on average: 32-row tiles for the pipelined kernel
@@ -1449,8 +1464,12 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
           const int cols_nt = SWIGLU ? dense_nt_cols<SWIGLU>() / 2 : dense_nt_cols<SWIGLU>();
           const int col_blocks_nt = (p.N + cols_nt - 1) / cols_nt;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks_nt));
-          hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages>), g1, dim3(512), 0, stream, p,
-                             n_tiles, col_blocks_nt);
+          if (p.K % 64 == 0)
+            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages64, 64>), g1, dim3(512), 0, stream,
+                               p, n_tiles, col_blocks_nt);
+          else
+            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages, 32>), g1, dim3(512), 0, stream,
+                               p, n_tiles, col_blocks_nt);
         } else {
           const int n_tiles = (p.M + 127) / 128;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
