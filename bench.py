@@ -56,9 +56,10 @@ def parse():
                     help="comma-separated workloads timed in the same run ('' for none); each runs "
                          "min(steps, 200) timed steps after min(warmup, 20) untimed ones")
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
-    ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
-                    help="timed steps as plain launches on one HIP stream or as replays of HIP graphs (one per "
-                         "cycle over the weight sets); the other form is timed afterwards for reference")
+    ap.add_argument("--launch", choices=["stream", "graph"], default="graph",
+                    help="timed steps as replays of HIP graphs (one per cycle over the weight sets, as a serving "
+                         "loop replays its captured step over a model's layers) or as plain launches on one HIP "
+                         "stream; the other form is timed afterwards for reference")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed forwards per weight set for kernel times")
     ap.add_argument("--cpu-sample", type=int, default=16, help="decode tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--json-out", default="")
