@@ -1232,22 +1232,29 @@ __global__ __launch_bounds__(512, DS <= 3 ? 2 : 1) void expert_gemm_dense_kernel
 // instructions (1 KB each: 8 rows x 128 bytes, or 16 x 64) are dealt to the
 // waves round-robin: waves below the remainder issue one more, and each
 // wave's wait counts its own loads.
-template <bool SWIGLU>
+// MODE: what the block tile's weight rows are and what the epilogue writes
+constexpr int kNtPlain = 0;   // 320 output columns, bf16
+constexpr int kNtSwiglu = 1;  // 144 h columns (9 gate, then 9 up MFMA tiles), clamped SwiGLU, bf16
+constexpr int kNtRouter = 2;  // 96 experts x the three bf16 terms of W_r (term t of expert tile u is MFMA
+                              // tile 6 t + u), the terms added in fp32, written as fp32 partial logits
+template <int MODE>
 constexpr int dense_nt_cols() {
-  return SWIGLU ? 288 : 320;
+  return MODE == kNtPlain ? 320 : 288;
 }
 // KC: K per chunk, 32 (64-byte row pieces) or 64 (128-byte pieces)
-template <bool SWIGLU, int DS, int KC>
+template <int MODE, int DS, int KC>
 constexpr int dense_nt_pool_bytes() {
-  return DS * (256 + dense_nt_cols<SWIGLU>()) * 2 * KC;
+  return DS * (256 + dense_nt_cols<MODE>()) * 2 * KC;
 }
 
 // one wave's share: MRW row tiles from row r0 of the block tile, NJW column
-// tiles (block tile columns 16 bt[j] ..), LW load instructions per chunk
-template <bool SWIGLU, int DS, int KC, int MRW, int NJW, int LW>
+// tiles (block tile columns 16 bt[j] ..), LW load instructions per chunk,
+// chunks [c_lo, c_lo + nchunks) of K
+template <int MODE, int DS, int KC, int MRW, int NJW, int LW>
 __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool, int m_begin, int rows, int n0,
-                                              int r0, const int (&bt)[NJW], int wave) {
-  constexpr int NT = dense_nt_cols<SWIGLU>();
+                                              int r0, const int (&bt)[NJW], int wave, int c_lo, int nchunks,
+                                              int slice) {
+  constexpr int NT = dense_nt_cols<MODE>();
   constexpr int kRowB = 2 * KC;          // bytes of a row per chunk
   constexpr int kPieces = kRowB / 16;    // 16-byte pieces per row
   constexpr int kRpi = 64 / kPieces;     // rows per load instruction
@@ -1258,7 +1265,7 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
   auto swz = [](int r) { return kPieces == 4 ? (r >> 2) & 3 : (r >> 1) & 7; };
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int lrow = lane / kPieces, lslot = lane % kPieces;
-  const int K = p.K, nchunks = K / KC;
+  const int K = p.K;
   const uint8_t* src[LW];
   int dst[LW];
 #pragma unroll
@@ -1268,17 +1275,19 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
     const int q = lslot ^ swz(r);
     if (i < kAInstr) {
       const int srow = min(m_begin + r, p.M - 1);
-      src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)srow * p.lda) + 16 * q;
+      src[t] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)srow * p.lda) + kRowB * c_lo + 16 * q;
     } else {
+      const int tj = r >> 4, n = r & 15;
       int64_t c;
-      if constexpr (SWIGLU) {
-        const int tj = r >> 4, n = r & 15;  // gate tiles 0..8, up tiles 9..17
+      if constexpr (MODE == kNtSwiglu) {  // gate tiles 0..8, up tiles 9..17
         const int h = min(n0 + 16 * (tj < 9 ? tj : tj - 9) + n, p.N - 1);
         c = h + (tj < 9 ? 0 : p.b_row_second);
+      } else if constexpr (MODE == kNtRouter) {  // term tj / 6 of expert n0 + 16 (tj % 6) + n
+        c = (int64_t)(tj / 6) * p.N + min(n0 + 16 * (tj % 6) + n, p.N - 1);
       } else {
         c = min(n0 + r, p.N - 1);
       }
-      src[t] = reinterpret_cast<const uint8_t*>(p.bh + c * K) + 16 * q;
+      src[t] = reinterpret_cast<const uint8_t*>(p.bh + c * K) + kRowB * c_lo + 16 * q;
     }
     dst[t] = 1024 * i;  // activation rows, then weight rows, kRowB bytes each
   }
@@ -1335,14 +1344,22 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + 16 * m + 4 * grp + i;
       if (r < rows) {
-        uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
-        if constexpr (SWIGLU) {
+        if constexpr (MODE == kNtSwiglu) {
+          uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
 #pragma unroll
           for (int j = 0; j < NJW / 2; ++j) {
             const int n = n0 + 16 * bt[j] + col;
             if (n < p.N) crow[n] = f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + NJW / 2][i], p.limit));
           }
+        } else if constexpr (MODE == kNtRouter) {
+          float* crow = p.Cf + (int64_t)slice * p.c_slice_stride + (int64_t)(m_begin + r) * p.ldc;
+#pragma unroll
+          for (int j = 0; j < NJW / 3; ++j) {
+            const int n = n0 + 16 * bt[j] + col;
+            if (n < p.N) crow[n] = (acc[m][j][i] + acc[m][j + NJW / 3][i]) + acc[m][j + 2 * NJW / 3][i];
+          }
         } else {
+          uint16_t* crow = p.C + (int64_t)(m_begin + r) * p.ldc;
 #pragma unroll
           for (int j = 0; j < NJW; ++j) {
             const int n = n0 + 16 * bt[j] + col;
@@ -1354,38 +1371,60 @@ __device__ __forceinline__ void dense_nt_wave(const GemmParams& p, uint8_t* pool
   }
 }
 
-template <bool SWIGLU, int DS, int KC>
+// Router mode: blockIdx.y is the K range (p.k_slices of them), written to
+// partial-logit slice blockIdx.y.
+template <int MODE, int DS, int KC>
 __global__ __launch_bounds__(512) void expert_gemm_dense_nt_kernel(GemmParams p, int n_tiles, int col_blocks) {
-  constexpr int NT = dense_nt_cols<SWIGLU>();
+  constexpr int NT = dense_nt_cols<MODE>();
   constexpr int kInstr = (256 + NT) * 2 * KC / 1024;  // load instructions per chunk
   constexpr int kLo = kInstr / 8, kRem = kInstr % 8;
   static_assert(kRem <= 4, "waves 0 .. kRem - 1 issue one load more");
-  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_nt_pool_bytes<SWIGLU, DS, KC>()];
+  __shared__ __attribute__((aligned(16))) uint8_t pool[dense_nt_pool_bytes<MODE, DS, KC>()];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const PipeBlock pb = pipe_block(col_blocks);
   if (pb.tile >= n_tiles) return;
   const int m_begin = pb.tile * 256;
   const int rows = min(256, p.M - m_begin);
-  const int n0 = pb.cb * (SWIGLU ? NT / 2 : NT);
-  if constexpr (SWIGLU) {
+  const int n0 = pb.cb * (MODE == kNtSwiglu ? NT / 2 : MODE == kNtRouter ? NT / 3 : NT);
+  int c_lo = 0, nchunks = p.K / KC, slice = 0;
+  if constexpr (MODE == kNtRouter) {
+    // the host sizes k_slices so that every range holds at least one chunk
+    slice = (int)blockIdx.y;
+    const int per = (nchunks + p.k_slices - 1) / p.k_slices;
+    c_lo = slice * per;
+    nchunks = min(nchunks - c_lo, per);
+  }
+  if constexpr (MODE == kNtSwiglu || MODE == kNtRouter) {
+    // rows 64 (w & 3) ..; waves 0-3 and 4-7 split the 18 column tiles so
+    // that each SIMD (waves w and w + 4) does all 18: SwiGLU h tiles 0-4 /
+    // 5-8 with their up tiles, router expert tiles 0-2 / 3-5 with all terms
     const int r0 = 64 * (wave & 3);
-    if (wave < 4) {
-      const int bt[10] = {0, 1, 2, 3, 4, 9, 10, 11, 12, 13};
-      if (wave < kRem)
-        dense_nt_wave<true, DS, KC, 4, 10, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
-      else
-        dense_nt_wave<true, DS, KC, 4, 10, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+    if constexpr (MODE == kNtSwiglu) {
+      if (wave < 4) {
+        const int bt[10] = {0, 1, 2, 3, 4, 9, 10, 11, 12, 13};
+        if (wave < kRem)
+          dense_nt_wave<MODE, DS, KC, 4, 10, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, 0);
+        else
+          dense_nt_wave<MODE, DS, KC, 4, 10, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, 0);
+      } else {
+        const int bt[8] = {5, 6, 7, 8, 14, 15, 16, 17};
+        dense_nt_wave<MODE, DS, KC, 4, 8, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, 0);
+      }
     } else {
-      const int bt[8] = {5, 6, 7, 8, 14, 15, 16, 17};
-      dense_nt_wave<true, DS, KC, 4, 8, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      const int u0 = wave < 4 ? 0 : 3;
+      const int bt[9] = {u0, u0 + 1, u0 + 2, u0 + 6, u0 + 7, u0 + 8, u0 + 12, u0 + 13, u0 + 14};
+      if (wave < kRem)
+        dense_nt_wave<MODE, DS, KC, 4, 9, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, slice);
+      else
+        dense_nt_wave<MODE, DS, KC, 4, 9, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, slice);
     }
   } else {
     const int r0 = 128 * (wave >> 2), j0 = 5 * (wave & 3);
     const int bt[5] = {j0, j0 + 1, j0 + 2, j0 + 3, j0 + 4};
     if (wave < kRem)
-      dense_nt_wave<false, DS, KC, 8, 5, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      dense_nt_wave<MODE, DS, KC, 8, 5, kLo + 1>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, 0);
     else
-      dense_nt_wave<false, DS, KC, 8, 5, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave);
+      dense_nt_wave<MODE, DS, KC, 8, 5, kLo>(p, pool, m_begin, rows, n0, r0, bt, wave, c_lo, nchunks, 0);
   }
 }
 
@@ -1460,15 +1499,16 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
         // from kDenseNtRows rows the whole-round tiles, below that 128-row tiles at two blocks per CU
         const int col_blocks = (int)g.y;
         if (p.M >= kDenseNtRows) {
+          constexpr int MODE = SWIGLU ? kNtSwiglu : kNtPlain;
           const int n_tiles = (p.M + 255) / 256;
-          const int cols_nt = SWIGLU ? dense_nt_cols<SWIGLU>() / 2 : dense_nt_cols<SWIGLU>();
+          const int cols_nt = SWIGLU ? dense_nt_cols<MODE>() / 2 : dense_nt_cols<MODE>();
           const int col_blocks_nt = (p.N + cols_nt - 1) / cols_nt;
           const dim3 g1((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks_nt));
           if (p.K % 64 == 0)
-            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages64, 64>), g1, dim3(512), 0, stream,
+            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<MODE, kDenseNtStages64, 64>), g1, dim3(512), 0, stream,
                                p, n_tiles, col_blocks_nt);
           else
-            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<SWIGLU, kDenseNtStages, 32>), g1, dim3(512), 0, stream,
+            hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<MODE, kDenseNtStages, 32>), g1, dim3(512), 0, stream,
                                p, n_tiles, col_blocks_nt);
         } else {
           const int n_tiles = (p.M + 127) / 128;
@@ -1517,6 +1557,31 @@ hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream)
   const dim3 g((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks), (unsigned)slices);
   hipLaunchKernelGGL((expert_gemm_dense_kernel<false, kDenseStages, true>), g, dim3(512), 0, stream, p, n_tiles,
                      col_blocks);
+  return hipGetLastError();
+}
+
+// Router logits from the whole-round kernel: p.bh holds the three bf16 terms
+// of W_r ([3][N][K]), p.k_slices K ranges, partial slice r = range r.
+int dense_router_kslices(int M, int n_experts, int K) {
+  const int tiles = (M + 255) / 256 * ((n_experts + 95) / 96);
+  const int nch = K % 64 == 0 ? K / 64 : K / 32;
+  int ks = (256 + tiles - 1) / tiles;
+  ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+  if (ks > nch) ks = nch;
+  const int per = (nch + ks - 1) / ks;
+  return (nch + per - 1) / per;  // every K range non-empty
+}
+
+hipError_t launch_dense_router(const GemmParams& p, hipStream_t stream) {
+  const int n_tiles = (p.M + 255) / 256;
+  const int col_blocks = (p.N + 95) / 96;
+  const dim3 g((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks), (unsigned)p.k_slices);
+  if (p.K % 64 == 0)
+    hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<kNtRouter, kDenseNtStages64, 64>), g, dim3(512), 0, stream, p,
+                       n_tiles, col_blocks);
+  else
+    hipLaunchKernelGGL((expert_gemm_dense_nt_kernel<kNtRouter, kDenseNtStages, 32>), g, dim3(512), 0, stream, p,
+                       n_tiles, col_blocks);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ struct RouterPlan {
   // workspace and the dense pipelined GEMM runs each over this many K ranges
   // (ksplit = 3 * dense_kslices); 0: router_logits_kernel
   int dense_kslices;
+  // the whole-round dense kernel over dense_kslices K ranges, the three terms
+  // added in its registers (ksplit = dense_kslices)
+  bool whole_round;
 };
 RouterPlan router_plan(int64_t tokens, int n_experts, int hidden);
 // workspace bytes for the split weights (0 unless plan.dense_kslices > 0)
@@ -112,6 +115,11 @@ hipError_t launch_expert_gemm(const GemmParams& p, bool swiglu, WeightFormat fmt
                               hipStream_t stream);
 // dense bf16 rows [0, M) of A against `slices` weight slices, fp32 outputs (see GemmParams)
 hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream);
+// the router logits on the whole-round dense kernel from kDenseRouterNtTokens
+// tokens: p.bh = the three bf16 terms of W_r [3][N][K], p.k_slices K ranges,
+// each written to partial slice Cf + r * c_slice_stride with the terms added
+int dense_router_kslices(int M, int n_experts, int K);
+hipError_t launch_dense_router(const GemmParams& p, hipStream_t stream);
 // One dense bf16 matrix (no tiles, no gather) split over K: k_slices fp32
 // partial products into `part` ([k_slices][M][N or 2N] floats), then their sum
 // (and clamp-SwiGLU with the up rows at b_row_second == N) to C in bf16.

@@ -162,6 +162,9 @@ __global__ __launch_bounds__(256) void router_split3_kernel(const float* __restr
 // GEMM with 128-token tiles (4096 tokens: logits 180 -> 81 us, the top-k over
 // twelve partials 19 -> 37 us; 16384 tokens: 269 + 18 -> 140 + 23 us).
 constexpr int64_t kDenseRouterMinTokens = 1024;
+// From this many tokens the whole-round dense kernel, the three terms added
+// in its registers: ksplit = the K ranges alone.
+constexpr int64_t kDenseRouterNtTokens = 2048;
 
 size_t router_w3_bytes(const RouterPlan& plan, int n_experts, int hidden) {
   return plan.dense_kslices > 0 ? sizeof(uint16_t) * 3 * (size_t)n_experts * hidden : 0;
@@ -170,6 +173,15 @@ size_t router_w3_bytes(const RouterPlan& plan, int n_experts, int hidden) {
 RouterPlan router_plan(int64_t tokens, int n_experts, int hidden) {
   RouterPlan p;
   p.dense_kslices = 0;
+  p.whole_round = false;
+  if (tokens >= kDenseRouterNtTokens) {
+    p.dense_kslices = dense_router_kslices((int)tokens, n_experts, hidden);
+    p.ksplit = p.dense_kslices;
+    p.whole_round = true;
+    p.mt = 4;
+    p.chunks_per_split = 0;
+    return p;
+  }
   if (tokens >= kDenseRouterMinTokens) {
     // three weight slices x K ranges: aim for ~768 blocks of 128 tokens x 256 experts
     const int64_t per_slice = (tokens + 127) / 128 * ((n_experts + 255) / 256);
@@ -221,6 +233,7 @@ hipError_t launch_router_logits(const RouterPlan& plan, const uint16_t* x, const
     q.k_slices = plan.dense_kslices;
     q.b_slice_stride = n;
     q.c_slice_stride = (int64_t)tokens * n_experts;
+    if (plan.whole_round) return launch_dense_router(q, stream);
     return launch_dense_f32(q, 3 * plan.dense_kslices, stream);
   }
   dim3 grid((tokens + 16 * plan.mt - 1) / (16 * plan.mt), (n_experts + 63) / 64, plan.ksplit);

@@ -264,12 +264,13 @@ def test_layer_one_two_tokens(tokens, variant):
 
 @pytest.mark.parametrize("variant", ["two_tiles_per_expert", "three_chunks", "ragged_k_fallback", "down_one_chunk",
                                      "dense_shared_ragged", "dense_shared_one_chunk", "dense_shared_256_ragged",
-                                     "sliced_shared_t128", "sliced_shared_t1023"])
+                                     "sliced_shared_t128", "sliced_shared_t1023", "whole_round_router_ragged"])
 def test_layer_many_rows_per_expert(variant):
     """Tiles of up to 128 rows (the pipelined grouped GEMM when K is a multiple of 128), sampled rows; from 1024
     tokens the shared expert takes the dense pipelined kernel (ragged last row tile and column block), from 128 to
     1023 tokens the same kernel over K slices plus their sum (one-chunk slices, fewer weight rows than a block);
-    from 2048 tokens the whole-round dense kernel's 256-row block tiles."""
+    from 2048 tokens the whole-round dense kernel's 256-row block tiles, also for the router logits (40 experts:
+    one 96-expert block, mostly past the end; K of 11 32-wide chunks over several K ranges)."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"two_tiles_per_expert": base.with_(tokens=1024),             # ~192 rows per expert
            "three_chunks": base.with_(tokens=600, n_experts=8, hidden=384, inter=128, shared_inter=256),
@@ -282,6 +283,8 @@ def test_layer_many_rows_per_expert(variant):
            "dense_shared_256_ragged": base.with_(tokens=8300, n_experts=8, hidden=256, inter=128,
                                                  shared_inter=160),
            "sliced_shared_t128": base.with_(tokens=128, n_experts=8, hidden=352, inter=128, shared_inter=96),
+           "whole_round_router_ragged": base.with_(tokens=2100, n_experts=40, hidden=352, inter=128,
+                                                   shared_inter=160),
            "sliced_shared_t1023": base.with_(tokens=1023, n_experts=16, hidden=256, inter=128,
                                              shared_inter=160)}[variant]
     inp = make_inputs(cfg, seed=21, device=DEV)
