@@ -49,17 +49,18 @@ DEFAULT_ALSO = "decode_t64_h5120_e384,prefill_t4096_h5120_e384,skew_t16384_h5120
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    # the clock ramps over the first ~0.1 s of work: 40 warm-up steps left the one-token layer ~2 us slower
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--workload", default="decode_t1_h5120_e384")
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="comma-separated workloads timed in the same run ('' for none); each runs "
                          "min(steps, 200) timed steps after min(warmup, 20) untimed ones")
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
-    ap.add_argument("--launch", choices=["stream", "graph"], default="graph",
-                    help="timed steps as replays of HIP graphs (one per cycle over the weight sets, as a serving "
-                         "loop replays its captured step over a model's layers) or as plain launches on one HIP "
-                         "stream; the other form is timed afterwards for reference")
+    ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
+                    help="timed steps as plain launches on one HIP stream or as replays of HIP graphs (one per "
+                         "cycle over the weight sets, as a serving loop replays its captured step over a model's "
+                         "layers); the other form is timed afterwards for reference")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed forwards per weight set for kernel times")
     ap.add_argument("--cpu-sample", type=int, default=16, help="decode tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--json-out", default="")

@@ -1604,6 +1604,165 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- skinny bf16, few rows
+// The shared expert at 17-127 tokens: fp32 partial products of all M rows
+// (up to 16 MT) against 64 weight rows per block over one K range
+// (blockIdx.y of p.k_slices, in 128-wide chunks), summed and finished by
+// slice_sum_kernel.  Four waves of 16 weight rows each: the weights stream
+// from memory straight to registers, kSkPf chunks ahead, each weight byte
+// read once by one wave; the rows' chunk goes global -> registers -> LDS
+// (two stages) and all four waves read it there.  The 128-row kernels above
+// computed at least 128 rows per tile, and their 32-row form re-read the
+// weights for every row tile: 64 tokens took 52 + 28 us for 71 MB, against 28
+// + 18 us here (with the partial sums).
+constexpr int kSkPf = 4;            // weight chunks in flight per wave
+constexpr int kSkRowB = 256 + 16;   // LDS bytes per staged row: 128 bf16 + 16 (8 rows on 8 bank quads)
+template <int MT>
+__global__ __launch_bounds__(256) void skinny_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * MT * kSkRowB];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nch_all = p.K / 128;
+  const int per = (nch_all + p.k_slices - 1) / p.k_slices;
+  const int slice = (int)blockIdx.y, c_lo = slice * per;
+  const int nch = min(per, nch_all - c_lo);  // >= 1: the host makes every range non-empty
+  const int n = (int)blockIdx.x * 64 + 16 * wave + col;  // this lane's weight row (B operand column)
+
+  // weights: row n, 16 bytes at K offset 128 c + 32 s + 8 grp (s = MFMA K step)
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bh, (uint32_t)((int64_t)p.N * p.K * 2));
+  const uint32_t b_off = (uint32_t)min(n, p.N - 1) * (uint32_t)(p.K * 2) + 16u * grp;
+  u32x4_t wb[kSkPf][4];
+  // a chunk past the range reads zeros (per-lane offset kOob, which the
+  // buffer range check turns into a zero), so its MFMAs add nothing
+  auto load_w = [&](int c, u32x4_t (&d)[4]) {
+    const int cc = c_lo + min(c, nch - 1);
+    const bool in = c < nch;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      d[s] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(in ? b_off + 64u * s : kOob), 256 * cc, 0));
+  };
+  // rows: piece q = tid + 256 i (row q / 16, 16-byte part q % 16) of the chunk
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)p.a_rows * p.lda * 2));
+  uint32_t a_off[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int q = (int)threadIdx.x + 256 * i, r = q >> 4;
+    a_off[i] = (uint32_t)((int64_t)min(r, p.M - 1) * p.lda * 2) + 16u * (q & 15);
+  }
+  // two chunks of rows in registers: each load has two iterations to land
+  u32x4_t xr[2][MT];
+  auto load_x = [&](int c, u32x4_t (&d)[MT]) {
+    const int cc = c_lo + min(c, nch - 1);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      d[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)a_off[i], 256 * cc, 0));
+  };
+  auto store_x = [&](int stage, const u32x4_t (&v)[MT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int q = (int)threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4_t*>(xs[stage] + (q >> 4) * kSkRowB + 16 * (q & 15)) = v[i];
+    }
+  };
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // the rows first: loads complete in issue order, so the wait for chunk 0's
+  // rows would otherwise also wait for the weights
+  load_x(0, xr[0]);
+  load_x(1, xr[1]);
+#pragma unroll
+  for (int b = 0; b < kSkPf; ++b) load_w(b, wb[b]);
+  store_x(0, xr[0]);
+  load_x(2, xr[0]);
+  __syncthreads();
+  // iteration c: chunk c's rows are in stage c & 1, chunks c + 1 and c + 2's
+  // in registers xr[(c + 1) & 1] and xr[c & 1]; chunk c's weights in wb[c % kSkPf]
+  auto step = [&](int c, u32x4_t (&w)[4], u32x4_t (&xn)[MT]) {
+    const uint8_t* st = xs[c & 1];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + (16 * m + col) * kSkRowB + 64 * s + 16 * grp);
+        acc[m] = mfma_16x16x32(a, __builtin_bit_cast(bf16x8_t, w[s]), acc[m]);
+      }
+    }
+    // issue order pinned (loads complete in that order, and the compiler's
+    // waits count it): this step's weights, then the rows stored from the
+    // registers loaded two steps ago, then the rows for two steps ahead
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(c + kSkPf, w);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x((c + 1) & 1, xn);  // stage (c + 1) & 1 was last read in iteration c - 1
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(c + 3, xn);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+  // whole groups of kSkPf steps, those past the range on zero weights: with
+  // a guard around each step the compiler's waits would have to hold for the
+  // path that skips steps, and they drained the weight prefetch every step
+  for (int c = 0; c < nch; c += kSkPf) {
+#pragma unroll
+    for (int u = 0; u < kSkPf; ++u) step(c + u, wb[u], xr[(u + 1) & 1]);
+  }
+
+  float* out = p.Cf + (int64_t)slice * p.c_slice_stride;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * m + 4 * grp + i;
+      if (r < p.M && n < p.N) out[(int64_t)r * p.ldc + n] = acc[m][i];
+    }
+}
+
+int skinny_k_slices(int M, int n_rows, int K) {
+  if (M < 1 || M > 128 || K % 128 != 0) return 0;
+  const int blocks = (n_rows + 63) / 64, nch = K / 128;
+  // ~128 blocks of long streams (64 tokens: 2 ranges 28 + 18 us, 4 ranges 31 + 21 us; 1 range 47 + 26 us)
+  int ks = (128 + blocks - 1) / blocks;
+  ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+  if (ks > nch) ks = nch;
+  const int per = (nch + ks - 1) / ks;
+  return (nch + per - 1) / per;  // every K range non-empty
+}
+
+hipError_t launch_skinny_sliced(const GemmParams& p, bool swiglu, int k_slices, float* part, hipStream_t stream) {
+  GemmParams q = p;
+  q.N = swiglu ? 2 * p.N : p.N;  // weight rows: gate rows, then up rows (b_row_second == N)
+  q.ldc = q.N;
+  q.Cf = part;
+  q.k_slices = k_slices;
+  q.c_slice_stride = (int64_t)p.M * q.N;
+  const dim3 g((unsigned)((q.N + 63) / 64), (unsigned)k_slices);
+  const int mt = (p.M + 15) / 16;
+  if (mt <= 2)
+    hipLaunchKernelGGL(skinny_bf16_kernel<2>, g, dim3(256), 0, stream, q);
+  else if (mt <= 4)
+    hipLaunchKernelGGL(skinny_bf16_kernel<4>, g, dim3(256), 0, stream, q);
+  else if (mt <= 6)
+    hipLaunchKernelGGL(skinny_bf16_kernel<6>, g, dim3(256), 0, stream, q);
+  else
+    hipLaunchKernelGGL(skinny_bf16_kernel<8>, g, dim3(256), 0, stream, q);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t total = (int64_t)p.M * p.N;
+  const int64_t blocks = (total + 255) / 256;
+  const dim3 gs((unsigned)(blocks < 4096 ? blocks : 4096));
+  if (swiglu)
+    hipLaunchKernelGGL(slice_sum_kernel<true>, gs, dim3(256), 0, stream, part, k_slices, q.c_slice_stride, p.M, p.N,
+                       q.N, p.limit, p.C, p.ldc);
+  else
+    hipLaunchKernelGGL(slice_sum_kernel<false>, gs, dim3(256), 0, stream, part, k_slices, q.c_slice_stride, p.M,
+                       p.N, q.N, p.limit, p.C, p.ldc);
+  return hipGetLastError();
+}
+
 int dense_k_slices(int M, int n_rows, int K) {
   const int64_t blocks = (int64_t)((M + 127) / 128) * ((n_rows + 255) / 256);
   const int nch = K / 32;

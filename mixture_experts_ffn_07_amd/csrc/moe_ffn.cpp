@@ -191,6 +191,7 @@ struct WsLayout {
   bool decode = false;  // few tokens: GEMV router, fused routing, weight-streaming projections
   int bm = 16;          // rows per routed GEMM tile
   int gemm_mt = 1, shared_mt = 1;
+  bool shared_skinny = false;   // shared expert on the skinny kernel (shared_ks_* K ranges)
   // shared expert at 128..1023 tokens: the dense kernel over K slices (0: off)
   int shared_ks_gu = 0, shared_ks_dn = 0;
   int64_t max_tiles = 0, shared_tiles = 0;
@@ -277,6 +278,17 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
                  moe::down_combine_shared_supported((int)tokens, c->top_k, c->inter, c->shared_inter, fp8));
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
+  if (c->n_shared == 1 && !L.decode && tokens < 128) {
+    // the skinny weight-streaming kernel over K ranges when both K are
+    // multiples of 128 (64 tokens: 52 + 28 -> 28 + 18 us), else 32-row tiles
+    const int gu = moe::skinny_k_slices((int)tokens, 2 * c->shared_inter, c->hidden);
+    const int dn = moe::skinny_k_slices((int)tokens, c->hidden, c->shared_inter);
+    if (gu > 0 && dn > 0) {
+      L.shared_skinny = true;
+      L.shared_ks_gu = gu;
+      L.shared_ks_dn = dn;
+    }
+  }
   if (c->n_shared == 1 && !L.decode && tokens >= 128 && tokens < 1024) {
     // 16-row tiles would re-read the shared weights once per tile (320
     // tokens: 184 + 114 -> 101 + 75 us); below 128 tokens the slices are too
@@ -1004,8 +1016,9 @@ moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t*
     q.ldc = Is;
     q.limit = c->swiglu_limit;
     float* sh_part = at<float>(ws, L.sh_part);
-    err = L.shared_ks_gu ? moe::launch_dense_sliced(q, true, L.shared_ks_gu, sh_part, st)
-                         : moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
+    err = L.shared_skinny  ? moe::launch_skinny_sliced(q, true, L.shared_ks_gu, sh_part, st)
+          : L.shared_ks_gu ? moe::launch_dense_sliced(q, true, L.shared_ks_gu, sh_part, st)
+                           : moe::launch_expert_gemm(q, true, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_gate_up", st);
     if (err != hipSuccess) return fail_hip(err, "shared gate/up launch");
     q.A = hs;
@@ -1018,8 +1031,9 @@ moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t*
     q.N = H;
     q.C = y_shared;
     q.ldc = H;
-    err = L.shared_ks_dn ? moe::launch_dense_sliced(q, false, L.shared_ks_dn, sh_part, st)
-                         : moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
+    err = L.shared_skinny  ? moe::launch_skinny_sliced(q, false, L.shared_ks_dn, sh_part, st)
+          : L.shared_ks_dn ? moe::launch_dense_sliced(q, false, L.shared_ks_dn, sh_part, st)
+                           : moe::launch_expert_gemm(q, false, moe::kWBf16, L.shared_mt, L.shared_tiles, st);
     if (err == hipSuccess) err = mark(tl, "shared_down", st);
     if (err != hipSuccess) return fail_hip(err, "shared down launch");
   }
