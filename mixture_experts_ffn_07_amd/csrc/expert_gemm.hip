@@ -1605,10 +1605,10 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- skinny bf16, few rows
-// The shared expert at 17-127 tokens: fp32 partial products of all M rows
-// (up to 16 MT) against 64 weight rows per block over one K range
-// (blockIdx.y of p.k_slices, in 128-wide chunks), summed and finished by
-// slice_sum_kernel.  Four waves of 16 weight rows each: the weights stream
+// The shared expert below 512 tokens: fp32 partial products of up to 16 MT
+// rows (row group blockIdx.z) against 64 weight rows per block over one K
+// range (blockIdx.y of p.k_slices, in 128-wide chunks), summed and finished
+// by slice_sum_kernel.  Four waves of 16 weight rows each: the weights stream
 // from memory straight to registers, kSkPf chunks ahead, each weight byte
 // read once by one wave; the rows' chunk goes global -> registers -> LDS
 // (two stages) and all four waves read it there.  The 128-row kernels above
@@ -1616,6 +1616,7 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict_
 // weights for every row tile: 64 tokens took 52 + 28 us for 71 MB, against 28
 // + 18 us here (with the partial sums).
 constexpr int kSkPf = 4;            // weight chunks in flight per wave
+constexpr int kSkMaxRows = 512;     // rows in up to four groups of 128
 constexpr int kSkRowB = 256 + 16;   // LDS bytes per staged row: 128 bf16 + 16 (8 rows on 8 bank quads)
 template <int MT>
 __global__ __launch_bounds__(256) void skinny_bf16_kernel(GemmParams p) {
@@ -1627,6 +1628,7 @@ __global__ __launch_bounds__(256) void skinny_bf16_kernel(GemmParams p) {
   const int slice = (int)blockIdx.y, c_lo = slice * per;
   const int nch = min(per, nch_all - c_lo);  // >= 1: the host makes every range non-empty
   const int n = (int)blockIdx.x * 64 + 16 * wave + col;  // this lane's weight row (B operand column)
+  const int r0 = 16 * MT * (int)blockIdx.z;              // this block's row group
 
   // weights: row n, 16 bytes at K offset 128 c + 32 s + 8 grp (s = MFMA K step)
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bh, (uint32_t)((int64_t)p.N * p.K * 2));
@@ -1647,7 +1649,7 @@ __global__ __launch_bounds__(256) void skinny_bf16_kernel(GemmParams p) {
   uint32_t a_off[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int q = (int)threadIdx.x + 256 * i, r = q >> 4;
+    const int q = (int)threadIdx.x + 256 * i, r = r0 + (q >> 4);
     a_off[i] = (uint32_t)((int64_t)min(r, p.M - 1) * p.lda * 2) + 16u * (q & 15);
   }
   // two chunks of rows in registers: each load has two iterations to land
@@ -1716,14 +1718,14 @@ __global__ __launch_bounds__(256) void skinny_bf16_kernel(GemmParams p) {
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * m + 4 * grp + i;
+      const int r = r0 + 16 * m + 4 * grp + i;
       if (r < p.M && n < p.N) out[(int64_t)r * p.ldc + n] = acc[m][i];
     }
 }
 
 int skinny_k_slices(int M, int n_rows, int K) {
-  if (M < 1 || M > 128 || K % 128 != 0) return 0;
-  const int blocks = (n_rows + 63) / 64, nch = K / 128;
+  if (M < 1 || M > kSkMaxRows || K % 128 != 0) return 0;
+  const int blocks = (n_rows + 63) / 64 * ((M + 127) / 128), nch = K / 128;
   // ~128 blocks of long streams (64 tokens: 2 ranges 28 + 18 us, 4 ranges 31 + 21 us; 1 range 47 + 26 us)
   int ks = (128 + blocks - 1) / blocks;
   ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
@@ -1739,8 +1741,9 @@ hipError_t launch_skinny_sliced(const GemmParams& p, bool swiglu, int k_slices, 
   q.Cf = part;
   q.k_slices = k_slices;
   q.c_slice_stride = (int64_t)p.M * q.N;
-  const dim3 g((unsigned)((q.N + 63) / 64), (unsigned)k_slices);
-  const int mt = (p.M + 15) / 16;
+  // rows in groups of up to 128 (blockIdx.z), each re-reading the weights from the caches
+  const dim3 g((unsigned)((q.N + 63) / 64), (unsigned)k_slices, (unsigned)((p.M + 127) / 128));
+  const int mt = (p.M < 128 ? p.M + 15 : 128) / 16;
   if (mt <= 2)
     hipLaunchKernelGGL(skinny_bf16_kernel<2>, g, dim3(256), 0, stream, q);
   else if (mt <= 4)

@@ -278,7 +278,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
                  moe::down_combine_shared_supported((int)tokens, c->top_k, c->inter, c->shared_inter, fp8));
   }
   L.shared_tiles = (tokens + 16 * L.shared_mt - 1) / (16 * L.shared_mt);
-  if (c->n_shared == 1 && !L.decode && tokens < 128) {
+  if (c->n_shared == 1 && !L.decode && tokens <= 512) {
     // the skinny weight-streaming kernel over K ranges when both K are
     // multiples of 128 (64 tokens: 52 + 28 -> 28 + 18 us), else 32-row tiles
     const int gu = moe::skinny_k_slices((int)tokens, 2 * c->shared_inter, c->hidden);
@@ -289,7 +289,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
       L.shared_ks_dn = dn;
     }
   }
-  if (c->n_shared == 1 && !L.decode && tokens >= 128 && tokens < 1024) {
+  if (c->n_shared == 1 && !L.decode && !L.shared_skinny && tokens >= 128 && tokens < 1024) {
     // 16-row tiles would re-read the shared weights once per tile (320
     // tokens: 184 + 114 -> 101 + 75 us); below 128 tokens the slices are too
     // short and their partial sums cost more (64 tokens: 57 + 31 -> 89 + 62 us)

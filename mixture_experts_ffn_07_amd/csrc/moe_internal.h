@@ -119,7 +119,7 @@ hipError_t launch_dense_f32(const GemmParams& p, int slices, hipStream_t stream)
 // tokens: p.bh = the three bf16 terms of W_r [3][N][K], p.k_slices K ranges,
 // each written to partial slice Cf + r * c_slice_stride with the terms added
 int dense_router_kslices(int M, int n_experts, int K);
-// One dense bf16 matrix against at most 128 rows with K a multiple of 128:
+// One dense bf16 matrix against at most 512 rows with K a multiple of 128:
 // skinny_k_slices K ranges (0: unsupported) of fp32 partials from the
 // weight-streaming skinny kernel into `part`, then their sum as
 // launch_dense_sliced does.

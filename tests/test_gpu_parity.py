@@ -115,7 +115,8 @@ def test_permute_bit_exact(t, e, k, skew):
 @pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k",
                                      "fp8_t2", "t200_sliced_shared", "t1100_dense_shared", "t2100_whole_round_shared",
                                      "t2100_whole_round_k64", "t2048_whole_round_one_chunk", "t12_skinny_shared",
-                                     "t64_skinny_shared", "t127_skinny_shared"])
+                                     "t64_skinny_shared", "t127_skinny_shared", "t300_skinny_row_groups",
+                                     "t512_skinny_row_groups"])
 def test_expert_ffn(variant):
     """Routed slots and the shared expert against the oracle over every row.  From 2048 tokens the shared
     expert takes the whole-round dense kernel: at 2100 tokens with a ragged last row tile, 160 h columns (a
@@ -123,7 +124,8 @@ def test_expert_ffn(variant):
     chunks; with K of 6 and 3 64-wide chunks (192 h columns, 384 output columns); at 2048 tokens with K of one
     chunk and fewer columns than one block.  Below 128 tokens, with both K multiples of 128, the skinny
     weight-streaming kernel over K ranges: 12 tokens (one row tile, K ranges of one chunk), 64 tokens, 127
-    tokens (eight row tiles, the last ragged)."""
+    tokens (eight row tiles, the last ragged); up to 512 tokens in row groups of 128 (300: the last group
+    ragged; 512: four whole groups)."""
     base = CONFIGS["tiny_t8_h512_e32"]
     cfg = {"tiny": base.with_(tokens=40),
            "t200_sliced_shared": base.with_(tokens=200, shared_inter=160),
@@ -133,6 +135,8 @@ def test_expert_ffn(variant):
            "t12_skinny_shared": base.with_(tokens=12),
            "t64_skinny_shared": base.with_(tokens=64, shared_inter=384),
            "t127_skinny_shared": base.with_(tokens=127, hidden=640, shared_inter=256),
+           "t300_skinny_row_groups": base.with_(tokens=300, hidden=384, shared_inter=256),
+           "t512_skinny_row_groups": base.with_(tokens=512, shared_inter=128),
            "t2048_whole_round_one_chunk": base.with_(tokens=2048, hidden=32, inter=32, shared_inter=32, n_experts=4,
                                                      top_k=2),
            "fp8": base.with_(tokens=40, expert_format="mxfp8"),
