@@ -527,6 +527,13 @@ struct Pipe8Cfg<32> {
   static constexpr int kA = 2;
   static constexpr int kB = 3;
 };
+// SG = 1 (whole scales): the block's scale bytes, 256 rows x K / 32, go to
+// LDS once in the prologue (at most kPipeWholeS bytes), with two weight
+// stages so that two blocks still fit on a CU.  Scale groups re-fetched each
+// 128-byte scale line once per group (the weight stream evicts it in
+// between): the 32-row down projection at 64 tokens moved 1.87 GB against
+// 1.53 GB algorithmic, and went 312 -> 290 us this way (320 tokens: 500 -> 470 us).
+constexpr int kPipeWholeS = 256 * 80;
 template <int AR>
 constexpr int pipe8_pool_bytes() {
   return Pipe8Cfg<AR>::kA * AR * 256 + Pipe8Cfg<AR>::kB * (kPipeBStage + kPipeSStage);
@@ -569,14 +576,16 @@ constexpr int pipe8_wait(int la, int lb) {
 // and chunk by the K-half-0 waves.
 template <bool SWIGLU, int AR, int SG = 0>
 __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kernel(GemmParams p, int n_tiles, int col_blocks) {
-  constexpr int kSA = Pipe8Cfg<AR>::kA, kSB = Pipe8Cfg<AR>::kB;
+  constexpr bool kWhole = SG == 1;
+  constexpr int kSA = Pipe8Cfg<AR>::kA, kSB = kWhole ? 2 : Pipe8Cfg<AR>::kB;
   constexpr bool kAFirst = kSA <= kSB;
   constexpr int kAStage = AR * 256;
   constexpr int kLoadsA = AR / 32;  // activation loads per wave and chunk at full tiles
   constexpr int MTMAX = AR / 16;
-  static_assert(SG == 0 || SG == 3 || SG == 4, "scale groups of 3 or 4 chunks");
+  static_assert(SG == 0 || SG == 1 || SG == 3 || SG == 4, "scale groups of 3 or 4 chunks, or whole");
   constexpr int kSGroup = 256 * 16;
-  constexpr int kPool = kSA * kAStage + kSB * kPipeBStage + (SG ? 3 * kSGroup : kSB * kPipeSStage);
+  constexpr int kPool =
+      kSA * kAStage + kSB * kPipeBStage + (kWhole ? kPipeWholeS : SG ? 3 * kSGroup : kSB * kPipeSStage);
   static_assert(kPool >= 4 * AR * 256, "the K-half reduction reuses 4 x AR x 256 B of the stage pool");
   // one pool: activation stages, weight-code stages, scale stages (the first
   // AR KB also hold the K-half reduction at the end)
@@ -649,13 +658,13 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
   const uint8_t* s_src = bs_e + brow_col(64 * (wave & 3) + lane) * (K / 32);
   // scale groups: row 64 i + lane of part i (i = 0..3)
   const uint8_t* sg_src[4];
-  if constexpr (SG != 0) {
+  if constexpr (SG > 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sg_src[i] = bs_e + brow_col(64 * i + lane) * (K / 32);
   }
-  const int n_groups = SG ? nchunks / SG : 1;
+  const int n_groups = SG > 1 ? nchunks / SG : 1;
   // the waves that issue scale loads in the main loop (wave-uniform)
-  const bool s_issuer = SG == 4 ? wave == 0 : SG == 3 ? wave < 2 : kh == 0;
+  const bool s_issuer = SG == 4 ? wave == 0 : SG == 3 ? wave < 2 : SG == 0 ? kh == 0 : false;
 
   auto issue_a = [&](int c) {
     const int cc = min(c, nchunks - 1);
@@ -681,13 +690,14 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
       if (ii == i) {
         if constexpr (SG == 4)
           load_lds16(sg_src[ii] + 16 * gg, lds_addr(sg_lds(g) + 1024 * ii));
-        else
+        else if constexpr (SG == 3)
           load_lds12(sg_src[ii] + 12 * gg, lds_addr(sg_lds(g) + 1024 * ii));
       }
     }
   };
   auto issue_sg_iter = [&](int c) {
-    if constexpr (SG == 4) {
+    if constexpr (kWhole) {
+    } else if constexpr (SG == 4) {
       if (s_issuer) issue_sg((c >> 2) + 2, c & 3);
     } else if constexpr (SG == 3) {
       if (s_issuer) issue_sg(c / 3 + 2, (2 * (c % 3) + wave) & 3);
@@ -705,7 +715,18 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
   for (int c = 0; c < kSB - 1; ++c) issue_b(c);
 #pragma unroll
   for (int c = 0; c < kSA - 1; ++c) issue_a(c);
-  if constexpr (SG != 0) {
+  if constexpr (kWhole) {
+    // the block's weight rows are one run of consecutive rows (n0 ..), so
+    // their scale bytes are one contiguous range; a piece past the expert's
+    // rows re-reads its first piece into LDS no one reads
+    const int run_bytes = 256 * (K / 32);
+    const int64_t avail = (int64_t)(p.N - n0) * (K / 32);
+    const uint8_t* sbase = bs_e + (int64_t)n0 * (K / 32);
+    for (int q0 = 16 * 64 * wave; q0 < run_bytes; q0 += 16 * 512) {
+      const int off = q0 + 16 * lane;
+      load_lds16(sbase + (off + 16 <= avail ? off : 0), lds_addr(pool + kSA * kAStage + kSB * kPipeBStage + q0));
+    }
+  } else if constexpr (SG != 0) {
     if (wave == 0) {  // wave-uniform
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -733,8 +754,10 @@ __global__ __launch_bounds__(512, AR == 32 ? 2 : 1) void expert_gemm_pipe8_kerne
       }
       const uint8_t* al = a_lds(c % kSA);
       const uint8_t* bl = b_lds(c % kSB);
-      const uint8_t* sl = SG ? sg_lds(c / (SG ? SG : 1)) + 4 * (c % (SG ? SG : 1)) : s_lds(c % kSB);
-      constexpr int kSRow = SG ? 16 : 4;  // scale bytes per row in LDS
+      const uint8_t* sl = kWhole ? pool + kSA * kAStage + kSB * kPipeBStage + 4 * c
+                          : SG ? sg_lds(c / (SG ? SG : 1)) + 4 * (c % (SG ? SG : 1))
+                               : s_lds(c % kSB);
+      const int kSRow = kWhole ? K / 32 : SG ? 16 : 4;  // scale bytes per row in LDS
       uint32_t q[4][2];
       float sc[4];
 #pragma unroll
@@ -1443,6 +1466,7 @@ constexpr int kDenseNtStages64 = 2;
 // MXFP4 weights with K a multiple of 128 at up to this many rows per expert
 // on average: 32-row tiles for the pipelined kernel
 constexpr int kPipeSmallMt = 2;
+constexpr bool kPipeDownWholeScales = true;  // the 32-row down projection with whole scales (K <= 2560)
 constexpr int64_t kPipeSmallAvgRows = 16;
 
 int expert_gemm_mt(int64_t n_rows, int n_groups, WeightFormat fmt, bool k_pipelined) {
@@ -1535,6 +1559,8 @@ static void launch_t(const GemmParams& p, int mt, dim3 grid, hipStream_t stream)
                            col_blocks);
       else
         hipLaunchKernelGGL((expert_gemm_pipe8_kernel<true, 128>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
+    } else if (p.K / 32 * 256 <= kPipeWholeS && kPipeDownWholeScales) {
+      hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32, 1>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
     } else if (p.K % 384 == 0) {
       hipLaunchKernelGGL((expert_gemm_pipe8_kernel<false, 32, 3>), g1, dim3(512), 0, stream, p, n_tiles, col_blocks);
     } else {
