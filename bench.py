@@ -19,7 +19,9 @@ published peaks.  Kernel durations come from HIP events on the library's
 stream around every kernel.  `cpu_baseline` times the CPU oracle on a few
 tokens of the headline workload, with its weights already in host memory.
 Timed steps are plain launches on one HIP stream by default (`--launch graph`
-replays HIP graphs; the other form is timed after for reference).
+replays HIP graphs; the other form is timed after for reference).  Before
+its W warm-up steps each workload runs untimed for `--settle-s` seconds, so
+that the clock has left its idle level when the K timed steps start.
 """
 
 from __future__ import annotations
@@ -49,13 +51,15 @@ DEFAULT_ALSO = "decode_t64_h5120_e384,prefill_t4096_h5120_e384,skew_t16384_h5120
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # the clock ramps over the first ~0.1 s of work: 40 warm-up steps left the one-token layer ~2 us slower
+    # the clock ramps over the first ~0.1 s of work; --settle-s covers that, whatever the warm-up count
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_t1_h5120_e384")
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="comma-separated workloads timed in the same run ('' for none); each runs "
                          "min(steps, 200) timed steps after min(warmup, 20) untimed ones")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed seconds of steps before the warm-up steps, for the clock to reach its busy level")
     ap.add_argument("--weight-sets", type=int, default=0, help="0: enough to exceed the last-level cache")
     ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
                     help="timed steps as plain launches on one HIP stream or as replays of HIP graphs (one per "
@@ -262,7 +266,7 @@ def cpu_baseline(cfg, inp, sample: int) -> dict:
 
 
 def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: int, kernel_reps: int, dev: str,
-                 keep_inputs: bool = False) -> dict:
+                 keep_inputs: bool = False, settle_s: float = 0.0) -> dict:
     import torch
 
     import mixture_experts_ffn_07_amd as moe
@@ -334,6 +338,15 @@ def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: i
                 i += 1
 
     use_graph = launch == "graph"
+    # clock settle: the chip's clock ramps up over the first ~0.1 s of steady work after idle, so the step
+    # runs untimed for a fixed wall time before the W warm-up steps, as it would in a serving loop that is
+    # already busy (a handful of warm-up steps alone still measures the ramp)
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle_s:
+        run(sets * 8, graph=use_graph)
+        settle_steps += sets * 8
+        torch.cuda.synchronize()
     run(warmup, graph=use_graph)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -372,7 +385,7 @@ def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: i
                            mx6="mx6_x" in kernel_ms)
     out = {
         "workload": cfg.name, "tokens": t, "ms_per_step": ms_per_step, "tokens_per_s": t / (ms_per_step * 1e-3),
-        "steps": steps, "warmup": warmup,
+        "steps": steps, "warmup": warmup, "clock_settle": {"seconds": settle_s, "steps": settle_steps},
         "config": {"workload": cfg.name, "tokens": t, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
                    "expert_weights": ("mxfp8 (e4m3 + e8m0 per 32)" if cfg.expert_format == "mxfp8"
@@ -415,7 +428,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     head = run_workload(args.workload, args.steps, args.warmup, args.launch, args.weight_sets, args.kernel_reps, dev,
-                        keep_inputs=args.cpu_sample > 0)
+                        keep_inputs=args.cpu_sample > 0, settle_s=args.settle_s)
     print(f"# {head['workload']}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     head_inputs = head.pop("_inputs", None)
     others = []
@@ -423,7 +436,7 @@ def main():
         if name not in CONFIGS:
             raise SystemExit(f"unknown workload {name}")
         r = run_workload(name, min(args.steps, 200), min(args.warmup, 20), args.launch, args.weight_sets,
-                         min(args.kernel_reps, 3), dev)
+                         min(args.kernel_reps, 3), dev, settle_s=args.settle_s)
         print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         others.append(r)
 
@@ -435,6 +448,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": head["clock_settle"],
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
