@@ -43,11 +43,23 @@ namespace {
 // 4 block scales of the chunk (byte g for lane group g).  Two batches are in
 // flight per wave.
 constexpr int kMxChunks = 4;  // a multiple of 4
-template <int NB>
+// W8: MXFP8 weights, 32 E4M3 codes per lane and chunk in two 16-byte pieces
+// (q: K offsets [16 g, 16 g + 16) of the chunk, q2: [64 + 16 g, 80 + 16 g),
+// the matrix instruction's 8-bit operand layout, as for the A rows)
+template <int NB, bool W8 = false>
 struct MxBatch {
   u32x4_t q[kMxChunks][NB];
+  u32x4_t q2[W8 ? kMxChunks : 1][NB];
   uint32_t s[kMxChunks][NB];
 };
+
+// D += A(16x128, E4M3, E8M0 per 32) * B(128x16, E4M3, E8M0 per 32), fp32:
+// the MXFP8-weight form of mfma_mx (B in the 8-bit layout of A).
+__device__ __forceinline__ f32x4_t mfma_mx8(const i32x8_t& a, const u32x4_t& b0, const u32x4_t& b1, int sa, int sb,
+                                            f32x4_t c) {
+  const i32x8_t bw = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 0, 0, 0, sa, 0, sb);
+}
 
 struct MxView {
   __amdgpu_buffer_rsrc_t q, s;
@@ -60,16 +72,23 @@ struct MxView {
 // wider loads bring the scales of 4, 2 or 1 chunks for all 4 lane groups
 // at once; the row offsets are then multiples of the load width.  SW = 0:
 // the block staged all its rows' scales in LDS once (no scale loads here).
-template <int NB, int SW>
-__device__ __forceinline__ void mx_load(MxBatch<NB>& b, const MxView& v, int c0, int grp) {
+template <int NB, int SW, bool W8 = false>
+__device__ __forceinline__ void mx_load(MxBatch<NB, W8>& b, const MxView& v, int c0, int grp) {
 #pragma unroll
   for (int u = 0; u < kMxChunks; ++u) {
     const int c = c0 + u;
     const bool ok = c < v.nchunks && c * 128 + grp * 32 < v.K;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t qo = ok ? v.qrow[nb] + (uint32_t)(c * 64 + grp * 16) : kOob;
-      b.q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(v.q, (int)qo, 0, 0));
+      if constexpr (W8) {
+        const uint32_t qo = ok ? v.qrow[nb] + (uint32_t)(c * 128 + grp * 16) : kOob;
+        const uint32_t qo2 = ok ? qo + 64u : kOob;
+        b.q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(v.q, (int)qo, 0, 0));
+        b.q2[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(v.q, (int)qo2, 0, 0));
+      } else {
+        const uint32_t qo = ok ? v.qrow[nb] + (uint32_t)(c * 64 + grp * 16) : kOob;
+        b.q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(v.q, (int)qo, 0, 0));
+      }
     }
   }
 #pragma unroll
@@ -116,8 +135,8 @@ __device__ __forceinline__ void mx_load(MxBatch<NB>& b, const MxView& v, int c0,
 // Two block-scaled MFMAs (hi and lo activation terms) per chunk and row set.
 // `row` is this lane's staged MX row (tile row `col`), r_ok = col < rows.
 // srow_lds: this lane's row scales in LDS (SW = 0), per NB at stride sl_stride.
-template <int NB, int SW>
-__device__ __forceinline__ void mx_mma(const MxBatch<NB>& b, f32x4_t (&acc)[NB], const uint8_t* row, bool r_ok,
+template <int NB, int SW, bool W8 = false>
+__device__ __forceinline__ void mx_mma(const MxBatch<NB, W8>& b, f32x4_t (&acc)[NB], const uint8_t* row, bool r_ok,
                                        int c0, const MxView& v, int grp, const uint8_t* srow_lds, int sl_stride) {
   const int K = v.K;
 #pragma unroll
@@ -138,8 +157,13 @@ __device__ __forceinline__ void mx_mma(const MxBatch<NB>& b, f32x4_t (&acc)[NB],
     for (int nb = 0; nb < NB; ++nb) {
       const int sb = SW == 0 ? (int)srow_lds[nb * sl_stride + kb / 32 + grp]
                              : (int)((b.s[u][nb] >> (8 * grp)) & 0xffu);
-      acc[nb] = mfma_mx(ahi, b.q[u][nb], sa, sb, acc[nb]);
-      acc[nb] = mfma_mx(alo, b.q[u][nb], sa, sb, acc[nb]);
+      if constexpr (W8) {
+        acc[nb] = mfma_mx8(ahi, b.q[u][nb], b.q2[u][nb], sa, sb, acc[nb]);
+        acc[nb] = mfma_mx8(alo, b.q[u][nb], b.q2[u][nb], sa, sb, acc[nb]);
+      } else {
+        acc[nb] = mfma_mx(ahi, b.q[u][nb], sa, sb, acc[nb]);
+        acc[nb] = mfma_mx(alo, b.q[u][nb], sa, sb, acc[nb]);
+      }
     }
   }
 }
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(256) void expert_gemv_bf16_kernel(GemvParams prm) {
 // staged rows are in LDS by the time the first weights arrive.
 // AMX: the activation rows come pre-converted (p.amx), else bf16 rows (p.A)
 // are converted while staging.
-template <int NB, int SW, bool AMX>
+template <int NB, int SW, bool AMX, bool W8 = false>
 __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int rows_cap, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -274,7 +298,8 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
   MxView v;
   v.K = K;
   v.nchunks = (K + 127) / 128;
-  const uint32_t qbytes = (uint32_t)(p.b_expert_rows * (K / 2));
+  const int row_q = W8 ? K : K / 2;  // code bytes per weight row
+  const uint32_t qbytes = (uint32_t)(p.b_expert_rows * row_q);
   const uint32_t sbytes = (uint32_t)(p.b_expert_rows * (K / 32));
   v.q = make_rsrc(p.bq + (int64_t)e * qbytes, qbytes);
   v.s = make_rsrc(p.bs + (int64_t)e * sbytes, sbytes);
@@ -282,7 +307,7 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const uint32_t r = (uint32_t)(n0 + col + nb * p.b_row_second);
-    v.qrow[nb] = n_ok ? r * (uint32_t)(K / 2) : kOob;
+    v.qrow[nb] = n_ok ? r * (uint32_t)row_q : kOob;
     v.srow[nb] = n_ok ? r * (uint32_t)(K / 32) : kOob;
   }
 
@@ -307,9 +332,9 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  MxBatch<NB> b0, b1;
-  mx_load<NB, SW>(b0, v, 0, grp);
-  mx_load<NB, SW>(b1, v, kMxChunks, grp);
+  MxBatch<NB, W8> b0, b1;
+  mx_load<NB, SW, W8>(b0, v, 0, grp);
+  mx_load<NB, SW, W8>(b1, v, kMxChunks, grp);
   __builtin_amdgcn_sched_barrier(0);
   mx_row_commit<AMX>(p, 0, 0, st, lds);
   if constexpr (SW == 0) {
@@ -339,11 +364,11 @@ __global__ __launch_bounds__(256) void expert_gemv_mx_kernel(GemvProblem p, int 
   const uint8_t* srow_lds = lds + a_bytes + (wave * 16 + col) * (K / 32);
   constexpr int CB = kMxChunks;
   for (int c = 0; c < v.nchunks; c += 2 * CB) {
-    mx_mma<NB, SW>(b0, acc, row, r_ok, c, v, grp, srow_lds, sl_stride);
+    mx_mma<NB, SW, W8>(b0, acc, row, r_ok, c, v, grp, srow_lds, sl_stride);
     if (c + CB >= v.nchunks) break;
-    mx_load<NB, SW>(b0, v, c + 2 * CB, grp);
-    mx_mma<NB, SW>(b1, acc, row, r_ok, c + CB, v, grp, srow_lds, sl_stride);
-    mx_load<NB, SW>(b1, v, c + 3 * CB, grp);
+    mx_load<NB, SW, W8>(b0, v, c + 2 * CB, grp);
+    mx_mma<NB, SW, W8>(b1, acc, row, r_ok, c + CB, v, grp, srow_lds, sl_stride);
+    mx_load<NB, SW, W8>(b1, v, c + 3 * CB, grp);
   }
   if (NB == 2 && p.cmx) {
     // two-term MXFP8 output rows (stride mx_row_bytes(N)): the block's 64
@@ -393,7 +418,7 @@ __device__ __forceinline__ int splitk_waves(int K) {
 
 __device__ __forceinline__ size_t splitk_scale_bytes(int nb, int K) { return (size_t)nb * 16 * (K / 32); }
 
-template <int NB, int CPW, bool AMX>
+template <int NB, int CPW, bool AMX, bool W8 = false>
 __global__ __launch_bounds__(512) void expert_gemv_splitk_kernel(GemvProblem p, int rows_cap, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
@@ -441,7 +466,8 @@ __global__ __launch_bounds__(512) void expert_gemv_splitk_kernel(GemvProblem p, 
   const int s_bytes = (int)splitk_scale_bytes(NB, K);
   uint8_t* s_lds = lds + a_bytes;                                   // [NB][16 rows][ks]
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + a_bytes + ((s_bytes + 15) & ~15));  // [W-1][NB][64]
-  const uint32_t qbytes = (uint32_t)(p.b_expert_rows * (K / 2));
+  const int row_q = W8 ? K : K / 2;  // code bytes per weight row
+  const uint32_t qbytes = (uint32_t)(p.b_expert_rows * row_q);
   const uint32_t sbytes = (uint32_t)(p.b_expert_rows * ks);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, qbytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bs + (int64_t)e * sbytes, sbytes);
@@ -491,15 +517,23 @@ __global__ __launch_bounds__(512) void expert_gemv_splitk_kernel(GemvProblem p, 
   // this wave's weights: chunks [c_begin, c_begin + CPW)
   const int c_begin = wave * CPW;
   u32x4_t q[CPW][NB];
+  u32x4_t q2[W8 ? CPW : 1][NB];  // MXFP8: the second 16-byte piece of each lane's codes
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     const int c = c_begin + u;
     const bool ok = c < nchunks && c * 128 + grp * 32 < K;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t qo = ok ? (uint32_t)(n0 + col + nb * p.b_row_second) * (uint32_t)(K / 2) + (uint32_t)(c * 64 + grp * 16)
-                             : kOob;
-      q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
+      const uint32_t rb = (uint32_t)(n0 + col + nb * p.b_row_second) * (uint32_t)row_q;
+      if constexpr (W8) {
+        const uint32_t qo = ok ? rb + (uint32_t)(c * 128 + grp * 16) : kOob;
+        const uint32_t qo2 = ok ? qo + 64u : kOob;
+        q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
+        q2[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo2, 0, 0));
+      } else {
+        const uint32_t qo = ok ? rb + (uint32_t)(c * 64 + grp * 16) : kOob;
+        q[u][nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qo, 0, 0));
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -544,8 +578,13 @@ __global__ __launch_bounds__(512) void expert_gemv_splitk_kernel(GemvProblem p, 
     for (int nb = 0; nb < NB; ++nb) {
       const bool sok = kb + 32 * grp < K;
       const int sb = sok ? (int)s_lds[(nb * 16 + col) * ks + kb / 32 + grp] : 127;
-      acc[nb] = mfma_mx(ahi, q[u][nb], sa, sb, acc[nb]);
-      acc[nb] = mfma_mx(alo, q[u][nb], sa, sb, acc[nb]);
+      if constexpr (W8) {
+        acc[nb] = mfma_mx8(ahi, q[u][nb], q2[u][nb], sa, sb, acc[nb]);
+        acc[nb] = mfma_mx8(alo, q[u][nb], q2[u][nb], sa, sb, acc[nb]);
+      } else {
+        acc[nb] = mfma_mx(ahi, q[u][nb], sa, sb, acc[nb]);
+        acc[nb] = mfma_mx(alo, q[u][nb], sa, sb, acc[nb]);
+      }
     }
   }
   const int nwaves = nthreads >> 6;
@@ -586,6 +625,19 @@ hipError_t launch_mx(const GemvProblem& p, int rows_cap, float limit, hipStream_
   const dim3 grid((unsigned)(p.grid_tiles * ((p.N + 63) / 64)));
   const size_t shm = gemv_lds_bytes(rows_cap, p.K, true);
   const size_t shm_s = shm + mx_scale_lds_bytes(NB, p.K);
+  if (p.w8) {
+    // MXFP8 weights: K a multiple of 128 (whole 32-code pieces per lane); the
+    // MXFP8 output rows (cmx) exist for the MXFP4 form only
+    if (p.K % 128 != 0 || p.cmx) return hipErrorInvalidValue;
+    if (p.K <= 5120 && shm_s <= kMxMaxLds)
+      hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 0, AMX, true>), grid, dim3(256), shm_s, stream, p, rows_cap,
+                         limit);
+    else if (p.K % 512 == 0)
+      hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 16, AMX, true>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+    else
+      hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 4, AMX, true>), grid, dim3(256), shm, stream, p, rows_cap, limit);
+    return hipGetLastError();
+  }
   if (p.K <= 5120 && p.K % 128 == 0 && shm_s <= kMxMaxLds)
     hipLaunchKernelGGL((expert_gemv_mx_kernel<NB, 0, AMX>), grid, dim3(256), shm_s, stream, p, rows_cap, limit);
   else if (p.K % 512 == 0)
@@ -605,8 +657,14 @@ hipError_t launch_splitk(const GemvProblem& p, int rows_cap, float limit, hipStr
   const dim3 grid((unsigned)(p.grid_tiles * (p.N / 16)));
   const size_t s_bytes = ((size_t)NB * 16 * (p.K / 32) + 15) & ~size_t(15);
   const size_t shm = gemv_lds_bytes(rows_cap, p.K, true) + s_bytes + (size_t)(waves - 1) * NB * 64 * 16;
-  hipLaunchKernelGGL((expert_gemv_splitk_kernel<NB, CPW, AMX>), grid, dim3(64 * waves), shm, stream, p, rows_cap,
-                     limit);
+  if (p.w8) {
+    if (p.K % 128 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((expert_gemv_splitk_kernel<NB, CPW, AMX, true>), grid, dim3(64 * waves), shm, stream, p,
+                       rows_cap, limit);
+  } else {
+    hipLaunchKernelGGL((expert_gemv_splitk_kernel<NB, CPW, AMX>), grid, dim3(64 * waves), shm, stream, p, rows_cap,
+                       limit);
+  }
   return hipGetLastError();
 }
 

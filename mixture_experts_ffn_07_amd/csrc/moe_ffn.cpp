@@ -234,7 +234,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     // the split-K down projection plus a separate combine measured faster than
     // the fused down+combine kernel (11.8 + 4.1 us against 19.8 us at T = 1)
     L.splitk_dn = moe::splitk_supported((int)tokens, c->inter);
-    L.down_combine = L.down_combine && !L.splitk_dn;
+    L.down_combine = L.down_combine && !L.splitk_dn && !fp8;  // its kernel reads MXFP4 weights
     L.valu_dn = L.route_small && moe::down_valu_supported((int)tokens, c->top_k, c->inter, fp8);
     L.router.ksplit = 1;  // full logits from the GEMV router
     L.router.dense_kslices = 0;
@@ -337,9 +337,11 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
 
 WsLayout plan_workspace(const moe_config* c, int64_t tokens) {
   WsLayout L = plan_workspace_impl(c, tokens, true);
-  // MXFP8 weights have few-token kernels only in the one/two-token streaming
-  // form; other token counts take the general launch sequence
-  if (L.fmt == moe::kWMxfp8 && L.decode && !L.stream4) L = plan_workspace_impl(c, tokens, false);
+  // MXFP8 weights outside the one/two-token streaming form take the
+  // few-token MFMA kernels when both K are multiples of 128 (whole 32-code
+  // pieces per lane), else the general launch sequence
+  if (L.fmt == moe::kWMxfp8 && L.decode && !L.stream4 && (c->hidden % 128 != 0 || c->inter % 128 != 0))
+    L = plan_workspace_impl(c, tokens, false);
   return L;
 }
 
@@ -395,6 +397,7 @@ moe::GemvParams routed_gemv(const moe_config* c, const moe_weights* w, const uin
   g.rows_cap = (int)T;
   g.limit = c->swiglu_limit;
   moe::GemvProblem& r = g.p[0];
+  r.w8 = L.fmt == moe::kWMxfp8;
   r.tiles = at<moe::GemmTile>(ws, L.tiles);
   r.tile_count = at<int32_t>(ws, L.tile_count);
   r.grid_tiles = (int)L.max_tiles;
@@ -811,6 +814,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     g.hidden = c->hidden;
     g.inter = c->inter;
     g.limit = c->swiglu_limit;
+    g.fp8 = L.fmt == moe::kWMxfp8;
     err = moe::launch_gate_up_valu(g, (int)L.max_tiles, st);
   } else {
     if (L.down_combine) gu.p[0].cmx = at<uint8_t>(ws, L.hmx);  // h in MXFP8 form for the down step
@@ -833,6 +837,7 @@ moe_status layer_forward_decode(const moe_config* c, const moe_weights* w, const
     dv.top_k = c->top_k;
     dv.hidden = c->hidden;
     dv.inter = c->inter;
+    dv.fp8 = L.fmt == moe::kWMxfp8;
     err = moe::launch_down_combine_valu(dv, st);
     if (err == hipSuccess) err = mark(tl, "routed_down_combine", st);
     if (err != hipSuccess) return fail_hip(err, "down/combine launch");
@@ -885,8 +890,10 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
                        hipStream_t st, Timeline* tl) {
   const int H = c->hidden, I = c->inter;
   uint16_t* h = at<uint16_t>(ws, L.h);
-  // few-token expert kernels exist for MXFP4 weights; MXFP8 ones take the grouped GEMM
-  if (L.decode && L.fmt == moe::kWMxfp4) return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
+  // few tokens: the MFMA GEMVs (MXFP4; MXFP8 with both K multiples of 128, as
+  // their 8-bit weight pieces need; other MXFP8 shapes take the grouped GEMM)
+  if (L.decode && (L.fmt == moe::kWMxfp4 || (H % 128 == 0 && I % 128 == 0)))
+    return run_experts_decode(c, w, x, T, sorted, y_slot, y_shared, ws, L, st, tl);
   // every grouped kernel below computes up to 16 * gemm_mt rows of a tile
   // (the MXFP6 one up to mx6_tile_rows()): a taller tile table would leave rows out
   if (L.bm > 16 * L.gemm_mt || (L.mx6 && L.bm > moe::mx6_tile_rows()))

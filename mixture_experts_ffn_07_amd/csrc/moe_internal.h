@@ -150,6 +150,7 @@ struct GemvProblem {
   int K;
   const uint8_t* bq;           // MXFP4 codes (NULL: bf16 weights in bh)
   const uint8_t* bs;
+  int w8;                      // bq holds MXFP8 codes (E4M3, one a byte; K a multiple of 128)
   const uint16_t* bh;
   int64_t b_expert_rows;
   int b_row_second;
@@ -167,12 +168,13 @@ struct GemvParams {
 };
 size_t gemv_lds_bytes(int rows_cap, int k_max, bool fp4);
 // fp4: one MXFP4 problem (p[0]; tiles of at most rows_cap <= 8 rows, grid over
-// 64-column blocks).  Otherwise up to two dense bf16 problems (bh).
+// 64-column blocks), or MXFP8 with p[0].w8 (K a multiple of 128, no cmx).
+// Otherwise up to two dense bf16 problems (bh).
 hipError_t launch_expert_gemv(const GemvParams& prm, bool swiglu, bool fp4, hipStream_t stream);
 
-// MXFP4 few-token down projection, split-K form: one block per (tile, 16
-// output columns), its waves splitting K into ranges of kSplitKChunksDown
-// 128-wide chunks.  Problem as for launch_expert_gemv with fp4.
+// MXFP4 (or, with w8, MXFP8) few-token down projection, split-K form: one
+// block per (tile, 16 output columns), its waves splitting K into ranges of
+// kSplitKChunksDown 128-wide chunks.  Problem as for launch_expert_gemv with fp4.
 constexpr int kSplitKChunksDown = 5;
 bool splitk_supported(int rows_cap, int K);
 hipError_t launch_expert_gemv_splitk(const GemvProblem& p, int rows_cap, hipStream_t stream);

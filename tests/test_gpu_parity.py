@@ -113,7 +113,7 @@ def test_permute_bit_exact(t, e, k, skew):
 
 
 @pytest.mark.parametrize("variant", ["tiny", "decode_t3", "ragged_k", "no_shared", "min_dims", "fp8", "fp8_ragged_k",
-                                     "fp8_t2", "t200_sliced_shared", "t1100_dense_shared", "t2100_whole_round_shared",
+                                     "fp8_t2", "fp8_t5", "fp8_t8", "t200_sliced_shared", "t1100_dense_shared", "t2100_whole_round_shared",
                                      "t2100_whole_round_k64", "t2048_whole_round_one_chunk", "t12_skinny_shared",
                                      "t64_skinny_shared", "t127_skinny_shared", "t300_skinny_row_groups",
                                      "t512_skinny_row_groups"])
@@ -141,6 +141,8 @@ def test_expert_ffn(variant):
                                                      top_k=2),
            "fp8": base.with_(tokens=40, expert_format="mxfp8"),
            "fp8_t2": base.with_(tokens=2, expert_format="mxfp8"),
+           "fp8_t5": base.with_(tokens=5, expert_format="mxfp8"),
+           "fp8_t8": base.with_(tokens=8, hidden=640, inter=384, expert_format="mxfp8"),
            "fp8_ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224, expert_format="mxfp8"),
            "decode_t3": base.with_(tokens=3),
            "ragged_k": base.with_(tokens=24, hidden=160, inter=96, shared_inter=224),
@@ -548,6 +550,24 @@ def test_layer_fp8_decode_t1_full():
     names = [n for n, _ in moe.moe_layer_forward_timed(cfg, moe.weights_from(inp), inp.x, 1, y,
                                                        moe.workspace(cfg, 1, device=DEV))]
     assert names == ["router_scores_shared_gate_up", "route_gate_up_shared_down", "routed_down_combine"]
+
+
+@pytest.mark.parametrize("tokens", [2, 3, 5, 6])
+def test_layer_fp8_few_tokens_full(tokens):
+    """MXFP8 experts at 2-6 tokens at full size take the few-token MFMA kernels (E4M3 weights fed to the
+    block-scaled instruction as its 8-bit operand, two-term MXFP8 x; the split-K down projection), not the
+    grouped GEMM; every token against the oracle.  Two tokens: the vector-ALU gate/up with the MFMA down
+    projection (the streaming down kernel holds at most 14 E4M3 vectors per lane).  From 7 tokens the staged
+    x rows of H = 5120 pass the few-token kernels' 64 KB of LDS and both formats take the grouped GEMM."""
+    cfg = CONFIGS["decode_t1_h5120_e384_fp8"].with_(tokens=tokens)
+    inp = make_inputs(cfg, seed=100 + tokens, device=DEV)
+    stats, _, alt = _check_layer(inp)
+    print(f"fp8 T={tokens} full:", stats, "near-tie alternatives", len(alt))
+    c = moe.config_from(cfg)
+    y = torch.empty((tokens, cfg.hidden), dtype=torch.int16, device=DEV)
+    names = [n for n, _ in moe.moe_layer_forward_timed(c, moe.weights_from(inp), inp.x, tokens, y,
+                                                       moe.workspace(c, tokens, device=DEV))]
+    assert names == ["router_shared_gate_up", "route_shared_down", "routed_gate_up", "routed_down", "combine"], names
 
 
 def test_layer_fp8_prefill_sampled():
