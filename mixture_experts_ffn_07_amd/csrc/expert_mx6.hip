@@ -217,6 +217,59 @@ constexpr int kMx6SPieces = kMx6SBytes / 16 / 256;           // 16-byte scale pi
 constexpr int kMx6ABufs = 4;                                // activation register buffers (chunks in flight)
 constexpr int kMx6Unroll = 4;                               // steps per loop iteration
 
+// Gate/up epilogue writing h as two-term MXFP6 records (the down
+// projection's A operand) instead of bf16 rows: the block's 256 h columns are
+// two 128-wide chunks of every row.  The bf16 values go to LDS as units of
+// one row and chunk (stride kMx6ConvIn), each thread converts one unit
+// exactly as mx6_rows_kernel converts bf16 rows, and the records leave
+// through LDS as whole 16-byte pieces (a row's two records are adjacent in
+// memory).  The LDS of the main loop is free: its last step ended at a
+// barrier after every read.
+template <int MT>
+__device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p, const f32x4_t (&acc)[MT][kMx6WaveTiles],
+                                                     uint8_t* stage, uint8_t* sall, int m_begin, int rows, int n0) {
+  constexpr int JW = kMx6WaveTiles;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  static_assert(2 * kMx6Rows * kMx6ConvIn <= kMx6SBytes && 2 * kMx6Rows * kMx6Rec <= 2 * kMx6Stage,
+                "the epilogue's units fit the main loop's LDS");
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * m + 4 * g + i;  // rows past the tile are converted but never stored
+#pragma unroll
+      for (int j = 0; j < JW / 2; ++j) {
+        const int c = (kMx6WaveRows / 2) * wave + 16 * j + n;  // block column, 0..255
+        *reinterpret_cast<uint16_t*>(sall + (2 * r + (c >> 7)) * kMx6ConvIn + 2 * (c & 127)) =
+            f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + JW / 2][i], p.limit));
+      }
+    }
+  __syncthreads();
+  const int t = (int)threadIdx.x;
+  if (t < 2 * 16 * MT) {
+    u32x4_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(sall + t * kMx6ConvIn + 16 * i);
+    uint32_t rec[52];
+    mx6_convert_unit(v, rec);
+#pragma unroll
+    for (int i = 0; i < 13; ++i)
+      *reinterpret_cast<u32x4_t*>(stage + t * kMx6Rec + 16 * i) =
+          u32x4_t{rec[4 * i], rec[4 * i + 1], rec[4 * i + 2], rec[4 * i + 3]};
+  }
+  __syncthreads();
+  // row r's two records: pieces [26 r, 26 r + 26) of the stage, to
+  // Cmx + row * ldcmx + (n0 / 128) * kMx6Rec; a chunk at or past N is not stored
+  constexpr int kRowPieces = 2 * kMx6Rec / 16;
+  for (int q = t; q < rows * kRowPieces; q += 256) {
+    const int r = q / kRowPieces, k = q - r * kRowPieces;
+    if (n0 + 128 * (k / (kMx6Rec / 16)) >= p.N) continue;
+    *reinterpret_cast<u32x4_t*>(p.Cmx + (int64_t)(m_begin + r) * p.ldcmx + (int64_t)(n0 / 128) * kMx6Rec + 16 * k) =
+        *reinterpret_cast<const u32x4_t*>(stage + 16 * q);
+  }
+}
+
 template <bool SWIGLU, int MT>
 __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sall, int e, int m_begin,
                                          int rows, int n0) {
@@ -412,6 +465,12 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   }
 
   // epilogue: lane 16 g + n holds rows 4 g + i of each row tile, column n of each column tile
+  if constexpr (SWIGLU) {
+    if (p.Cmx) {
+      mx6_epilogue_records<MT>(p, acc, stage, sall, m_begin, rows, n0);
+      return;
+    }
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll

@@ -250,11 +250,14 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     // tiles of that height; 32-row tiles stay, since the down projection's
     // 32-row kernel, which shares the tile table, computes 32 rows per tile
     if (L.mx6 && L.bm > moe::mx6_tile_rows()) L.bm = moe::mx6_tile_rows();
-    // the down projection (K = I, 18 chunks at I = 2304) measured slower on
-    // it than on the 512-row bf16 kernel, counting the pass that writes h as
-    // MXFP6 (4096 tokens: 838 + 94 us against 813 us; 16384 tokens: 1253 +
-    // 178 against 1133 us), so it keeps bf16 h and the wide kernel
-    L.mx6_dn = false;
+    // the down projection (K = I, 18 chunks at I = 2304) takes it too when
+    // the tiles are its own height (experts averaging more than 16 rows), h
+    // then leaving the gate/up epilogue as MXFP6 records.  With a pass of its
+    // own writing the records (4096 tokens 710 + 55 us against 768 us on the
+    // 512-row bf16 kernel; 16384 tokens 1099 + 97 against 1106) the layer
+    // gained 1.7% and 0.3%.  With 32-row tiles (64 and 320 tokens) the
+    // 32-row bf16 kernel is faster (64 tokens: 300 against 284 us)
+    L.mx6_dn = L.mx6 && L.bm == moe::mx6_tile_rows();
   }
   L.max_tiles = moe::max_gemm_tiles(n, E, L.bm);
   {
@@ -322,7 +325,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
   take(L.slot_pos, sizeof(int32_t) * n);
   take(L.xq, L.mx6 ? (size_t)moe::mx6_bytes(tokens, c->hidden) : 0);
   take(L.hq, L.mx6_dn ? (size_t)moe::mx6_bytes(n, c->inter) : 0);
-  take(L.h, sizeof(uint16_t) * n * c->inter);
+  take(L.h, L.mx6_dn ? 0 : sizeof(uint16_t) * n * c->inter);  // MXFP6 down: h only as records (hq)
   take(L.y_slot, sizeof(uint16_t) * n * c->hidden);
   const int64_t is = c->n_shared ? c->shared_inter : 0;
   take(L.h_sh, sizeof(uint16_t) * tokens * is);
@@ -923,15 +926,16 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     q.N = I;
     q.C = h;
     q.ldc = I;
+    // with the MXFP6 down projection the epilogue writes h as its records
+    q.Cmx = L.mx6_dn ? hq : nullptr;
+    q.ldcmx = moe::mx6_bytes(1, I);
     q.limit = c->swiglu_limit;
     err = moe::launch_expert_mx6(q, true, (int)L.max_tiles, st);
     if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
     if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
     if (!L.mx6_dn) return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl);
-    err = moe::launch_mx6_rows(h, I, n, I, hq, st);
-    if (err == hipSuccess) err = mark(tl, "mx6_h", st);
-    if (err != hipSuccess) return fail_hip(err, "h to MXFP6 launch");
     // down: A = h records in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
+    q.Cmx = nullptr;
     q.gather = nullptr;
     q.A = hq;
     q.a_stride = moe::mx6_bytes(1, I);

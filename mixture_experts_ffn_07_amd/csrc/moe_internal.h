@@ -360,6 +360,8 @@ struct Mx6Params {
   int N;                       // output columns (h columns for gate/up)
   uint16_t* C;                 // bf16 [.][ldc], row = position p
   int64_t ldc;
+  uint8_t* Cmx;                // gate/up: h as two-term MXFP6 records instead of C (row stride ldcmx bytes)
+  int64_t ldcmx;
   float limit;
 };
 // hidden and inter multiples of 128, at most 5120 (the scales of a block's weight rows fit its LDS)

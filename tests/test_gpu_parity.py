@@ -305,6 +305,21 @@ def test_layer_many_rows_per_expert(variant):
     print(f"{variant}:", stats, "near-tie alternatives", len(alt))
 
 
+@pytest.mark.parametrize("tokens,inter,experts", [(1500, 384, 8), (700, 256, 8), (2000, 640, 16)])
+def test_layer_mx6_down_records(tokens, inter, experts):
+    """96-row tiles: the gate/up epilogue writes h as two-term MXFP6 records for the MXFP6 down projection.
+    Inter 384 and 640: the last 256-column block holds one valid 128-wide chunk of the two; ragged last row
+    tiles; every row against the oracle."""
+    cfg = CONFIGS["tiny_t8_h512_e32"].with_(tokens=tokens, n_experts=experts, hidden=384, inter=inter,
+                                            shared_inter=128)
+    inp = make_inputs(cfg, seed=41, device=DEV)
+    gpu = gpu_layer(inp)
+    load = np.bincount(gpu[1].cpu().numpy().reshape(-1), minlength=cfg.n_experts)
+    assert load.sum() / max(1, np.count_nonzero(load)) > 16  # the 96-row tile table
+    stats, _, alt = _check_layer(inp, gpu=gpu)
+    print(f"mx6 down records T={tokens} I={inter}:", stats, "near-tie alternatives", len(alt))
+
+
 @pytest.mark.parametrize("variant", ["hot_expert", "one_chunk", "two_rows_per_expert"])
 def test_layer_small_tiles(variant):
     """32-row tiles of the pipelined grouped GEMM (K a multiple of 128, at most 16 rows per expert on average):
