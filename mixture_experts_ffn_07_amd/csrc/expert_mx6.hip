@@ -201,6 +201,16 @@ __device__ __forceinline__ f32x4_t mfma_f6f4(const i32x8_t& a, const u32x4_t& b,
                    : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 4, 1, sa_word, 0, sb);
 }
 
+// A: FP6 E2M3 (format 2), B: FP8 E4M3 (format 0), 32 codes per lane in the
+// instruction's 8-bit operand layout (b0: K offsets [16 g, 16 g + 16) of the
+// chunk, b1: [64 + 16 g, 80 + 16 g)); runs at the FP8 rate.
+__device__ __forceinline__ f32x4_t mfma_f6f8(const i32x8_t& a, const u32x4_t& b0, const u32x4_t& b1, int sa_word,
+                                             int sb, f32x4_t c, int term) {
+  const i32x8_t bw = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return term == 0 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 0, 0, sa_word, 0, sb)
+                   : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 2, 0, 1, sa_word, 0, sb);
+}
+
 // The block's weight scale bytes (K / 32 per weight row) go to LDS whole,
 // once, in the block's prologue: the weight rows of a block are one or two
 // runs of consecutive matrix rows, so their scales are one or two contiguous
@@ -208,12 +218,21 @@ __device__ __forceinline__ f32x4_t mfma_f6f4(const i32x8_t& a, const u32x4_t& b,
 // line per row and chunk and measured 35% of the kernel's time; groups of a
 // few chunks per row re-fetched each scale line once per group, because the
 // weight stream evicts it from L2 in between.)
-constexpr int kMx6WaveTiles = 8;                            // MFMA column tiles (16 weight rows) per wave
-constexpr int kMx6WaveRows = 16 * kMx6WaveTiles;            // weight rows per wave
-constexpr int kMx6BlockRows = 4 * kMx6WaveRows;             // weight rows per block
-constexpr int kMx6MaxK = 5120;                              // scales of kMx6BlockRows rows fit kMx6SBytes
-constexpr int kMx6SBytes = kMx6BlockRows * (kMx6MaxK / 32);  // LDS bytes of the block's scales
-constexpr int kMx6SPieces = kMx6SBytes / 16 / 256;           // 16-byte scale pieces per thread (at most)
+// W8 (MXFP8 weights, 128 code bytes per row and chunk): a wave owns half the
+// weight rows, so its weight registers and the block's activation bytes per
+// weight byte stay those of the MXFP4 form, and its MFMAs per chunk (at the
+// FP8 rate) take the same time.
+template <bool W8>
+struct Mx6Shape {
+  static constexpr int kWaveTiles = W8 ? 4 : 8;         // MFMA column tiles (16 weight rows) per wave
+  static constexpr int kWaveRows = 16 * kWaveTiles;     // weight rows per wave
+  static constexpr int kBlockRows = 4 * kWaveRows;      // weight rows per block
+  static constexpr int kRowBytes(int K) { return W8 ? K : K / 2; }  // code bytes per weight row
+};
+constexpr int kMx6MaxK = 5120;                              // scales of a block's rows fit kMx6SBytes
+constexpr int kMx6SBytes = Mx6Shape<false>::kBlockRows * (kMx6MaxK / 32);  // LDS bytes of the block's scales
+template <bool W8>
+constexpr int kMx6SPieces = Mx6Shape<W8>::kBlockRows * (kMx6MaxK / 32) / 16 / 256;  // scale pieces per thread
 constexpr int kMx6ABufs = 4;                                // activation register buffers (chunks in flight)
 constexpr int kMx6Unroll = 4;                               // steps per loop iteration
 
@@ -225,13 +244,16 @@ constexpr int kMx6Unroll = 4;                               // steps per loop it
 // through LDS as whole 16-byte pieces (a row's two records are adjacent in
 // memory).  The LDS of the main loop is free: its last step ended at a
 // barrier after every read.
-template <int MT>
-__device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p, const f32x4_t (&acc)[MT][kMx6WaveTiles],
+template <int MT, bool W8>
+__device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p,
+                                                     const f32x4_t (&acc)[MT][Mx6Shape<W8>::kWaveTiles],
                                                      uint8_t* stage, uint8_t* sall, int m_begin, int rows, int n0) {
-  constexpr int JW = kMx6WaveTiles;
+  using S = Mx6Shape<W8>;
+  constexpr int JW = S::kWaveTiles;
+  constexpr int kCh = S::kBlockRows / 2 / 128;  // 128-wide h chunks per block row: 2 (MXFP4), 1 (MXFP8)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  static_assert(2 * kMx6Rows * kMx6ConvIn <= kMx6SBytes && 2 * kMx6Rows * kMx6Rec <= 2 * kMx6Stage,
+  static_assert(kCh * kMx6Rows * kMx6ConvIn <= kMx6SBytes && kCh * kMx6Rows * kMx6Rec <= 2 * kMx6Stage,
                 "the epilogue's units fit the main loop's LDS");
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -240,14 +262,14 @@ __device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p, const f
       const int r = 16 * m + 4 * g + i;  // rows past the tile are converted but never stored
 #pragma unroll
       for (int j = 0; j < JW / 2; ++j) {
-        const int c = (kMx6WaveRows / 2) * wave + 16 * j + n;  // block column, 0..255
-        *reinterpret_cast<uint16_t*>(sall + (2 * r + (c >> 7)) * kMx6ConvIn + 2 * (c & 127)) =
+        const int c = (S::kWaveRows / 2) * wave + 16 * j + n;  // block column, 0 .. 128 kCh - 1
+        *reinterpret_cast<uint16_t*>(sall + (kCh * r + (c >> 7)) * kMx6ConvIn + 2 * (c & 127)) =
             f32_to_bf16(clamped_swiglu(acc[m][j][i], acc[m][j + JW / 2][i], p.limit));
       }
     }
   __syncthreads();
   const int t = (int)threadIdx.x;
-  if (t < 2 * 16 * MT) {
+  if (t < kCh * 16 * MT) {
     u32x4_t v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(sall + t * kMx6ConvIn + 16 * i);
@@ -259,9 +281,9 @@ __device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p, const f
           u32x4_t{rec[4 * i], rec[4 * i + 1], rec[4 * i + 2], rec[4 * i + 3]};
   }
   __syncthreads();
-  // row r's two records: pieces [26 r, 26 r + 26) of the stage, to
+  // row r's kCh records: pieces [13 kCh r, 13 kCh (r + 1)) of the stage, to
   // Cmx + row * ldcmx + (n0 / 128) * kMx6Rec; a chunk at or past N is not stored
-  constexpr int kRowPieces = 2 * kMx6Rec / 16;
+  constexpr int kRowPieces = kCh * kMx6Rec / 16;
   for (int q = t; q < rows * kRowPieces; q += 256) {
     const int r = q / kRowPieces, k = q - r * kRowPieces;
     if (n0 + 128 * (k / (kMx6Rec / 16)) >= p.N) continue;
@@ -270,10 +292,12 @@ __device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p, const f
   }
 }
 
-template <bool SWIGLU, int MT>
+template <bool SWIGLU, int MT, bool W8>
 __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uint8_t* sall, int e, int m_begin,
                                          int rows, int n0) {
-  constexpr int JW = kMx6WaveTiles;
+  using S = Mx6Shape<W8>;
+  constexpr int JW = S::kWaveTiles;
+  constexpr int kMx6WaveRows = S::kWaveRows, kMx6BlockRows = S::kBlockRows;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int K = p.K, nchunks = K / 128;
@@ -284,7 +308,7 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   // weight rows of this block (expert-relative): SwiGLU, two runs of
   // kMx6BlockRows / 2 rows (gate rows n0.., up rows b_row_second + n0..);
   // otherwise one run of kMx6BlockRows rows from n0
-  const int64_t qbytes = p.b_expert_rows * (K / 2), sbytes = p.b_expert_rows * (K / 32);
+  const int64_t qbytes = p.b_expert_rows * S::kRowBytes(K), sbytes = p.b_expert_rows * (K / 32);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.bq + (int64_t)e * qbytes, (uint32_t)qbytes);
   // activation pieces this thread stages: piece q = tid + 256 i of the
   // stage (row q / 13, part q % 13); LDS byte 16 q.  Rows past the tile
@@ -318,7 +342,7 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   {
     const uint8_t* sbase = p.bs + (int64_t)e * sbytes;
 #pragma unroll
-    for (int i = 0; i < kMx6SPieces; ++i) {
+    for (int i = 0; i < kMx6SPieces<W8>; ++i) {
       const int q = (int)threadIdx.x + 256 * i;
       const int run = q / run_pieces, part = q - run * run_pieces;
       const int64_t off = (int64_t)(run * p.b_row_second + n0) * srow_bytes + 16 * part;
@@ -345,13 +369,14 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
 #pragma unroll
   for (int j = 0; j < JW; ++j) {
     const int row = weight_row(kMx6WaveRows * wave + 16 * j + n);
-    q_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)g : kOob;
+    q_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)S::kRowBytes(K) + 16u * (uint32_t)g : kOob;
   }
 
   // NB weight buffers, filled two chunks at a time (see step)
   constexpr int NB = 4;
   u32x4_t areg[kMx6ABufs][kPerThread];
   u32x4_t bq[NB][JW];
+  u32x4_t bq2[W8 ? NB : 1][JW];  // MXFP8: the second 16-byte piece of each lane's codes
   f32x4_t acc[MT][JW];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -375,11 +400,26 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   };
   // two chunks per burst, the same rows back to back: each row is read 128
   // contiguous bytes (a whole cache line) at a time
+  // (MXFP8: one chunk is already 128 contiguous bytes of a row, read as two
+  // 16-byte pieces per lane)
   auto load_b2 = [&](int c0, int c1, int buf0, int buf1) {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
-      bq[buf0][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c0, 0));
-      bq[buf1][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c1, 0));
+      if constexpr (W8) {
+        bq[buf0][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 128 * c0, 0));
+        bq2[buf0][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 128 * c0 + 64, 0));
+        bq[buf1][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 128 * c1, 0));
+        bq2[buf1][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 128 * c1 + 64, 0));
+      } else {
+        bq[buf0][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c0, 0));
+        bq[buf1][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off[j], 64 * c1, 0));
+      }
     }
   };
   // A operands of one row tile: the hi and lo terms and the scale word
@@ -420,8 +460,13 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
       if (m + 1 < MT) nxt = read_a(st + (m + 1) * 16 * kMx6Rec);
 #pragma unroll
       for (int j = 0; j < JW; ++j) {
-        acc[m][j] = mfma_f6f4(cur.hi, bq[buf][j], cur.sc, sb[j], acc[m][j], 0);
-        acc[m][j] = mfma_f6f4(cur.lo, bq[buf][j], cur.sc, sb[j], acc[m][j], 1);
+        if constexpr (W8) {
+          acc[m][j] = mfma_f6f8(cur.hi, bq[buf][j], bq2[buf][j], cur.sc, sb[j], acc[m][j], 0);
+          acc[m][j] = mfma_f6f8(cur.lo, bq[buf][j], bq2[buf][j], cur.sc, sb[j], acc[m][j], 1);
+        } else {
+          acc[m][j] = mfma_f6f4(cur.hi, bq[buf][j], cur.sc, sb[j], acc[m][j], 0);
+          acc[m][j] = mfma_f6f4(cur.lo, bq[buf][j], cur.sc, sb[j], acc[m][j], 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (m + 1 < MT) cur = nxt;
@@ -453,10 +498,11 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   store_a(0, 0);
   load_a(min(kMx6ABufs, last), 0);
   // the scale loads were issued before the (kMx6ABufs + 1) kPerThread
-  // activation and 2 JW weight loads above, and loads complete in issue
-  // order: this wait leaves at most those in flight (any other load issued
-  // after the scales only makes it stricter)
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kMx6ABufs + 1) * kPerThread + 2 * JW) : "memory");
+  // activation and the first burst's weight loads above (2 JW, MXFP8 4 JW),
+  // and loads complete in issue order: this wait leaves at most those in
+  // flight (any other load issued after the scales only makes it stricter)
+  constexpr int kBurstLoads = (W8 ? 4 : 2) * JW;
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kMx6ABufs + 1) * kPerThread + kBurstLoads) : "memory");
   __syncthreads();
   static_assert(kMx6Unroll % NB == 0 && kMx6Unroll % kMx6ABufs == 0, "the buffer indices repeat per iteration");
   for (int c = 0; c < nchunks; c += kMx6Unroll) {
@@ -467,7 +513,7 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
   // epilogue: lane 16 g + n holds rows 4 g + i of each row tile, column n of each column tile
   if constexpr (SWIGLU) {
     if (p.Cmx) {
-      mx6_epilogue_records<MT>(p, acc, stage, sall, m_begin, rows, n0);
+      mx6_epilogue_records<MT, W8>(p, acc, stage, sall, m_begin, rows, n0);
       return;
     }
   }
@@ -495,8 +541,8 @@ __device__ __forceinline__ void mx6_tile(const Mx6Params& p, uint8_t* stage, uin
 }
 
 // h columns (gate/up) or output columns (down) per block
-template <bool SWIGLU>
-constexpr int kMx6BlockCols = SWIGLU ? kMx6BlockRows / 2 : kMx6BlockRows;
+template <bool SWIGLU, bool W8>
+constexpr int kMx6BlockCols = SWIGLU ? Mx6Shape<W8>::kBlockRows / 2 : Mx6Shape<W8>::kBlockRows;
 
 // XCD-aware block order (as the pipelined kernels): block b runs on XCD
 // b % 8, which takes the tiles t with t % 8 == its index and runs a tile's
@@ -506,7 +552,7 @@ constexpr int kMx6BlockCols = SWIGLU ? kMx6BlockRows / 2 : kMx6BlockRows;
 // reads through the memory-side cache (grouping them on one XCD measured
 // slower: 1873 -> 1930-2130 us for the 16384-token gate/up).  One block per
 // CU, one wave per SIMD (512 registers a wave).
-template <bool SWIGLU>
+template <bool SWIGLU, bool W8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void expert_mx6_kernel(const Mx6Params p, int n_tiles, int col_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kMx6Stage];
@@ -517,12 +563,12 @@ void expert_mx6_kernel(const Mx6Params p, int n_tiles, int col_blocks) {
   const GemmTile tl = p.tiles[tile];
   const int m_begin = tl.m_begin, rows = min(tl.m_end, tl.m_begin + kMx6Rows) - tl.m_begin;
   if (rows <= 0) return;
-  const int n0 = cb * kMx6BlockCols<SWIGLU>;
+  const int n0 = cb * kMx6BlockCols<SWIGLU, W8>;
   const int mt = min(kMx6Rows / 16, 2 * ((rows + 31) / 32));
   switch (mt) {
-    case 2: mx6_tile<SWIGLU, 2>(p, stage, sall, tl.e, m_begin, rows, n0); break;
-    case 4: mx6_tile<SWIGLU, 4>(p, stage, sall, tl.e, m_begin, rows, n0); break;
-    default: mx6_tile<SWIGLU, 6>(p, stage, sall, tl.e, m_begin, rows, n0); break;
+    case 2: mx6_tile<SWIGLU, 2, W8>(p, stage, sall, tl.e, m_begin, rows, n0); break;
+    case 4: mx6_tile<SWIGLU, 4, W8>(p, stage, sall, tl.e, m_begin, rows, n0); break;
+    default: mx6_tile<SWIGLU, 6, W8>(p, stage, sall, tl.e, m_begin, rows, n0); break;
   }
 }
 
@@ -549,13 +595,13 @@ hipError_t launch_mx6_rows(const uint16_t* src, int64_t ld_src, int rows, int K,
 }
 
 hipError_t launch_expert_mx6(const Mx6Params& p, bool swiglu, int n_tiles, hipStream_t stream) {
-  const int cols = swiglu ? kMx6BlockCols<true> : kMx6BlockCols<false>;
+  const int cols = p.w8 ? (swiglu ? kMx6BlockCols<true, true> : kMx6BlockCols<false, true>)
+                        : (swiglu ? kMx6BlockCols<true, false> : kMx6BlockCols<false, false>);
   const int col_blocks = (p.N + cols - 1) / cols;
   const dim3 grid((unsigned)((n_tiles + 7) / 8 * 8 * col_blocks));
-  if (swiglu)
-    hipLaunchKernelGGL(expert_mx6_kernel<true>, grid, dim3(256), 0, stream, p, n_tiles, col_blocks);
-  else
-    hipLaunchKernelGGL(expert_mx6_kernel<false>, grid, dim3(256), 0, stream, p, n_tiles, col_blocks);
+  auto kern = p.w8 ? (swiglu ? expert_mx6_kernel<true, true> : expert_mx6_kernel<false, true>)
+                   : (swiglu ? expert_mx6_kernel<true, false> : expert_mx6_kernel<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, p, n_tiles, col_blocks);
   return hipGetLastError();
 }
 

@@ -245,7 +245,7 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     // MXFP6 rows, in tiles of its own height, at any row count past the
     // few-token kernels (it streams the weights straight to registers: 64
     // tokens, routed gate/up 664 -> 533 us against the 32-row bf16 kernel)
-    L.mx6 = L.fmt == moe::kWMxfp4 && moe::mx6_supported(c->hidden, c->inter);
+    L.mx6 = moe::mx6_supported(c->hidden, c->inter);
     // it takes tiles of up to mx6_tile_rows() rows: 128-row tiles become
     // tiles of that height; 32-row tiles stay, since the down projection's
     // 32-row kernel, which shares the tile table, computes 32 rows per tile
@@ -912,6 +912,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     moe::Mx6Params q{};
     q.tiles = at<moe::GemmTile>(ws, L.tiles);
     q.tile_count = at<int32_t>(ws, L.tile_count);
+    q.w8 = L.fmt == moe::kWMxfp8;
     // gate/up: A = x records of the tile's tokens, B = W_gu[e] [2I][H], C = h [n][I]
     q.gather = sorted;
     q.gather_div = c->top_k;

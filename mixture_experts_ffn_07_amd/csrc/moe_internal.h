@@ -353,8 +353,9 @@ struct Mx6Params {
   int64_t a_stride;
   int a_rows;
   int K;                       // multiple of 128
-  const uint8_t* bq;           // [E][b_expert_rows][K/2] E2M1 codes
+  const uint8_t* bq;           // [E][b_expert_rows][K/2] E2M1 codes ([..][K] E4M3 codes with w8)
   const uint8_t* bs;           // [E][b_expert_rows][K/32] E8M0 scales
+  int w8;                      // MXFP8 weights (FP6 x FP8 at the FP8 rate)
   int64_t b_expert_rows;
   int b_row_second;            // SwiGLU: first row of the up half
   int N;                       // output columns (h columns for gate/up)

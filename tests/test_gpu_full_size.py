@@ -24,9 +24,9 @@ DEV = "cuda"
 
 
 @pytest.mark.parametrize("name", ["decode_t64_h5120_e384", "prefill_t4096_h5120_e384", "skew_t16384_h5120_e128",
-                                  "verify_t320_h5120_e384"])
+                                  "verify_t320_h5120_e384", "prefill_t4096_h5120_e384_fp8", "decode_t64_fp8"])
 def test_layer_full_tensor(name):
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if name in CONFIGS else CONFIGS["decode_t64_h5120_e384"].with_(expert_format="mxfp8")
     inp = make_inputs(cfg, seed=0, device=DEV)
     gpu = gpu_layer(inp)
     load = np.bincount(gpu[1].cpu().numpy().reshape(-1), minlength=cfg.n_experts)
