@@ -256,8 +256,11 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     // own writing the records (4096 tokens 710 + 55 us against 768 us on the
     // 512-row bf16 kernel; 16384 tokens 1099 + 97 against 1106) the layer
     // gained 1.7% and 0.3%.  With 32-row tiles (64 and 320 tokens) the
-    // 32-row bf16 kernel is faster (64 tokens: 300 against 284 us)
-    L.mx6_dn = L.mx6 && L.bm == moe::mx6_tile_rows();
+    // 32-row bf16 kernel is faster (64 tokens: 300 against 284 us).  MXFP8
+    // weights take it at every tile height: against the 16-row bf16 kernel at
+    // 16-row tiles, 16 tokens 672 -> 647 us, 64 tokens 1707 -> 1645, 320
+    // tokens 2840 -> 2588, 700 tokens 3412 -> 2852
+    L.mx6_dn = L.mx6 && (L.bm == moe::mx6_tile_rows() || L.fmt == moe::kWMxfp8);
   }
   L.max_tiles = moe::max_gemm_tiles(n, E, L.bm);
   {
