@@ -16,8 +16,10 @@
 // into gfx950's block-scaled matrix instruction
 // (v_mfma_scale_f32_16x16x128_f8f6f4) as the B operand with their E8M0
 // scales, no dequantisation; activation rows are in two-term MXFP8 form
-// (mx_device.h), two MFMAs (hi, lo) per 128-wide chunk.  A wave owns 16
-// output columns over all of K.  Scale bytes are fetched as whole words
+// (mx_device.h), two MFMAs (hi, lo) per 128-wide chunk.  MXFP8 weights
+// (E4M3, one code a byte) go in the same way as the instruction's 8-bit B
+// operand, 32 codes per lane and chunk in two 16-byte pieces, at the FP8
+// rate.  A wave owns 16 output columns over all of K.  Scale bytes are fetched as whole words
 // covering several chunks: per-chunk byte loads cost as much memory-pipe
 // time as the code loads they accompany.
 //

@@ -3,7 +3,10 @@
 // MXFP4 weights as stored (E2M1 codes, E8M0 scale per 32 along K: Strata
 // DEEPSEEK41 notes, opening paragraph; the MAX API's float4_e2m1fnx2),
 // v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation, the clamped
-// SwiGLU (swiglu_limit, DeepseekV41Config) in the gate/up epilogue.
+// SwiGLU (swiglu_limit, DeepseekV41Config) in the gate/up epilogue.  MXFP8
+// weights (E4M3 codes with the same E8M0 scales: the MAX API's
+// float8_e4m3fn) take the same kernel as the instruction's 8-bit operand,
+// FP6 x FP8 at the FP8 rate.
 //
 // FP6 x FP4 runs at the FP4 rate on gfx950 (measured 7.9 PFLOP/s on a
 // register-only probe, against 4.4 for FP8 x FP4 and 2.3 for bf16), so the

@@ -241,10 +241,12 @@ WsLayout plan_workspace_impl(const moe_config* c, int64_t tokens, bool allow_dec
     L.bm = (int)tokens;   // an expert gets at most T rows: one tile per expert
   } else {
     L.bm = 16 * L.gemm_mt;
-    // MXFP4 experts with K multiples of 128: the block-scaled MFMA on two-term
-    // MXFP6 rows, in tiles of its own height, at any row count past the
-    // few-token kernels (it streams the weights straight to registers: 64
-    // tokens, routed gate/up 664 -> 533 us against the 32-row bf16 kernel)
+    // K multiples of 128: the block-scaled MFMA on two-term MXFP6 rows, in
+    // tiles of its own height, at any row count past the few-token kernels
+    // (it streams the weights straight to registers: 64 tokens, routed
+    // gate/up 664 -> 533 us against the 32-row bf16 kernel); MXFP8 weights
+    // too, as its 8-bit operand (64 tokens 1227 -> 962 us, 4096 tokens
+    // 2325 -> 2132 us against the bf16 kernels on dequantised E4M3)
     L.mx6 = moe::mx6_supported(c->hidden, c->inter);
     // it takes tiles of up to mx6_tile_rows() rows: 128-row tiles become
     // tiles of that height; 32-row tiles stay, since the down projection's
