@@ -33,10 +33,17 @@ def _outputs(t: int, cfg):
     return y, idx, wt
 
 
+# beside the workloads: the MXFP8 few-token GEMVs (5 tokens) and the MXFP6 kernels with E4M3 weights and h
+# records on a small layer (1100 tokens); the 4096-token layer takes the MXFP6 down projection on h records
+EXTRA = {"fp8_t5": CONFIGS["decode_t1_h5120_e384_fp8"].with_(tokens=5),
+         "fp8_t1100_small": CONFIGS["tiny_t8_h512_e32"].with_(tokens=1100, expert_format="mxfp8")}
+
+
 @pytest.mark.parametrize("name", ["tiny_t8_h512_e32", "decode_t1_h5120_e384", "decode_t1_h5120_e384_norm",
-                                  "decode_t64_h5120_e384"])
+                                  "decode_t64_h5120_e384", "prefill_t4096_h5120_e384", "decode_t1_h5120_e384_fp8",
+                                  "fp8_t5", "fp8_t1100_small"])
 def test_graph_replay_matches_eager(name):
-    inp = make_inputs(CONFIGS[name], seed=3, device=DEV)
+    inp = make_inputs(EXTRA[name] if name in EXTRA else CONFIGS[name], seed=3, device=DEV)
     cfg = moe.config_from(inp.cfg)
     w = moe.weights_from(inp)
     t = inp.cfg.tokens

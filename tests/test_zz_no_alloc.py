@@ -34,6 +34,7 @@ def _both(inp, tokens):
 @pytest.mark.parametrize("name,first,second", [("decode_t64_h5120_e384", 64, 5),
                                                ("decode_t1_h5120_e384", 2, 1),
                                                ("prefill_t4096_h5120_e384_fp8", 40, 17),
+                                               ("decode_t1_h5120_e384_fp8", 5, 2),
                                                ("tiny_t8_h512_e32", 8, 3)])
 def test_noalloc_matches_workspace_entry_point(name, first, second):
     cfg = CONFIGS[name].with_(tokens=first)
