@@ -393,7 +393,9 @@ def run_workload(name: str, steps: int, warmup: int, launch: str, weight_sets: i
                    "router_bias": "zipf(1.2)" if cfg.bias == "zipf" else "none",
                    "pre_ffn_rmsnorm": bool(cfg.norm), "weight_sets_cycled": sets,
                    "launch": ("hipgraph (one graph per cycle over the weight sets)" if use_graph
-                              else "stream (plain launches on one HIP stream)"),
+                              else "stream (plain launches on the caller's HIP stream; from 17 to 512 tokens the "
+                                    "library forks the shared expert onto its side stream and joins it before the "
+                                    "combine)"),
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "layer": dict(layer, experts_touched_per_step=touched_avg, kernel_ms=kernel_ms,

@@ -31,10 +31,11 @@
  *
  *   Memory.  Every tensor pointer is a DEVICE pointer owned by the caller
  *   (for instance the data pointer of a torch tensor); the library never
- *   allocates, frees or synchronises.  Config and weight structs are host
- *   memory, read only during the call.  Scratch memory comes from the
- *   caller's workspace `ws` of `ws_bytes` bytes, at least
- *   moe_workspace_bytes(cfg, tokens).
+ *   allocates device memory, frees or synchronises (moe_layer_forward
+ *   creates one side stream and two events per device, once: see there).
+ *   Config and weight structs are host memory, read only during the call.
+ *   Scratch memory comes from the caller's workspace `ws` of `ws_bytes`
+ *   bytes, at least moe_workspace_bytes(cfg, tokens).
  *
  *   Layout.  Row-major, the contracted dimension contiguous.  bf16 travels as
  *   its 16-bit pattern (uint16_t).  MXFP4 matrices [R][K] are two arrays:
@@ -185,7 +186,14 @@ moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int3
 /* The whole layer: y bf16 [T][H] from x bf16 [T][H], with the RMSNorm in
  * front when w->norm_gamma is non-NULL (then norm_eps is checked as for
  * moe_rmsnorm; x itself is not modified).  topk_idx_out [T][k] and
- * topk_w_out [T][k] receive the routing when non-NULL. */
+ * topk_w_out [T][k] receive the routing when non-NULL.
+ * From 17 to 512 tokens the shared expert's launches go to a side stream
+ * that the library holds per device (created, at default priority, with its
+ * two events by the first such call that is not under graph capture; until
+ * then, and under capture without it, one stream serves): an event recorded
+ * on `stream` orders them after the caller's earlier work, and `stream`
+ * waits for them before the combine, so every result is in `stream`'s order
+ * as above and a capture of `stream` holds both branches. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);

@@ -19,9 +19,9 @@
 // (mx_device.h), two MFMAs (hi, lo) per 128-wide chunk.  MXFP8 weights
 // (E4M3, one code a byte) go in the same way as the instruction's 8-bit B
 // operand, 32 codes per lane and chunk in two 16-byte pieces, at the FP8
-// rate.  A wave owns 16 output columns over all of K.  Scale bytes are fetched as whole words
-// covering several chunks: per-chunk byte loads cost as much memory-pipe
-// time as the code loads they accompany.
+// rate.  A wave owns 16 output columns over all of K.  Scale bytes are
+// fetched as whole words covering several chunks: per-chunk byte loads cost
+// as much memory-pipe time as the code loads they accompany.
 //
 // bf16 (shared expert, expert_gemv_bf16_kernel): v_mfma_f32_16x16x32_bf16
 // on bf16 rows; the 4 waves of a block split K and add their partial tiles

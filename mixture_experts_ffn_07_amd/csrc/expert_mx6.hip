@@ -240,13 +240,13 @@ constexpr int kMx6ABufs = 4;                                // activation regist
 constexpr int kMx6Unroll = 4;                               // steps per loop iteration
 
 // Gate/up epilogue writing h as two-term MXFP6 records (the down
-// projection's A operand) instead of bf16 rows: the block's 256 h columns are
-// two 128-wide chunks of every row.  The bf16 values go to LDS as units of
-// one row and chunk (stride kMx6ConvIn), each thread converts one unit
-// exactly as mx6_rows_kernel converts bf16 rows, and the records leave
-// through LDS as whole 16-byte pieces (a row's two records are adjacent in
-// memory).  The LDS of the main loop is free: its last step ended at a
-// barrier after every read.
+// projection's A operand) instead of bf16 rows: the block's 256 h columns
+// (128 with MXFP8 weights) are two (one) 128-wide chunks of every row.  The
+// bf16 values go to LDS as units of one row and chunk (stride kMx6ConvIn),
+// each thread converts one unit exactly as mx6_rows_kernel converts bf16
+// rows, and the records leave through LDS as whole 16-byte pieces (a row's
+// records are adjacent in memory).  The LDS of the main loop is free: its
+// last step ended at a barrier after every read.
 template <int MT, bool W8>
 __device__ __forceinline__ void mx6_epilogue_records(const Mx6Params& p,
                                                      const f32x4_t (&acc)[MT][Mx6Shape<W8>::kWaveTiles],

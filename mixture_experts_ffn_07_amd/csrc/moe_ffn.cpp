@@ -58,6 +58,43 @@ moe_status scratch_ptr(int dev, void** out) {
   return MOE_OK;
 }
 
+// Side stream of the many-token layer: the shared expert (independent of
+// the routing) runs on it beside the router, top-k, permutation and routed
+// GEMMs of the caller's stream, forked and joined by events.  One stream and
+// one event pair per device, created by the first call that can use them
+// (not under graph capture); the lock keeps each call's record and wait
+// sequence whole when several host threads call at once.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;  // creation failed once: the single-stream form serves
+};
+std::mutex g_side_mu[kMaxDevices];
+SideStream g_side[kMaxDevices];
+
+// The side stream of device `dev` (its lock held), or nullptr when the
+// single-stream form must serve.
+SideStream* side_stream(int dev, hipStream_t caller) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& s = g_side[dev];
+  if (s.st && s.fork && s.join) return &s;
+  if (s.failed) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (caller && hipStreamIsCapturing(caller, &cap) != hipSuccess) return nullptr;
+  if (cap != hipStreamCaptureStatusNone) return nullptr;
+  if (!s.st && hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) != hipSuccess) {
+    s.st = nullptr;
+    s.failed = true;
+    return nullptr;
+  }
+  if ((!s.fork && hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess) ||
+      (!s.join && hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)) {
+    s.failed = true;  // the stream and any event made stay unused until the process ends
+    return nullptr;
+  }
+  return &s;
+}
+
 // Optional per-kernel timing: an event recorded after every launch.
 struct Timeline {
   static constexpr int kMax = 32;
@@ -890,12 +927,13 @@ moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t*
 
 moe_status run_down(const moe_config* c, const moe_weights* w, int64_t T, const uint16_t* h, uint16_t* y_slot,
                     uint16_t* y_shared, const uint16_t* x, void* ws, const WsLayout& L, hipStream_t st,
-                    Timeline* tl);
+                    Timeline* tl, bool shared);
 
-// Routed gate/up + down over the tile table in ws, then the shared expert.
+// Routed gate/up + down over the tile table in ws, then (with `shared`) the
+// shared expert.
 moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T,
                        const int32_t* sorted, uint16_t* y_slot, uint16_t* y_shared, void* ws, const WsLayout& L,
-                       hipStream_t st, Timeline* tl) {
+                       hipStream_t st, Timeline* tl, bool shared = true) {
   const int H = c->hidden, I = c->inter;
   uint16_t* h = at<uint16_t>(ws, L.h);
   // few tokens: the MFMA GEMVs (MXFP4; MXFP8 with both K multiples of 128, as
@@ -939,7 +977,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     err = moe::launch_expert_mx6(q, true, (int)L.max_tiles, st);
     if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
     if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
-    if (!L.mx6_dn) return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl);
+    if (!L.mx6_dn) return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl, shared);
     // down: A = h records in position order, B = W_dn[e] [H][I], C = y_slot [n][H]
     q.Cmx = nullptr;
     q.gather = nullptr;
@@ -957,7 +995,7 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
     err = moe::launch_expert_mx6(q, false, (int)L.max_tiles, st);
     if (err == hipSuccess) err = mark(tl, "routed_down", st);
     if (err != hipSuccess) return fail_hip(err, "routed down launch");
-    return run_shared(c, w, x, T, y_shared, ws, L, st, tl);
+    return shared ? run_shared(c, w, x, T, y_shared, ws, L, st, tl) : MOE_OK;
   }
   moe::GemmParams p{};
   p.tiles = at<moe::GemmTile>(ws, L.tiles);
@@ -980,13 +1018,13 @@ moe_status run_experts(const moe_config* c, const moe_weights* w, const uint16_t
   err = moe::launch_expert_gemm(p, true, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_gate_up", st);
   if (err != hipSuccess) return fail_hip(err, "routed gate/up launch");
-  return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl);
+  return run_down(c, w, T, h, y_slot, y_shared, x, ws, L, st, tl, shared);
 }
 
 // Routed down projection on bf16 h over the tile table, then the shared expert.
 moe_status run_down(const moe_config* c, const moe_weights* w, int64_t T, const uint16_t* h, uint16_t* y_slot,
                     uint16_t* y_shared, const uint16_t* x, void* ws, const WsLayout& L, hipStream_t st,
-                    Timeline* tl) {
+                    Timeline* tl, bool shared) {
   const int H = c->hidden, I = c->inter;
   moe::GemmParams p{};
   p.tiles = at<moe::GemmTile>(ws, L.tiles);
@@ -1008,10 +1046,11 @@ moe_status run_down(const moe_config* c, const moe_weights* w, int64_t T, const 
   hipError_t err = moe::launch_expert_gemm(p, false, L.fmt, L.gemm_mt, L.max_tiles, st);
   if (err == hipSuccess) err = mark(tl, "routed_down", st);
   if (err != hipSuccess) return fail_hip(err, "routed down launch");
-  return run_shared(c, w, x, T, y_shared, ws, L, st, tl);
+  return shared ? run_shared(c, w, x, T, y_shared, ws, L, st, tl) : MOE_OK;
 }
 
-// The shared expert for the general path (after the routed GEMMs).
+// The shared expert for the general path (after the routed GEMMs, or on the
+// side stream beside them).
 moe_status run_shared(const moe_config* c, const moe_weights* w, const uint16_t* x, int64_t T, uint16_t* y_shared,
                       void* ws, const WsLayout& L, hipStream_t st, Timeline* tl) {
   const int H = c->hidden;
@@ -1173,7 +1212,7 @@ moe_status check_layer_args(const moe_config* cfg, const moe_weights* w, const u
 
 moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
                               uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                              hipStream_t st, Timeline* tl) {
+                              hipStream_t st, Timeline* tl, bool side_ok) {
   moe_status s;
   if ((s = check_layer_args(cfg, w, x, tokens, y, topk_idx_out, topk_w_out)) != MOE_OK) return s;
   const WsLayout L = plan_workspace(cfg, tokens);
@@ -1195,12 +1234,35 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   }
   if (L.stream4) return layer_forward_decode4(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl, nullptr);
   if (L.decode) return layer_forward_decode(cfg, w, x, tokens, y, idx, wts, ws, L, st, tl);
-  if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
-  if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;
   uint16_t* y_slot = at<uint16_t>(ws, L.y_slot);
   uint16_t* y_sh = cfg->n_shared ? at<uint16_t>(ws, L.y_sh) : nullptr;
-  if ((s = run_experts(cfg, w, x, tokens, sorted, y_slot, y_sh, ws, L, st, tl)) != MOE_OK) return s;
-  hipError_t err = moe::launch_combine(y_slot, slot_pos, wts, y_sh, (int)tokens, cfg->top_k, cfg->hidden, y, st);
+  // From 17 to 512 tokens (the skinny shared-expert kernel) the shared expert
+  // runs on the side stream (its inputs are x and its weights, its workspace
+  // regions its own), joined before the combine: its latency-bound launches
+  // then fill the CUs that the router, top-k and permutation leave idle
+  // (64 tokens 905 -> 884 us, 320 tokens 1469 -> 1428 us).  With more
+  // tokens it competes with the routed GEMMs for the CUs and is not faster.
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  int dev = -1;
+  if (side_ok && !tl && cfg->n_shared && L.shared_skinny && hipGetDevice(&dev) == hipSuccess && dev >= 0 &&
+      dev < kMaxDevices) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mu[dev]);
+    side = side_stream(dev, st);
+  }
+  hipError_t err;
+  if (side) {
+    if ((err = hipEventRecord(side->fork, st)) != hipSuccess) return fail_hip(err, "hipEventRecord(fork)");
+    if ((err = hipStreamWaitEvent(side->st, side->fork, 0)) != hipSuccess)
+      return fail_hip(err, "hipStreamWaitEvent(fork)");
+    if ((s = run_shared(cfg, w, x, tokens, y_sh, ws, L, side->st, nullptr)) != MOE_OK) return s;
+    if ((err = hipEventRecord(side->join, side->st)) != hipSuccess) return fail_hip(err, "hipEventRecord(join)");
+  }
+  if ((s = run_route(cfg, w, x, tokens, idx, wts, nullptr, ws, L, st, tl)) != MOE_OK) return s;
+  if ((s = run_permute(cfg, idx, tokens, offsets, sorted, slot_pos, ws, L, true, st, tl)) != MOE_OK) return s;
+  if ((s = run_experts(cfg, w, x, tokens, sorted, y_slot, y_sh, ws, L, st, tl, !side)) != MOE_OK) return s;
+  if (side && (err = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return fail_hip(err, "hipStreamWaitEvent(join)");
+  err = moe::launch_combine(y_slot, slot_pos, wts, y_sh, (int)tokens, cfg->top_k, cfg->hidden, y, st);
   if (err == hipSuccess) err = mark(tl, "combine", st);
   if (err != hipSuccess) return fail_hip(err, "combine launch");
   return MOE_OK;
@@ -1214,7 +1276,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                              void* stream) {
   return layer_forward_impl(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes,
-                            static_cast<hipStream_t>(stream), nullptr);
+                            static_cast<hipStream_t>(stream), nullptr, true);
 }
 
 moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
@@ -1241,7 +1303,7 @@ moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w
   void* ws = nullptr;
   if ((s = scratch_ptr(dev, &ws)) != MOE_OK) return s;
   return layer_forward_impl(cfg, w, x, tokens, y, topk_idx_out, topk_w_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
-                            st, nullptr);
+                            st, nullptr, false);
 }
 
 moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int64_t tokens,
@@ -1262,7 +1324,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, 
   } else if ((err = hipEventRecord(tl.ev[0], st)) != hipSuccess) {
     s = fail_hip(err, "hipEventRecord");
   } else {
-    s = layer_forward_impl(cfg, w, x, tokens, y, nullptr, nullptr, ws, ws_bytes, st, &tl);
+    s = layer_forward_impl(cfg, w, x, tokens, y, nullptr, nullptr, ws, ws_bytes, st, &tl, false);
     if (s == MOE_OK && tl.n > 0 && (err = hipEventSynchronize(tl.ev[tl.n])) != hipSuccess)
       s = fail_hip(err, "hipEventSynchronize");
     if (s == MOE_OK) {
