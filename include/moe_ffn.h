@@ -190,7 +190,8 @@ moe_status moe_combine(const moe_config* cfg, const uint16_t* y_slot, const int3
  * From 17 to 512 tokens the shared expert's launches go to a side stream
  * that the library holds per device (created, at default priority, with its
  * two events by the first such call that is not under graph capture; until
- * then, and under capture without it, one stream serves): an event recorded
+ * then, under capture without it, and when `stream` belongs to another
+ * device than the current one, one stream serves): an event recorded
  * on `stream` orders them after the caller's earlier work, and `stream`
  * waits for them before the combine, so every result is in `stream`'s order
  * as above and a capture of `stream` holds both branches. */

@@ -1247,8 +1247,13 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w, const
   int dev = -1;
   if (side_ok && !tl && cfg->n_shared && L.shared_skinny && hipGetDevice(&dev) == hipSuccess && dev >= 0 &&
       dev < kMaxDevices) {
-    side_lock = std::unique_lock<std::mutex>(g_side_mu[dev]);
-    side = side_stream(dev, st);
+    // the side stream is the current device's: a caller's stream of another
+    // device keeps the single-stream order
+    hipDevice_t sdev = dev;
+    if (!st || (hipStreamGetDevice(st, &sdev) == hipSuccess && (int)sdev == dev)) {
+      side_lock = std::unique_lock<std::mutex>(g_side_mu[dev]);
+      side = side_stream(dev, st);
+    }
   }
   hipError_t err;
   if (side) {
